@@ -1,0 +1,296 @@
+/*
+ * binattn_oracle.c -- plain, slow CPU oracle for the BinaryAttention forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the yardstick the GPU path is checked
+ * against.  Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark may load it.  It shares no code, header, table or constant with the
+ * HIP library, and it never reads anything the HIP library produced.
+ *
+ * Source of the method: "BinaryAttention: One-bit QK-Attention for Vision and
+ * Diffusion Transformers" (CVPR 2026, arXiv 2603.09582), paper-notes page,
+ * section "Method details":
+ *   - Key design 1 (Scaled Binary Representations): Q and K keep only their sign,
+ *     a per-token scale mu carries the magnitude; the sign dot product is computed
+ *     with XNOR/XOR + popcount.
+ *   - Key design 2 (Bias Enhancement): S_ij = mu_q mu_k s_i^T t_j / sqrt(d) + b_ij,
+ *     with b a dense learnable matrix or a relative-position bias.
+ *   - Key design 3 (Hybrid Quantization): the softmax output P is quantised to
+ *     unsigned 8 bit with the static scale 1/255; V is quantised channel-wise to
+ *     8 bit; PV is an integer product.
+ *   - Loss and training strategy (hardware implementation bullet): the kernel is a
+ *     FlashAttention2-style tiled kernel (softmax with running max and row sum).
+ *
+ * Arithmetic: fp64 throughout, except the V quantiser, which is defined in fp32
+ * so that a GPU implementation can reproduce it bit for bit.  Readings of points
+ * the pages leave open (all listed in the design notes of the repository):
+ *   mu      = mean |x| over the d channels of one token, stored as fp32;
+ *   sign    = +1 iff x >= 0 (so -0.0 -> +1), bit = 1 <=> +1, pad bits 0;
+ *   softmax = FlashAttention2 reading: the quantised quantity is the unnormalised
+ *             P~ = exp(S - rowmax) in (0,1]; the row sum l = sum P~ is kept in
+ *             floating point and divides in the epilogue;
+ *   P^      = round-half-even(255 * P~) in {0..255};
+ *   V^      = clamp(rint(fl32(v * fl32(127/a_c))), -127, 127), s_c = fl32(a_c/127),
+ *             a_c = max_j |v_jc| over the tokens of one (batch, head), a_c = 0 -> 0;
+ *   O_ic    = s_c * sum_j P^_ij V^_jc / (255 * l_i).
+ * Relative-position bias: token n sits at (r, c) = (n / gw, n % gw) on a gh x gw
+ * grid; b_ij = T[h, (r_i - r_j + gh - 1) * (2 gw - 1) + (c_i - c_j + gw - 1)].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_NO_PQUANT 1 /* flag: use P~ itself instead of P^/255 */
+#define ORACLE_NO_VQUANT 2 /* flag: use v itself instead of s * V^ */
+
+enum { BIAS_NONE = 0, BIAS_DENSE = 1, BIAS_RELPOS = 2 };
+
+int oracle_words(int d) { return (d + 31) / 32; }
+
+int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* Key design 1: one sign bit per channel plus the per-token scale mu. */
+void oracle_pack_qk(const double* x, int64_t ntok, int d, uint32_t* bits, float* mu) {
+    const int W = oracle_words(d);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < ntok; ++t) {
+        const double* row = x + t * d;
+        uint32_t* out = bits + t * W;
+        double sum = 0.0;
+        for (int w = 0; w < W; ++w) out[w] = 0u;
+        for (int c = 0; c < d; ++c) {
+            if (row[c] >= 0.0) out[c / 32] |= 1u << (c % 32);
+            sum += fabs(row[c]);
+        }
+        mu[t] = (float)(sum / (double)d);
+    }
+}
+
+/* Key design 3, V half: symmetric channel-wise int8 with one fp32 scale per
+ * (batch, head, channel).  vq is [nheads, N, d] row-major. */
+void oracle_quant_v(const double* v, int64_t nheads, int64_t N, int d, int8_t* vq, float* scale) {
+#pragma omp parallel for schedule(static)
+    for (int64_t bh = 0; bh < nheads; ++bh) {
+        const double* vh = v + bh * N * d;
+        int8_t* qh = vq + bh * N * d;
+        for (int c = 0; c < d; ++c) {
+            float a = 0.0f;
+            for (int64_t j = 0; j < N; ++j) {
+                float x = fabsf((float)vh[j * d + c]);
+                if (x > a) a = x;
+            }
+            if (a == 0.0f) {
+                scale[bh * d + c] = 0.0f;
+                for (int64_t j = 0; j < N; ++j) qh[j * d + c] = 0;
+                continue;
+            }
+            const float s = a / 127.0f;
+            const float inv = 127.0f / a;
+            scale[bh * d + c] = s;
+            for (int64_t j = 0; j < N; ++j) {
+                const float prod = (float)vh[j * d + c] * inv;
+                float r = rintf(prod);
+                if (r > 127.0f) r = 127.0f;
+                if (r < -127.0f) r = -127.0f;
+                qh[j * d + c] = (int8_t)r;
+            }
+        }
+    }
+}
+
+static int popcount32(uint32_t x) {
+    int n = 0;
+    while (x) {
+        x &= x - 1u;
+        ++n;
+    }
+    return n;
+}
+
+/* Key design 1: D_ij = sum_c sign(q_ic) sign(k_jc) = d - 2 * popcount(q XOR k). */
+static int32_t sign_dot(const uint32_t* a, const uint32_t* b, int d) {
+    const int W = oracle_words(d);
+    int h = 0;
+    for (int w = 0; w < W; ++w) h += popcount32(a[w] ^ b[w]);
+    return (int32_t)(d - 2 * h);
+}
+
+void oracle_scores_i32(const uint32_t* qbits, const uint32_t* kbits, int64_t nheads, int64_t N, int d,
+                       int32_t* D) {
+    const int W = oracle_words(d);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nheads * N; ++r) {
+        const int64_t bh = r / N;
+        const uint32_t* qi = qbits + r * W;
+        for (int64_t j = 0; j < N; ++j) D[r * N + j] = sign_dot(qi, kbits + (bh * N + j) * W, d);
+    }
+}
+
+typedef struct {
+    int64_t B, H, N;
+    int d, W, flags;
+    int bias_kind, gh, gw;
+    const double* bias;
+    const double* v;
+    uint32_t* qb;
+    uint32_t* kb;
+    float* qmu;
+    float* kmu;
+    int8_t* vq;
+    float* vs;
+} fwd_ctx;
+
+static double bias_at(const fwd_ctx* c, int64_t h, int64_t i, int64_t j) {
+    if (c->bias_kind == BIAS_DENSE) return c->bias[(h * c->N + i) * c->N + j];
+    if (c->bias_kind == BIAS_RELPOS) {
+        const int64_t ri = i / c->gw, ci = i % c->gw, rj = j / c->gw, cj = j % c->gw;
+        const int64_t row = ri - rj + c->gh - 1, col = ci - cj + c->gw - 1;
+        const int64_t tsz = (int64_t)(2 * c->gh - 1) * (2 * c->gw - 1);
+        return c->bias[h * tsz + row * (2 * c->gw - 1) + col];
+    }
+    return 0.0;
+}
+
+/* One query row (b, h, i): score, exact-max softmax, P quantiser, integer PV,
+ * dequantise and normalise.  S and ph are caller scratch of length N. */
+static void forward_row(const fwd_ctx* c, int64_t bh, int64_t i, double* S, double* ph, double* out,
+                        double* m_out, double* l_out, uint8_t* phat_out) {
+    const int64_t N = c->N, h = bh % c->H;
+    const int d = c->d, W = c->W;
+    const uint32_t* qi = c->qb + (bh * N + i) * W;
+    const double muq = (double)c->qmu[bh * N + i];
+    const double sqrt_d = sqrt((double)d);
+    double m = -INFINITY;
+    for (int64_t j = 0; j < N; ++j) {
+        const int32_t D = sign_dot(qi, c->kb + (bh * N + j) * W, d);
+        S[j] = muq * (double)c->kmu[bh * N + j] * (double)D / sqrt_d + bias_at(c, h, i, j);
+        if (S[j] > m) m = S[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+        const double pt = exp(S[j] - m);
+        l += pt;
+        ph[j] = (c->flags & ORACLE_NO_PQUANT) ? pt : nearbyint(255.0 * pt);
+        if (phat_out) phat_out[j] = (uint8_t)nearbyint(255.0 * pt);
+    }
+    const double pscale = (c->flags & ORACLE_NO_PQUANT) ? 1.0 : 255.0;
+    for (int ch = 0; ch < d; ++ch) {
+        double acc = 0.0;
+        if (c->flags & ORACLE_NO_VQUANT) {
+            const double* vh = c->v + bh * N * d;
+            for (int64_t j = 0; j < N; ++j) acc += ph[j] * vh[j * d + ch];
+            out[ch] = acc / (pscale * l);
+        } else {
+            const int8_t* qh = c->vq + bh * N * d;
+            for (int64_t j = 0; j < N; ++j) acc += ph[j] * (double)qh[j * d + ch];
+            out[ch] = (double)c->vs[bh * d + ch] * acc / (pscale * l);
+        }
+    }
+    if (m_out) *m_out = m;
+    if (l_out) *l_out = l;
+}
+
+static int ctx_init(fwd_ctx* c, const double* q, const double* k, const double* v, int bias_kind,
+                    const double* bias, int gh, int gw, int64_t B, int64_t H, int64_t N, int d, int flags) {
+    if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return -1;
+    if (bias_kind == BIAS_RELPOS && ((int64_t)gh * gw != N || gh <= 0 || gw <= 0)) return -1;
+    if (bias_kind != BIAS_NONE && !bias) return -1;
+    memset(c, 0, sizeof(*c));
+    c->B = B; c->H = H; c->N = N; c->d = d; c->W = oracle_words(d); c->flags = flags;
+    c->bias_kind = bias_kind; c->bias = bias; c->gh = gh; c->gw = gw; c->v = v;
+    const int64_t ntok = B * H * N;
+    c->qb = (uint32_t*)malloc(sizeof(uint32_t) * ntok * c->W);
+    c->kb = (uint32_t*)malloc(sizeof(uint32_t) * ntok * c->W);
+    c->qmu = (float*)malloc(sizeof(float) * ntok);
+    c->kmu = (float*)malloc(sizeof(float) * ntok);
+    c->vq = (int8_t*)malloc((size_t)ntok * d);
+    c->vs = (float*)malloc(sizeof(float) * B * H * d);
+    if (!c->qb || !c->kb || !c->qmu || !c->kmu || !c->vq || !c->vs) return -2;
+    oracle_pack_qk(q, ntok, d, c->qb, c->qmu);
+    oracle_pack_qk(k, ntok, d, c->kb, c->kmu);
+    oracle_quant_v(v, B * H, N, d, c->vq, c->vs);
+    return 0;
+}
+
+static void ctx_free(fwd_ctx* c) {
+    free(c->qb); free(c->kb); free(c->qmu); free(c->kmu); free(c->vq); free(c->vs);
+}
+
+/* Whole forward: out [B,H,N,d] fp64.  m_out / l_out [B,H,N] and phat_out
+ * [B,H,N,N] are optional diagnostics (NULL to skip).  Returns 0 on success. */
+int oracle_forward(const double* q, const double* k, const double* v, int bias_kind, const double* bias,
+                   int gh, int gw, int64_t B, int64_t H, int64_t N, int d, int flags, double* out,
+                   double* m_out, double* l_out, uint8_t* phat_out) {
+    fwd_ctx c;
+    int rc = ctx_init(&c, q, k, v, bias_kind, bias, gh, gw, B, H, N, d, flags);
+    if (rc) { if (rc == -2) ctx_free(&c); return rc; }
+    const int64_t rows = B * H * N;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double* S = (double*)malloc(sizeof(double) * N);
+        double* ph = (double*)malloc(sizeof(double) * N);
+        if (!S || !ph) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t r = 0; r < rows; ++r) {
+                forward_row(&c, r / N, r % N, S, ph, out + r * d, m_out ? m_out + r : NULL,
+                            l_out ? l_out + r : NULL, phat_out ? phat_out + r * N : NULL);
+            }
+        }
+        free(S);
+        free(ph);
+    }
+    ctx_free(&c);
+    return fail ? -2 : 0;
+}
+
+/* Selected rows only: rows[] index the flattened (b, h, i) space; out_rows is
+ * [nrows, d].  Used to check full-size launches on a sample of outputs. */
+int oracle_forward_rows(const double* q, const double* k, const double* v, int bias_kind, const double* bias,
+                        int gh, int gw, int64_t B, int64_t H, int64_t N, int d, int flags, const int64_t* rows,
+                        int64_t nrows, double* out_rows) {
+    fwd_ctx c;
+    int rc = ctx_init(&c, q, k, v, bias_kind, bias, gh, gw, B, H, N, d, flags);
+    if (rc) { if (rc == -2) ctx_free(&c); return rc; }
+    int fail = 0;
+#pragma omp parallel
+    {
+        double* S = (double*)malloc(sizeof(double) * N);
+        double* ph = (double*)malloc(sizeof(double) * N);
+        if (!S || !ph) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < nrows; ++t) {
+                const int64_t r = rows[t];
+                if (r < 0 || r >= B * H * N) continue;
+                forward_row(&c, r / N, r % N, S, ph, out_rows + t * d, NULL, NULL, NULL);
+            }
+        }
+        free(S);
+        free(ph);
+    }
+    ctx_free(&c);
+    return fail ? -2 : 0;
+}
