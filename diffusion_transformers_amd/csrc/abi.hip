@@ -1,0 +1,139 @@
+// abi.hip -- extern "C" entry points declared in include/binattn.h: argument
+// validation (before any HIP call), error codes, kernel launches.
+#include <math.h>
+#include <stdint.h>
+
+#include "binattn.h"
+#include "internal.h"
+
+using namespace binattn;
+
+namespace {
+
+constexpr int kMaxN = 65536;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dims(int B, int H, int N, int d) {
+    if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return BINATTN_EINVAL;
+    if (N > kMaxN || d % 8 != 0 || d < 8 || d > 128) return BINATTN_EUNSUPPORTED;
+    const double big = (double)B * H * N * (double)(N > d ? N : d);
+    if (big > 4.6e18) return BINATTN_EUNSUPPORTED;
+    if ((int64_t)B * H > (int64_t)1 << 24) return BINATTN_EUNSUPPORTED;
+    return BINATTN_OK;
+}
+
+bool dtype_ok(int dt) { return dt == BINATTN_F32 || dt == BINATTN_F16; }
+
+int device_ready() {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return BINATTN_ENODEVICE;
+    return BINATTN_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? BINATTN_OK : BINATTN_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int binattn_abi_version(void) { return BINATTN_ABI_VERSION; }
+
+const char* binattn_strerror(int code) {
+    switch (code) {
+        case BINATTN_OK: return "ok";
+        case BINATTN_EINVAL: return "invalid argument (null pointer, non-positive size, inconsistent grid or stride)";
+        case BINATTN_EUNSUPPORTED: return "unsupported size, dtype or bias layout";
+        case BINATTN_EALIGN: return "device pointer or bias row not 16-byte aligned";
+        case BINATTN_ENODEVICE: return "no HIP device visible";
+        case BINATTN_ELAUNCH: return "kernel launch failed";
+        default: return "unknown error";
+    }
+}
+
+int binattn_words(int d) { return d > 0 ? (d + 31) / 32 : 0; }
+
+int64_t binattn_vq_ld(int N) { return N > 0 ? ((int64_t)N + 63) / 64 * 64 : 0; }
+
+int binattn_pack_qk(const void* x, int dtype, int B, int H, int N, int d, uint32_t* bits, float* mu,
+                    void* stream) {
+    if (!x || !bits || !mu) return BINATTN_EINVAL;
+    int rc = check_dims(B, H, N, d);
+    if (rc) return rc;
+    if (!dtype_ok(dtype)) return BINATTN_EUNSUPPORTED;
+    if (!aligned16(x) || !aligned16(bits) || !aligned16(mu)) return BINATTN_EALIGN;
+    if ((rc = device_ready())) return rc;
+    return launched(launch_pack_qk(x, dtype == BINATTN_F32, (int64_t)B * H * N, d, bits, mu, (hipStream_t)stream));
+}
+
+int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t* vq, float* vscale,
+                    void* stream) {
+    if (!v || !vq || !vscale) return BINATTN_EINVAL;
+    int rc = check_dims(B, H, N, d);
+    if (rc) return rc;
+    if (!dtype_ok(dtype)) return BINATTN_EUNSUPPORTED;
+    if (!aligned16(v) || !aligned16(vq) || !aligned16(vscale)) return BINATTN_EALIGN;
+    if ((rc = device_ready())) return rc;
+    return launched(launch_quant_v(v, dtype == BINATTN_F32, B * H, N, d, binattn_vq_ld(N), vq, vscale,
+                                   (hipStream_t)stream));
+}
+
+int binattn_forward(const uint32_t* q_bits, const float* q_mu, const uint32_t* k_bits, const float* k_mu,
+                    const int8_t* vq, const float* vscale, int bias_kind, int bias_dtype, const void* bias,
+                    int64_t bias_ld, int grid_h, int grid_w, int B, int H, int N, int d, void* out,
+                    int out_dtype, void* stream) {
+    if (!q_bits || !q_mu || !k_bits || !k_mu || !vq || !vscale || !out) return BINATTN_EINVAL;
+    int rc = check_dims(B, H, N, d);
+    if (rc) return rc;
+    if (!dtype_ok(out_dtype)) return BINATTN_EUNSUPPORTED;
+    if (!aligned16(q_bits) || !aligned16(q_mu) || !aligned16(k_bits) || !aligned16(k_mu) || !aligned16(vq) ||
+        !aligned16(vscale) || !aligned16(out))
+        return BINATTN_EALIGN;
+    switch (bias_kind) {
+        case BINATTN_BIAS_NONE:
+            if (bias) return BINATTN_EINVAL;
+            break;
+        case BINATTN_BIAS_DENSE: {
+            if (!bias) return BINATTN_EINVAL;
+            if (!dtype_ok(bias_dtype)) return BINATTN_EUNSUPPORTED;
+            if (bias_ld < N) return BINATTN_EINVAL;
+            const int64_t row_bytes = bias_ld * (bias_dtype == BINATTN_F32 ? 4 : 2);
+            if (row_bytes % 16 != 0 || !aligned16(bias)) return BINATTN_EALIGN;
+            break;
+        }
+        case BINATTN_BIAS_RELPOS:
+            if (!bias) return BINATTN_EINVAL;
+            if (!dtype_ok(bias_dtype)) return BINATTN_EUNSUPPORTED;
+            if (grid_h <= 0 || grid_w <= 0 || (int64_t)grid_h * grid_w != N) return BINATTN_EINVAL;
+            if (grid_w % 16 != 0 || grid_w > 512) return BINATTN_EUNSUPPORTED;
+            if (!aligned16(bias)) return BINATTN_EALIGN;
+            break;
+        default:
+            return BINATTN_EUNSUPPORTED;
+    }
+    if ((rc = device_ready())) return rc;
+    FwdArgs a = {};
+    a.qbits = q_bits; a.qmu = q_mu; a.kbits = k_bits; a.kmu = k_mu; a.vq = vq; a.vscale = vscale;
+    a.bias = bias; a.bias_ld = bias_ld; a.bias_f32 = bias_dtype == BINATTN_F32;
+    a.gh = grid_h; a.gw = grid_w;
+    a.B = B; a.H = H; a.N = N; a.d = d; a.W = binattn_words(d); a.ldv = binattn_vq_ld(N);
+    a.out = out; a.out_f32 = out_dtype == BINATTN_F32;
+    a.qk_scale = (float)(1.0 / sqrt((double)d));
+    return launched(launch_forward(a, bias_kind, (hipStream_t)stream));
+}
+
+int binattn_scores_i32(const uint32_t* q_bits, const uint32_t* k_bits, int B, int H, int N, int d, int32_t* D,
+                       void* stream) {
+    if (!q_bits || !k_bits || !D) return BINATTN_EINVAL;
+    int rc = check_dims(B, H, N, d);
+    if (rc) return rc;
+    if (!aligned16(q_bits) || !aligned16(k_bits) || !aligned16(D)) return BINATTN_EALIGN;
+    if ((rc = device_ready())) return rc;
+    FwdArgs a = {};
+    a.qbits = q_bits; a.kbits = k_bits;
+    a.B = B; a.H = H; a.N = N; a.d = d; a.W = binattn_words(d);
+    a.scores = D;
+    return launched(launch_scores(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+// internal.h -- launchers behind the C ABI (host side; arguments are already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace binattn {
+
+struct FwdArgs {
+    const uint32_t* qbits;
+    const float* qmu;
+    const uint32_t* kbits;
+    const float* kmu;
+    const int8_t* vq;
+    const float* vscale;
+    const void* bias;
+    int64_t bias_ld;      // dense: row stride in elements
+    int bias_f32;         // bias / table stored as fp32 (else fp16)
+    int gh, gw;           // relative-position grid
+    int B, H, N, d, W;
+    int64_t ldv;          // key stride of vq rows
+    void* out;
+    int out_f32;
+    float qk_scale;       // 1 / sqrt(d)
+    int32_t* scores;      // scores export only
+};
+
+hipError_t launch_pack_qk(const void* x, int f32, int64_t ntok, int d, uint32_t* bits, float* mu,
+                          hipStream_t s);
+hipError_t launch_quant_v(const void* v, int f32, int BH, int N, int d, int64_t ldv, int8_t* vq, float* vscale,
+                          hipStream_t s);
+hipError_t launch_forward(const FwdArgs& a, int bias_kind, hipStream_t s);
+hipError_t launch_scores(const FwdArgs& a, hipStream_t s);
+
+}  // namespace binattn

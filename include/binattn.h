@@ -1,0 +1,155 @@
+/*
+ * binattn.h -- C ABI of the BinaryAttention forward library (AMD MI355X, gfx950).
+ *
+ * The method: "BinaryAttention: One-bit QK-Attention for Vision and Diffusion
+ * Transformers" (CVPR 2026, arXiv 2603.09582), paper-notes page, section
+ * "Method details":
+ *   key design 1 (Scaled Binary Representations)  -> binattn_pack_qk, binattn_scores_i32
+ *   key design 2 (Bias Enhancement)               -> the bias arguments of binattn_forward
+ *   key design 3 (Hybrid Quantization)            -> binattn_quant_v, binattn_forward
+ *   hardware implementation bullet (a FlashAttention2-style tiled kernel with a
+ *   binary QK product and an integer PV product)  -> binattn_forward
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument except `stream` is a DEVICE pointer owned by the
+ *    caller.  The library never allocates, frees or caches device memory and
+ *    keeps no state between calls.  Inputs are read only; outputs are fully
+ *    overwritten.  Inputs and outputs must not overlap.
+ *  - Every device pointer must be 16-byte aligned (else BINATTN_EALIGN).
+ *  - Tensors are dense row-major in the order their shape is written.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call only enqueues work on that stream and returns; results are
+ *    visible after the caller synchronises the stream.
+ *  - Return value: BINATTN_OK (0) or a negative BINATTN_E* code.  All argument
+ *    checks run before any HIP call; nothing is launched when a check fails.
+ *    No call aborts or throws.  A fault inside a kernel (for example from a
+ *    pointer that does not cover the documented extent) surfaces at the
+ *    caller's next synchronisation, not here.
+ *  - Supported sizes: B, H, N >= 1; N <= 65536; d a multiple of 8 with
+ *    8 <= d <= 128 (BINATTN_EUNSUPPORTED otherwise); B*H*N*max(d,N) must fit
+ *    in 2^62.
+ *  - dtype codes: BINATTN_F32 (IEEE binary32), BINATTN_F16 (IEEE binary16).
+ */
+#ifndef BINATTN_H
+#define BINATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BINATTN_ABI_VERSION 1
+
+#define BINATTN_F32 0
+#define BINATTN_F16 1
+
+#define BINATTN_BIAS_NONE 0
+#define BINATTN_BIAS_DENSE 1
+#define BINATTN_BIAS_RELPOS 2
+
+#define BINATTN_OK 0
+#define BINATTN_EINVAL (-1)       /* NULL pointer, non-positive size, inconsistent grid or leading dimension */
+#define BINATTN_EUNSUPPORTED (-2) /* size, dtype or bias layout outside what the kernels implement */
+#define BINATTN_EALIGN (-3)       /* a device pointer or bias row is not 16-byte aligned */
+#define BINATTN_ENODEVICE (-4)    /* no HIP device is visible */
+#define BINATTN_ELAUNCH (-5)      /* the HIP runtime rejected a kernel launch */
+
+/* Version of this ABI (BINATTN_ABI_VERSION of the built library). */
+int binattn_abi_version(void);
+
+/* Static text for a return code ("unknown error" for codes it does not know). */
+const char* binattn_strerror(int code);
+
+/* Number of 32-bit sign words per token: ceil(d / 32). */
+int binattn_words(int d);
+
+/* Key stride (bytes) of a quantised V row: N rounded up to a multiple of 64. */
+int64_t binattn_vq_ld(int N);
+
+/*
+ * binattn_pack_qk -- sign bits and per-token scale of Q or K.
+ * Passage: key design 1 (Scaled Binary Representations): only the sign of each
+ * channel is kept, and a per-token scale mu keeps the token's magnitude.
+ *
+ *   x     [B,H,N,d]   dtype (BINATTN_F16 or BINATTN_F32), read only
+ *   bits  [B,H,N,W]   uint32, W = binattn_words(d); bit (c % 32) of word c / 32
+ *                     is 1 iff x[..., c] >= 0 (so -0.0 counts as +1); bits for
+ *                     c >= d are 0
+ *   mu    [B,H,N]     fp32, mean |x| over the d channels of the token
+ * x must hold finite values.
+ */
+int binattn_pack_qk(const void* x, int dtype, int B, int H, int N, int d, uint32_t* bits, float* mu,
+                    void* stream);
+
+/*
+ * binattn_quant_v -- channel-wise symmetric int8 quantisation of V.
+ * Passage: key design 3 (Hybrid Quantization): V is quantised channel-wise to
+ * 8 bits.
+ *
+ *   v      [B,H,N,d]   dtype, read only, finite
+ *   vq     [B,H,d,ldv] int8, ldv = binattn_vq_ld(N) (channel-major: the N
+ *                      tokens of one channel are contiguous); entries for
+ *                      tokens n >= N are written as 0
+ *   vscale [B,H,d]     fp32
+ * Per (b, h, channel c), in fp32 with IEEE division and round-half-even:
+ *   a = max_n |v[n,c]|;  vscale = a / 127;  inv = 127 / a;
+ *   vq[c,n] = clamp(rint(v[n,c] * inv), -127, 127);  a == 0 -> vscale = 0, vq = 0.
+ * vscale doubles as scratch while the call runs.
+ */
+int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t* vq, float* vscale,
+                    void* stream);
+
+/*
+ * binattn_forward -- BinaryAttention forward from packed Q/K and quantised V.
+ * Passages: key design 1 (binary score with per-token scales), key design 2
+ * (S_ij = mu_q mu_k s_i.t_j / sqrt(d) + b_ij), key design 3 (P quantised to u8
+ * with scale 1/255, integer PV), hardware implementation bullet (one tiled
+ * kernel with running max and row sum).
+ *
+ *   q_bits, k_bits  [B,H,N,W] uint32   from binattn_pack_qk
+ *   q_mu, k_mu      [B,H,N]   fp32     from binattn_pack_qk
+ *   vq              [B,H,d,ldv] int8   from binattn_quant_v
+ *   vscale          [B,H,d]   fp32     from binattn_quant_v
+ *   bias_kind       BINATTN_BIAS_NONE:   bias must be NULL.
+ *                   BINATTN_BIAS_DENSE:  bias [H,N,bias_ld] of bias_dtype, entry
+ *                       (h,i,j) = b_ij for every batch item; bias_ld >= N and
+ *                       bias_ld * sizeof(dtype) a multiple of 16 bytes.
+ *                   BINATTN_BIAS_RELPOS: bias is a table [H,(2gh-1)*(2gw-1)] of
+ *                       bias_dtype; token n sits at (n / gw, n % gw) on a
+ *                       gh x gw grid (gh*gw == N) and
+ *                       b_ij = T[h, (r_i-r_j+gh-1)*(2gw-1) + (c_i-c_j+gw-1)].
+ *                       Requires gw % 16 == 0 and gw <= 512.  bias_ld ignored.
+ *   out             [B,H,N,d] of out_dtype
+ *
+ * Computes, per (b, h, query i):
+ *   D_ij = d - 2 popcount(q_bits_i XOR k_bits_j)                (exact integer)
+ *   S_ij = q_mu_i * k_mu_j * D_ij / sqrt(d) + b_ij             (fp32)
+ *   streamed over key tiles with a running row max m and row sum l:
+ *   P^_ij = rint(255 * exp(S_ij - m)) in [0,255], l = sum exp(S_ij - m) (fp32),
+ *   O_ic = vscale_c * sum_j P^_ij vq_cj / (255 * l_i)
+ * (integer PV; the max used for a key tile is the running max after that tile,
+ * so P^ may differ by the rounding of an earlier tile from a two-pass exact-max
+ * result).
+ */
+int binattn_forward(const uint32_t* q_bits, const float* q_mu, const uint32_t* k_bits, const float* k_mu,
+                    const int8_t* vq, const float* vscale, int bias_kind, int bias_dtype, const void* bias,
+                    int64_t bias_ld, int grid_h, int grid_w, int B, int H, int N, int d, void* out,
+                    int out_dtype, void* stream);
+
+/*
+ * binattn_scores_i32 -- the integer sign score matrix, computed by the same
+ * binary QK tile code as binattn_forward (test and inspection export).
+ * Passage: key design 1: s_i.t_j through XOR and popcount.
+ *
+ *   q_bits, k_bits [B,H,N,W] uint32;  D [B,H,N,N] int32, D_ij = d - 2 popcount(q_i XOR k_j).
+ */
+int binattn_scores_i32(const uint32_t* q_bits, const uint32_t* k_bits, int B, int H, int N, int d, int32_t* D,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BINATTN_H */

@@ -60,6 +60,7 @@ def _load():
     lib.oracle_pack_qk.argtypes = [vp, i64, i32, vp, vp]
     lib.oracle_quant_v.argtypes = [vp, i64, i64, i32, vp, vp]
     lib.oracle_scores_i32.argtypes = [vp, vp, i64, i64, i32, vp]
+    lib.oracle_scores_rows.argtypes = [vp, vp, i64, i64, i32, vp, i64, vp]
     lib.oracle_forward.argtypes = [vp, vp, vp, i32, vp, i32, i32, i64, i64, i64, i32, i32, vp, vp, vp, vp]
     lib.oracle_forward.restype = i32
     lib.oracle_forward_rows.argtypes = [vp, vp, vp, i32, vp, i32, i32, i64, i64, i64, i32, i32, vp, i64, vp]
@@ -117,6 +118,17 @@ def scores_i32(qbits, kbits, d: int):
     B, H, N, _ = qbits.shape
     D = np.zeros((B, H, N, N), dtype=np.int32)
     _load().oracle_scores_i32(_ptr(qbits), _ptr(kbits), B * H, N, d, _ptr(D))
+    return D
+
+
+def scores_rows(qbits, kbits, d: int, rows):
+    """Rows of D for selected flattened (b, h, i) indices -> [len(rows), N] int32."""
+    qbits = np.ascontiguousarray(qbits, dtype=np.uint32)
+    kbits = np.ascontiguousarray(kbits, dtype=np.uint32)
+    B, H, N, _ = qbits.shape
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    D = np.zeros((rows.size, N), dtype=np.int32)
+    _load().oracle_scores_rows(_ptr(qbits), _ptr(kbits), B * H, N, d, _ptr(rows), rows.size, _ptr(D))
     return D
 
 

@@ -143,6 +143,19 @@ void oracle_scores_i32(const uint32_t* qbits, const uint32_t* kbits, int64_t nhe
     }
 }
 
+/* Selected rows of D: rows[] index the flattened (bh, i) space; D_rows is [nrows, N]. */
+void oracle_scores_rows(const uint32_t* qbits, const uint32_t* kbits, int64_t nheads, int64_t N, int d,
+                        const int64_t* rows, int64_t nrows, int32_t* D_rows) {
+    const int W = oracle_words(d);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < nrows; ++t) {
+        const int64_t r = rows[t];
+        if (r < 0 || r >= nheads * N) continue;
+        const int64_t bh = r / N;
+        for (int64_t j = 0; j < N; ++j) D_rows[t * N + j] = sign_dot(qbits + r * W, kbits + (bh * N + j) * W, d);
+    }
+}
+
 typedef struct {
     int64_t B, H, N;
     int d, W, flags;

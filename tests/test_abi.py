@@ -1,0 +1,100 @@
+"""The C-ABI library loads, exports every symbol include/binattn.h declares, and rejects
+bad arguments before touching a device (no compute calls are made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "binattn.h")
+LIB = os.path.join(ROOT, "diffusion_transformers_amd", "libbinattn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libbinattn.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(binattn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from diffusion_transformers_amd import binding
+    return binding.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"binattn_pack_qk", "binattn_quant_v", "binattn_forward", "binattn_scores_i32"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} missing from libbinattn.so"
+    from diffusion_transformers_amd import binding
+    assert sorted(binding.EXPORTS) == names
+
+
+def test_header_has_no_torch_types():
+    text = open(HEADER).read()
+    assert "torch" not in text.lower().replace("pytorch", "")
+    assert "extern \"C\"" in text
+
+
+def test_small_helpers(lib):
+    assert lib.binattn_abi_version() == 1
+    assert [lib.binattn_words(d) for d in (1, 32, 33, 64, 72, 128)] == [1, 1, 2, 2, 3, 4]
+    assert [lib.binattn_vq_ld(n) for n in (1, 64, 65, 197, 577, 16384)] == [64, 64, 128, 256, 640, 16384]
+    assert lib.binattn_strerror(-2) and lib.binattn_strerror(12345) == b"unknown error"
+
+
+P = ctypes.c_void_p
+
+
+def _a(x):
+    return P(x)
+
+
+def test_pack_and_quant_validation(lib):
+    ok = (_a(256), 1, 2, 3, 5, 64, _a(512), _a(1024), None)
+    # null pointers / sizes / dtype / d / alignment are all rejected before any device call
+    assert lib.binattn_pack_qk(None, *ok[1:]) == -1
+    assert lib.binattn_pack_qk(ok[0], 1, 0, 3, 5, 64, ok[6], ok[7], None) == -1
+    assert lib.binattn_pack_qk(ok[0], 1, 2, 3, -5, 64, ok[6], ok[7], None) == -1
+    assert lib.binattn_pack_qk(ok[0], 7, 2, 3, 5, 64, ok[6], ok[7], None) == -2
+    assert lib.binattn_pack_qk(ok[0], 1, 2, 3, 5, 60, ok[6], ok[7], None) == -2
+    assert lib.binattn_pack_qk(ok[0], 1, 2, 3, 5, 136, ok[6], ok[7], None) == -2
+    assert lib.binattn_pack_qk(ok[0], 1, 2, 3, 70000, 64, ok[6], ok[7], None) == -2
+    assert lib.binattn_pack_qk(_a(258), 1, 2, 3, 5, 64, ok[6], ok[7], None) == -3
+    assert lib.binattn_quant_v(ok[0], 1, 2, 3, 5, 64, None, ok[7], None) == -1
+    assert lib.binattn_quant_v(ok[0], 1, 2, 3, 5, 64, _a(520), ok[7], None) == -3
+
+
+def _fwd(lib, **kw):
+    args = dict(qb=_a(256), qm=_a(512), kb=_a(768), km=_a(1024), vq=_a(1280), vs=_a(1536), kind=0, bdt=1,
+                bias=None, ld=0, gh=0, gw=0, B=2, H=3, N=256, d=64, out=_a(2048), odt=1, stream=None)
+    args.update(kw)
+    return lib.binattn_forward(*args.values())
+
+
+def test_forward_validation(lib):
+    assert _fwd(lib, qb=None) == -1
+    assert _fwd(lib, kind=0, bias=_a(4096)) == -1            # bias given with kind NONE
+    assert _fwd(lib, kind=1, bias=None, ld=256) == -1        # dense without data
+    assert _fwd(lib, kind=1, bias=_a(4096), ld=255) == -1    # ld < N
+    assert _fwd(lib, kind=1, bias=_a(4096), ld=260, N=257) == -3  # 520-byte rows are not 16-byte multiples
+    assert _fwd(lib, kind=1, bias=_a(4100), ld=256) == -3    # misaligned base
+    assert _fwd(lib, kind=2, bias=_a(4096), gh=16, gw=15) == -1   # grid does not cover N
+    assert _fwd(lib, kind=2, bias=_a(4096), N=240, gh=16, gw=15) == -2  # gw % 16 != 0
+    assert _fwd(lib, kind=2, bias=_a(4096), N=1024, gh=1, gw=1024) == -2  # gw > 512
+    assert _fwd(lib, kind=3, bias=_a(4096)) == -2
+    assert _fwd(lib, odt=5) == -2
+    assert _fwd(lib, d=72, out=_a(2056)) == -3
+    assert lib.binattn_scores_i32(_a(256), None, 1, 1, 4, 64, _a(512), None) == -1
+
+
+def test_valid_arguments_without_a_device_report_enodevice(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    assert lib.binattn_pack_qk(_a(256), 1, 2, 3, 5, 64, _a(512), _a(1024), None) == -4
+    assert _fwd(lib) == -4
+    assert _fwd(lib, kind=2, bias=_a(4096), gh=16, gw=16) == -4
