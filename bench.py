@@ -1,0 +1,266 @@
+"""Benchmark of the BinaryAttention forward hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch: sign-pack Q, sign-pack
+K, quantise V, fused forward -- four calls through the C ABI.  The default
+workload is DeiT-S 224^2 (B=64, H=6, N=197, d=64, fp16, dense per-head bias);
+``--workload`` selects another named shape.  Inputs are seeded synthetic
+activations (diffusion_transformers_amd/workloads.py) already resident in HBM;
+``--rotate`` input sets are cycled so the 256 MB last-level cache does not hold
+the step's working set.
+
+Prints ONE JSON line.  value = effective TOPS of the step, counting
+2*B*H*N^2*d for QK^T plus the same for PV.  The roofline object is for the
+dominant kernel (the fused forward): algorithmic bytes per launch over its
+average launch time measured with HIP events on the launch stream, against the
+binding roofline of the two the method names (int8 MFMA 5.0 POPS, HBM 8 TB/s).
+cpu_baseline times the CPU oracle (whole hot path) on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "binary-attention fwd ms/call & effective TOPS; % of int8 MFMA peak (1 GPU)"
+HBM_PEAK_GBS = 8000.0
+I8_PEAK_TOPS = 5000.0
+FWD_SOURCE = os.path.join(ROOT, "diffusion_transformers_amd", "csrc", "forward.hip")
+
+
+def fwd_bytes(w) -> float:
+    """Algorithmic HBM bytes of one forward launch: each input read once, O written once."""
+    B, H, N, d = w.B, w.H, w.N, w.d
+    W = (d + 31) // 32
+    bits = 2 * B * H * N * W * 4            # Q and K sign words
+    mu = 2 * B * H * N * 4                  # mu_q, mu_k
+    vq = B * H * N * d                      # int8 V^
+    vs = B * H * d * 4                      # V scales
+    esz = 2 if w.dtype == "f16" else 4
+    if w.bias == "dense":
+        bias = H * N * N * esz              # shared over the batch
+    elif w.bias == "relpos":
+        gh, gw = w.grid
+        bias = H * (2 * gh - 1) * (2 * gw - 1) * esz
+    else:
+        bias = 0
+    out = B * H * N * d * esz
+    return float(bits + mu + vq + vs + bias + out)
+
+
+def step_bytes(w) -> float:
+    """Algorithmic HBM bytes of a whole step (pack Q, pack K, quantise V, forward)."""
+    B, H, N, d = w.B, w.H, w.N, w.d
+    esz = 2 if w.dtype == "f16" else 4
+    W = (d + 31) // 32
+    pack = 2 * (B * H * N * d * esz + B * H * N * (4 * W + 4))
+    quant = B * H * N * d * esz + B * H * N * d + B * H * d * 4
+    return float(pack + quant + fwd_bytes(w))
+
+
+def stored_traffic(workload: str):
+    """HBM traffic per forward launch from the committed rocprofv3 PMC summary, or None when
+    that summary was taken on a different forward kernel source."""
+    path = os.path.join(ROOT, "profiles", f"forward_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(FWD_SOURCE, "rb").read()).hexdigest()[:16]
+    if kv.get("forward_source_sha256_16") != sha or "traffic_bytes_per_launch" not in kv:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def cpu_baseline(inp, w, seconds: float):
+    import numpy as np
+
+    import oracle
+    q, k, v = (np.ascontiguousarray(inp[n], dtype=np.float64) for n in ("q", "k", "v"))
+    bias = None if inp["bias"] is None else np.ascontiguousarray(inp["bias"], dtype=np.float64)
+    kind = {"none": oracle.BIAS_NONE, "dense": oracle.BIAS_DENSE, "relpos": oracle.BIAS_RELPOS}[w.bias]
+    grid = w.grid or None
+    # bound the sample: whole batch when one oracle step is cheap, else a prefix of the batch
+    per_item = w.H * w.N * w.N * (w.d + 8)
+    nb = max(1, min(w.B, int(2e9 // max(per_item, 1))))
+    qs, ks, vs = q[:nb], k[:nb], v[:nb]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(qs, ks, vs, bias, kind, grid=grid)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or el >= 30.0:
+            break
+    ops = 4.0 * nb * w.H * w.N * w.N * w.d * reps
+    return {"value": ops / el / 1e12, "unit": "TOPS", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{reps} oracle pass(es) of the whole hot path (pack, quantise, forward) over "
+                      f"{nb} of {w.B} batch items of {w.name}, {el:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="deit_s_224")
+    ap.add_argument("--rotate", type=int, default=8, help="input sets cycled through the timed steps")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (PMC scaling reference) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py: this build runs on one GPU only; --gpus above 1 is not supported "
+                  "(the forward shards by (batch, head) with no communication; see the design notes).",
+                  file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from diffusion_transformers_amd import binding as b
+    from diffusion_transformers_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                          "dispatches": 5}))
+        return
+
+    w = W.BY_NAME[args.workload]
+    sets = []
+    for r in range(max(1, args.rotate)):
+        inp = W.make(w, seed=W.WORKLOADS.index(w) + 1000 * r)
+        q, k, v = (torch.from_numpy(inp[n]).to(dev) for n in ("q", "k", "v"))
+        bias, kind, grid = None, b.BIAS_NONE, None
+        if w.bias == "dense":
+            bias, kind = b.aligned_dense_bias(torch.from_numpy(inp["bias"]).to(dev)), b.BIAS_DENSE
+        elif w.bias == "relpos":
+            bias, kind, grid = torch.from_numpy(inp["bias"]).to(dev), b.BIAS_RELPOS, w.grid
+        qb, qm = b.pack_qk(q)
+        kb, km = b.pack_qk(k)
+        vq, vs = b.quant_v(v)
+        out_dt = torch.float16 if w.dtype == "f16" else torch.float32
+        o = torch.empty((w.B, w.H, w.N, w.d), dtype=out_dt, device=dev)
+        sets.append(dict(inp=inp if r == 0 else None, q=q, k=k, v=v, bias=bias, kind=kind, grid=grid,
+                         qb=qb, qm=qm, kb=kb, km=km, vq=vq, vs=vs, o=o))
+    torch.cuda.synchronize()
+
+    def step(s):
+        b.pack_qk(s["q"], s["qb"], s["qm"])
+        b.pack_qk(s["k"], s["kb"], s["km"])
+        b.quant_v(s["v"], s["vq"], s["vs"])
+        b.forward(s["qb"], s["qm"], s["kb"], s["km"], s["vq"], s["vs"], w.d, s["bias"], s["kind"], s["grid"],
+                  out=s["o"])
+
+    def capture(fn):
+        """Capture fn() into a HIP graph on a side stream (default priority)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    nset = len(sets)
+    # one graph holds one step per input set; K steps = K / nset replays
+    reps = max(1, -(-args.steps // nset))
+    steps = reps * nset
+    step_graph = capture(lambda: [step(st) for st in sets])
+    fwd_graph = capture(lambda: [b.forward(st["qb"], st["qm"], st["kb"], st["km"], st["vq"], st["vs"], w.d,
+                                           st["bias"], st["kind"], st["grid"], out=st["o"]) for st in sets])
+
+    for i in range(max(1, args.warmup // nset)):
+        step_graph.replay()
+    torch.cuda.synchronize()
+
+    def timed(fn, n):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(n):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
+
+    # timed region: exactly `steps` steps, bracketed by synchronisation
+    step_ms = timed(step_graph.replay, reps) / steps
+    # forward kernel alone: average launch duration over the same number of launches
+    fwd_ms = timed(fwd_graph.replay, reps) / steps
+    # eager launches through the ABI (host launch cost included), for reference
+    eager_ms = timed(lambda: [step(st) for st in sets], reps) / steps
+
+    ops = w.ops()
+    fb = fwd_bytes(w)
+    t_mfma = ops / (I8_PEAK_TOPS * 1e12)
+    t_hbm = fb / (HBM_PEAK_GBS * 1e9)
+    fwd_s = fwd_ms * 1e-3
+    if t_hbm >= t_mfma:
+        achieved = fb / fwd_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        achieved = ops / fwd_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": I8_PEAK_TOPS, "unit": "TOPS",
+                "frac": achieved / I8_PEAK_TOPS}
+    roof["traffic"] = stored_traffic(w.name)
+    roof["kernel"] = "binattn_fwd_kernel"
+    roof["algorithmic_bytes_per_launch"] = fb
+    roof["mfma_frac"] = ops / fwd_s / 1e12 / I8_PEAK_TOPS
+    roof["hbm_frac"] = fb / fwd_s / 1e9 / HBM_PEAK_GBS
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(sets[0]["inp"], w, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": ops / (step_ms * 1e-3) / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": max(1, args.warmup // nset) * nset,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "input_dtype": w.dtype,
+                   "bias": w.bias, "rotated_input_sets": len(sets)},
+        "fwd_ms_per_call": fwd_ms,
+        "eager_ms_per_step": eager_ms,
+        "timing": "HIP events around graph replays; one graph = one step per rotated input set",
+        "fwd_effective_tops": ops / fwd_s / 1e12,
+        "step_hbm_gbs": step_bytes(w) / (step_ms * 1e-3) / 1e9,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -29,7 +29,9 @@ def hipcc() -> str:
 
 def common_flags():
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument",
+            # MFMA results straight into VGPRs (the softmax consumes them on the VALU)
+            "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def build(verbose: bool = False, extra_flags=None) -> str:

@@ -105,7 +105,7 @@ int binattn_forward(const uint32_t* q_bits, const float* q_mu, const uint32_t* k
             if (!bias) return BINATTN_EINVAL;
             if (!dtype_ok(bias_dtype)) return BINATTN_EUNSUPPORTED;
             if (grid_h <= 0 || grid_w <= 0 || (int64_t)grid_h * grid_w != N) return BINATTN_EINVAL;
-            if (grid_w % 16 != 0 || grid_w > 512) return BINATTN_EUNSUPPORTED;
+            if (grid_w % 16 != 0 || !relpos_window_fits(grid_w)) return BINATTN_EUNSUPPORTED;
             if (!aligned16(bias)) return BINATTN_EALIGN;
             break;
         default:

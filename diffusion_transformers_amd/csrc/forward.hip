@@ -7,23 +7,30 @@
 //                 integer PV product, float dequantisation;
 //   hardware implementation bullet: one FlashAttention2-style tiled kernel.
 //
-// gfx950 design (one workgroup = 4 waves = 128 queries of one (b,h); key tiles of 64):
-//  * QK^T on the int8 MFMA (v_mfma_i32_16x16x64_i8) with sign bits unpacked to
-//    +-1 bytes: exact integer D.  The tile is computed transposed (keys are MFMA
-//    rows, queries columns) and the key rows are permuted so that lane (query n,
-//    group g) ends up holding the 16 consecutive keys 16g..16g+15 of the tile for
-//    query n -- exactly the A-operand layout of the PV MFMA, so P never leaves
-//    registers, and the per-lane bias run is contiguous in memory.
-//  * K bits are unpacked once per workgroup per tile into LDS in MFMA-operand
-//    order (each lane reads 16 consecutive bytes); V^ (channel-major in HBM) is
-//    staged the same way.
+// gfx950 design (one workgroup = 4 waves x 16 queries of one (b,h); key tiles of 64):
+//  * QK^T on the fp8 MFMA (v_mfma_f32_16x16x128_f8f6f4; one instruction covers d <= 128).
+//    With s = +-1 query signs and b = 0/1 key bits, s.t = sum s (2b - 1) = 2 s.b - sum(s):
+//    the K operand is the bits as fp8 {0, 1}, the Q operand is fp8 {+-2}, and the
+//    accumulator is seeded with -sum(s) of the lane's query.  Every product and partial
+//    sum is a small integer, so the fp32 result is D exactly, already in float.
+//  * The tile is computed transposed (keys are MFMA rows, queries columns) and the
+//    key rows are permuted so that lane (query n, group g) holds the 16 consecutive
+//    keys 16g..16g+15 of the tile for query n -- exactly the A-operand layout of the
+//    int8 PV MFMA, so P never leaves registers, and the per-lane bias run is contiguous.
+//  * K bits are unpacked once per workgroup per tile into LDS in MFMA-operand order
+//    (each lane reads 32 consecutive bytes); V^ (channel-major in HBM) is staged the
+//    same way.  LDS is double-buffered and the loads of tile t+1 are issued before
+//    tile t is computed: one barrier per tile.  All global reads go through buffer
+//    resources rebased per tile on the scalar unit, so addresses cost no vector ALU
+//    and reads past a head's end return zero.
 //  * Online softmax in fp32 with the running max reduced over the 4 lanes that
-//    share a query.  p = 255 * exp(S - m) = exp2(S*log2e - m*log2e + log2 255),
-//    P^ = rint(p) via v_cvt_pk_u8_f32.
-//  * PV with signed int8 MFMA: sum (P^-128) V^ + 128 sum V^, the column sum coming
-//    from one extra MFMA against a ones operand.  The int32 accumulators run on
-//    across tiles while no row max in the wave changes; when one does, the wave
-//    folds them into fp32 accumulators rescaled by exp(m_old - m_new).
+//    share a query (row-swap permutes).  p = 255 exp(S - m) =
+//    exp2(S log2e - m log2e + log2 255), P^ = rint(p) via v_cvt_pk_u8_f32.
+//  * PV with signed int8 MFMA: sum P^ V^ = sum (P^-128) V^ + 2 * sum 64 V^; the two
+//    64-weighted column sums are two more MFMAs into the same accumulator.
+//    Short rows fold each tile's int32 result into the fp32 accumulator (with the
+//    running-max rescale); long rows keep accumulating in int32 across tiles and
+//    fold only when some row max in the wave moves.
 //  * Epilogue: O = acc * vscale_c / sum(p).
 #include "common.h"
 #include "internal.h"
@@ -31,10 +38,10 @@
 namespace binattn {
 
 constexpr int kWaves = 4;
-constexpr int kCB = 2;                      // 16-query column blocks per wave
-constexpr int kBR = kWaves * kCB * 16;      // queries per workgroup
+constexpr int kBR = kWaves * 16;            // queries per workgroup (16 per wave)
 constexpr int kBC = 64;                     // keys per tile
-constexpr int kRelposWin = 3072;            // fp32 entries of the staged relative-position window
+constexpr int kRelposWin = 1024;            // fp32 entries of the per-tile relative-position window
+constexpr int kDeferTiles = 16;             // rows of at least this many tiles accumulate in int32
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2_255 = 7.99435343685886f;
 
@@ -47,88 +54,323 @@ __device__ __forceinline__ int key_slot(int j, int& t) {
     return 4 * (j >> 4) + (j & 3);
 }
 
-template <int KC>
-struct KTile {
-    // [kc][t][lane] x 16 bytes: the A operand of QK MFMA (kc, t) for each lane.
-    uint32_t w[KC * 4 * kWave * 4];
+// Raw global data of one tile held in registers between its load and its LDS store.
+template <int NT, int BIAS>
+struct TileRegs {
+    static constexpr int W = (NT + 1) / 2;                 // sign words per key
+    static constexpr int KT = (kBC * W + 255) / 256;       // K word tasks per thread
+    static constexpr int VCH = (NT * 64 + 255) / 256;      // 16-byte V^ chunks per thread
+    static constexpr int TW = BIAS == BK_RELPOS ? kRelposWin / 256 : 1;
+    uint32_t kw[KT];
+    uint4 v[VCH];
+    float mu;
+    float tw[TW];
 };
 
-// Unpack the K sign bits of keys [j0, j0+64) into LDS operand order (+-1 int8, zero for
-// channels >= d and keys >= N).
-template <int KC>
-__device__ __forceinline__ void stage_k(const uint32_t* __restrict__ kb, int N, int d, int W, int j0,
-                                        KTile<KC>& sK) {
-    for (int id = threadIdx.x; id < kBC * 4 * KC; id += 256) {
-        const int j = id / (4 * KC), grp = id % (4 * KC);
-        const int kc = grp >> 2, g = grp & 3;
-        const int ch0 = 64 * kc + 16 * g;
-        uint32_t word = 0;
-        if (j0 + j < N && ch0 < d) word = kb[(int64_t)(j0 + j) * W + (ch0 >> 5)];
-        uint32_t o[4];
-        unpack_signs16((word >> (ch0 & 16)) & 0xFFFFu, o);
-        const bool live = j0 + j < N;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = (live && ch0 + 4 * q < d) ? o[q] : 0u;
-        int t;
-        const int m = key_slot(j, t);
-        const int lane = m + 16 * g;
-        uint4* dst = reinterpret_cast<uint4*>(&sK.w[((kc * 4 + t) * kWave + lane) * 4]);
-        *dst = make_uint4(o[0], o[1], o[2], o[3]);
-    }
+// LDS of one pipeline stage (a multiple of 16 bytes, so both stages keep 16-byte alignment).
+template <int NT, int BIAS>
+struct alignas(16) TileLds {
+    static constexpr int W = (NT + 1) / 2;
+    uint32_t k[4 * 4 * 16 * 8];            // [t][group][row] x 32 B: A operand of QK MFMA t, lane (row, group);
+                                           // groups >= W stay zero
+    uint32_t v[NT * kWave * 4];            // [ct][lane] x 16 B: B operand of PV MFMA ct
+    float mu[kBC];
+    float tw[BIAS == BK_RELPOS ? kRelposWin : 4];
+};
+
+struct RelposWin {
+    int dr_lo, row_len, count;
+};
+
+// Rows of the relative-position table touched by queries [q0, q0+kBR) and keys [j0, j0+kBC).
+__device__ __forceinline__ RelposWin relpos_window(int q0, int j0, int N, int gh, int gw) {
+    const int ri_min = q0 / gw, ri_max = (min(q0 + kBR, N) - 1) / gw;
+    const int rj_min = j0 / gw, rj_max = (min(j0 + kBC, N) - 1) / gw;
+    RelposWin w;
+    w.dr_lo = ri_min - rj_max + gh - 1;
+    w.row_len = 2 * gw - 1;
+    w.count = ((ri_max - ri_min) + (rj_max - rj_min) + 1) * w.row_len;
+    return w;
 }
 
-// Q operand (B of the QK MFMA) for one lane: query row, channels 64kc + 16g .. +15.
-template <int KC>
-__device__ __forceinline__ void load_q(const uint32_t* __restrict__ qrow, bool live, int d, int g, v4i q[KC]) {
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-        const int ch0 = 64 * kc + 16 * g;
-        uint32_t word = (live && ch0 < d) ? qrow[ch0 >> 5] : 0u;
-        uint32_t o[4];
-        unpack_signs16((word >> (ch0 & 16)) & 0xFFFFu, o);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) q[kc][c] = (live && ch0 + 4 * c < d) ? (int)o[c] : 0;
-    }
-}
+// Per-workgroup pointers of one (b, h).
+struct HeadPtrs {
+    const uint32_t* kb;
+    const float* kmu;
+    const int8_t* vq;
+    const void* table;  // relative-position table of head h
+};
 
-template <int KC>
-__device__ __forceinline__ void qk_tile(const KTile<KC>& sK, const v4i q[KC], int lane, v4i D[4]) {
+template <int NT, int BIAS>
+__device__ __forceinline__ void load_tile(TileRegs<NT, BIAS>& r, const FwdArgs& a, const HeadPtrs& hp, int q0,
+                                          int j0) {
+    typedef TileRegs<NT, BIAS> R;
+    const int tid = threadIdx.x, N = a.N, d = a.d;
+    // sign words of keys j0.. (keys >= N read as 0)
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(hp.kb + j0 * R::W, (N - j0) * R::W * 4);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        D[t] = v4i{0, 0, 0, 0};
+    for (int i = 0; i < R::KT; ++i)
+        r.kw[i] = __builtin_amdgcn_raw_buffer_load_b32(kr, (tid + 256 * i) * 4, 0, 0);
+    // V^ columns j0 .. j0+63 of every channel (channels >= d read as 0)
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(hp.vq + j0, d * (int)a.ldv - j0);
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            const v4i a = *reinterpret_cast<const v4i*>(&sK.w[((kc * 4 + t) * kWave + lane) * 4]);
-            D[t] = mfma_i8(a, q[kc], D[t]);
+    for (int i = 0; i < R::VCH; ++i) {
+        const int id = tid + 256 * i;
+        const int c = id >> 2, gg = id & 3;
+        const v4i x = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(vr, (int)(c * a.ldv) + 16 * gg, 0, 0));
+        r.v[i] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
+    const __amdgpu_buffer_rsrc_t mr = buffer_rsrc(hp.kmu + j0, (N - j0) * 4);
+    r.mu = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mr, (tid & 63) * 4, 0, 0));
+    if (BIAS == BK_RELPOS) {
+        const RelposWin w = relpos_window(q0, j0, N, a.gh, a.gw);
+        const int tsz = (2 * a.gh - 1) * w.row_len;
+        const int off = w.dr_lo * w.row_len;
+        if (a.bias_f32) {
+            const __amdgpu_buffer_rsrc_t tr = buffer_rsrc((const float*)hp.table + off, (tsz - off) * 4);
+#pragma unroll
+            for (int i = 0; i < r.TW; ++i)
+                r.tw[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(tr, (tid + 256 * i) * 4, 0, 0));
+        } else {
+            const __amdgpu_buffer_rsrc_t tr = buffer_rsrc((const _Float16*)hp.table + off, (tsz - off) * 2);
+#pragma unroll
+            for (int i = 0; i < r.TW; ++i) {
+                const uint16_t hbits = __builtin_amdgcn_raw_buffer_load_b16(tr, (tid + 256 * i) * 2, 0, 0);
+                r.tw[i] = (float)__builtin_bit_cast(_Float16, hbits);
+            }
         }
     }
 }
 
-__device__ __forceinline__ float quad_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    return fmaxf(v, __shfl_xor(v, 32));
-}
-
-__device__ __forceinline__ float quad_sum(float v) {
-    v += __shfl_xor(v, 16);
-    return v + __shfl_xor(v, 32);
-}
-
 template <int NT, int BIAS>
-__global__ __launch_bounds__(256, 2) void binattn_fwd_kernel(FwdArgs a) {
-    constexpr int KC = (NT + 3) / 4;
-    __shared__ __attribute__((aligned(16))) KTile<KC> sK;
-    __shared__ __attribute__((aligned(16))) uint32_t sV[NT * kWave * 4];
-    __shared__ __attribute__((aligned(16))) float sMu[kBC];
-    __shared__ float sT[BIAS == BK_RELPOS ? kRelposWin : 1];
+__device__ __forceinline__ void store_tile(const TileRegs<NT, BIAS>& r, TileLds<NT, BIAS>& s, int d) {
+    typedef TileRegs<NT, BIAS> R;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < R::KT; ++i) {
+        const int id = tid + 256 * i;
+        if (id < kBC * R::W) {
+            const int j = id / R::W, w = id % R::W;
+            uint32_t word = r.kw[i];
+            const int left = d - 32 * w;  // channels >= d contribute nothing
+            if (left < 32) word &= (1u << left) - 1u;
+            uint32_t o[8];
+            unpack_bits32_f8(word, o);
+            int t;
+            const int m = key_slot(j, t);
+            uint32_t* dst = &s.k[((t * 4 + w) * 16 + m) * 8];
+            *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<uint4*>(dst + 4) = make_uint4(o[4], o[5], o[6], o[7]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < R::VCH; ++i) {
+        const int id = tid + 256 * i;
+        if (id < NT * 64) {
+            const int c = id >> 2, gg = id & 3;
+            *reinterpret_cast<uint4*>(&s.v[((c >> 4) * kWave + (c & 15) + 16 * gg) * 4]) = r.v[i];
+        }
+    }
+    if (tid < kBC) s.mu[tid] = r.mu;
+    if (BIAS == BK_RELPOS) {
+#pragma unroll
+        for (int i = 0; i < r.TW; ++i) s.tw[tid + 256 * i] = r.tw[i];
+    }
+}
 
-    const int N = a.N, d = a.d, W = a.W;
+// Zero the K-operand rows of channel groups >= W (they are never written by store_tile).
+template <int NT, int BIAS>
+__device__ __forceinline__ void zero_unused_groups(TileLds<NT, BIAS>& s) {
+    constexpr int W = (NT + 1) / 2;
+    if (W < 4) {
+        for (int id = threadIdx.x; id < 4 * (4 - W) * 16 * 2; id += 256) {
+            const int half = id & 1, m = (id >> 1) & 15, tg = id >> 5;
+            const int t = tg / (4 - W), gg = W + tg % (4 - W);
+            *reinterpret_cast<uint4*>(&s.k[((t * 4 + gg) * 16 + m) * 8 + 4 * half]) = make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
+// Q operand (B of the QK MFMA) for one lane: fp8 2*sign of channels 32g .. 32g+31 (0 past d);
+// returns -sum of the query's d signs (the accumulator seed), 0 for a query past N.
+template <int W>
+__device__ __forceinline__ float load_q(const uint32_t* __restrict__ qrow, bool live, int d, int g, v8i& q) {
+    uint32_t o[8];
+    const uint32_t word = (live && g < W) ? qrow[g] : 0u;
+    unpack_signs32_f8x2(word, o);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) q[c] = (live && g < W && 32 * g + 4 * c < d) ? (int)o[c] : 0;
+    int pos = 0;
+    if (live) {
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const int left = d - 32 * w;
+            const uint32_t mask = left >= 32 ? 0xFFFFFFFFu : ((1u << left) - 1u);
+            pos += __builtin_popcount(qrow[w] & mask);
+        }
+    }
+    return live ? (float)(d - 2 * pos) : 0.0f;  // -(pos - (d - pos))
+}
+
+// Dense bias of one lane for one tile: its query row, keys jg .. jg+15 (raw fp16 or fp32 words).
+template <int BIAS>
+struct BiasRegs {
+    static constexpr int NV = BIAS == BK_DENSE_F32 ? 4 : (BIAS == BK_DENSE_F16 ? 2 : 1);
+    v4i w[NV];
+};
+
+// rows: buffer over this wave's 16 query rows starting at key column j0 (rows past N read 0).
+template <int BIAS>
+__device__ __forceinline__ void load_bias(BiasRegs<BIAS>& b, __amdgpu_buffer_rsrc_t rows, int voff) {
+    if (BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32) {
+#pragma unroll
+        for (int k = 0; k < BiasRegs<BIAS>::NV; ++k)
+            b.w[k] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rows, voff + 16 * k, 0, 0));
+    }
+}
+
+template <int BIAS>
+__device__ __forceinline__ float bias_at(const BiasRegs<BIAS>& b, int k) {
+    if (BIAS == BK_DENSE_F16) {
+        const uint32_t word = (uint32_t)b.w[k >> 3][(k >> 1) & 3];
+        const uint16_t bits16 = (k & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
+        return (float)__builtin_bit_cast(_Float16, bits16);
+    } else {
+        return __int_as_float(b.w[k >> 2][k & 3]);
+    }
+}
+
+// Per-wave state carried across key tiles.
+template <int NT>
+struct WaveState {
+    v8i qop;
+    v4f dseed;                 // accumulator seed: -sum of the query's signs
+    float cq, mrun, lpart;
+    int qi;
+    bool live;                 // some query of this wave is < N (wave-uniform)
+    v4i acci[NT];              // deferred int32 PV accumulators (long rows)
+    v4f accf[NT];
+};
+
+template <int NT, int BIAS, bool DEFER>
+__device__ __forceinline__ void tile_body(const FwdArgs& a, TileLds<NT, BIAS>& s, WaveState<NT>& st,
+                                          const BiasRegs<BIAS>& bcur, int tile, int ntiles, int q0) {
+    constexpr int W = (NT + 1) / 2;
+    const int N = a.N;
+    const int lane = threadIdx.x & 63, g = lane >> 4, m16 = lane & 15;
+    const int j0 = tile * kBC;
+    const int jg = j0 + 16 * g;  // first key of this lane's run
+
+    // ---- QK^T: D exactly, in fp32
+    v4f D[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t* src = &s.k[((t * 4 + g) * 16 + m16) * 8];
+        const v4i lo = *reinterpret_cast<const v4i*>(src);
+        const v4i hi = *reinterpret_cast<const v4i*>(src + 4);
+        const v8i kop = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        D[t] = mfma_f8(kop, st.qop, st.dseed);
+    }
+    // ---- scale + bias
+    float muk[16];
+#pragma unroll
+    for (int k = 0; k < 16; k += 4) {
+        const float4 m4 = *reinterpret_cast<const float4*>(&s.mu[16 * g + k]);
+        muk[k] = m4.x; muk[k + 1] = m4.y; muk[k + 2] = m4.z; muk[k + 3] = m4.w;
+    }
+    int idx0 = 0;
+    if (BIAS == BK_RELPOS) {
+        const RelposWin w = relpos_window(q0, j0, N, a.gh, a.gw);
+        const int gw = a.gw;
+        const int ri = st.qi / gw, ci = st.qi % gw;
+        const int rj = jg / gw, cj = jg % gw;
+        idx0 = (ri - rj + a.gh - 1 - w.dr_lo) * w.row_len + (ci - cj + gw - 1);
+        if (jg >= N) idx0 = 15;  // the whole run is past N and masked below; keep reads in the window
+    }
+    float sc[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        float b = 0.0f;
+        if (BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32) b = bias_at<BIAS>(bcur, k);
+        if (BIAS == BK_RELPOS) b = s.tw[idx0 - k];
+        sc[k] = __builtin_fmaf(D[k >> 2][k & 3] * muk[k], st.cq, b);
+    }
+    if (tile == ntiles - 1) {  // ragged tail: keys >= N take no weight
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            if (jg + k >= N) sc[k] = -INFINITY;
+    }
+    // ---- running max over the 64 keys of the tile (4 lanes share a query)
+    float mloc = sc[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) mloc = fmaxf(mloc, sc[k]);
+    const float mnew = fmaxf(st.mrun, rows4_max(mloc));
+    const bool up = __any(mnew > st.mrun);
+    float ar[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // rescale of the O rows this lane holds (queries 4g + r)
+    if (up) {
+        const float alpha = fast_exp2((st.mrun - mnew) * kLog2e);  // 0 on the first tile
+        st.lpart *= alpha;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r);
+        if (DEFER) {
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st.accf[ct][r] = (st.accf[ct][r] + (float)st.acci[ct][r]) * ar[r];
+                st.acci[ct] = v4i{0, 0, 0, 0};
+            }
+        }
+    }
+    st.mrun = mnew;
+
+    // ---- P^ = rint(255 exp(S - m)) - 128 as int8, row sums, integer PV
+    const float negm = kLog2_255 - mnew * kLog2e;
+    v4i pw;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float p = fast_exp2(__builtin_fmaf(sc[4 * t + r], kLog2e, negm));
+            lsum += p;
+            word = __builtin_amdgcn_cvt_pk_u8_f32(p, r, word);
+        }
+        pw[t] = (int)(word ^ 0x80808080u);
+    }
+    st.lpart += lsum;
+    const v4i c64 = v4i{0x40404040, 0x40404040, 0x40404040, 0x40404040};
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+        const v4i vop = *reinterpret_cast<const v4i*>(&s.v[(ct * kWave + lane) * 4]);
+        if (DEFER) {
+            v4i acc = mfma_i8(pw, vop, st.acci[ct]);
+            acc = mfma_i8(c64, vop, acc);
+            st.acci[ct] = mfma_i8(c64, vop, acc);
+        } else {
+            v4i acc = mfma_i8(pw, vop, v4i{0, 0, 0, 0});
+            acc = mfma_i8(c64, vop, acc);
+            acc = mfma_i8(c64, vop, acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st.accf[ct][r] = __builtin_fmaf(st.accf[ct][r], ar[r], (float)acc[r]);
+        }
+    }
+}
+
+template <int NT, int BIAS, bool DEFER>
+__global__ __launch_bounds__(256) void binattn_fwd_kernel(FwdArgs a) {
+    constexpr int W = (NT + 1) / 2;
+    typedef TileRegs<NT, BIAS> Regs;
+    typedef TileLds<NT, BIAS> Lds;
+    __shared__ Lds lds[2];
+
+    const int N = a.N, d = a.d;
     const int nqb = (N + kBR - 1) / kBR;
     const int nblk = a.B * a.H * nqb;
     const int lb = xcd_logical_block(blockIdx.x, nblk);
     int bh, qb;
     if (BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32) {
-        // dense bias is shared over the batch: keep the batch items of one (h, query block) together
+        // the dense bias is shared over the batch: keep the batch items of one (h, query block) together
         const int b = lb % a.B, hq = lb / a.B;
         qb = hq % nqb;
         bh = b * a.H + hq / nqb;
@@ -137,277 +379,176 @@ __global__ __launch_bounds__(256, 2) void binattn_fwd_kernel(FwdArgs a) {
         qb = lb % nqb;
     }
     const int h = bh % a.H;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, n16 = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: keeps row pointers scalar
     const int q0 = qb * kBR;
 
-    const uint32_t* kbh = a.kbits + (int64_t)bh * N * W;
-    const float* kmuh = a.kmu + (int64_t)bh * N;
-    const int8_t* vqh = a.vq + (int64_t)bh * d * a.ldv;
+    HeadPtrs hp;
+    hp.kb = a.kbits + (int64_t)bh * N * W;
+    hp.kmu = a.kmu + (int64_t)bh * N;
+    hp.vq = a.vq + (int64_t)bh * d * a.ldv;
+    hp.table = nullptr;
+    if (BIAS == BK_RELPOS) {
+        const int64_t tsz = (int64_t)(2 * a.gh - 1) * (2 * a.gw - 1);
+        hp.table = a.bias_f32 ? (const void*)((const float*)a.bias + h * tsz)
+                              : (const void*)((const _Float16*)a.bias + h * tsz);
+    }
 
-    // per column block: Q operand, row scale, running max, partial row sum
-    v4i qop[kCB][KC];
-    float cq[kCB], mrun[kCB], lpart[kCB];
-    int qi[kCB];
-#pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-        const int i = q0 + (wave * kCB + cb) * 16 + n16;
+    WaveState<NT> st;
+    const int qw0 = q0 + wave * 16;  // first query of this wave
+    {
+        const int i = qw0 + n16;
         const bool live = i < N;
-        qi[cb] = live ? i : N - 1;
-        load_q<KC>(a.qbits + ((int64_t)bh * N + qi[cb]) * W, live, d, g, qop[cb]);
-        cq[cb] = live ? a.qmu[(int64_t)bh * N + i] * a.qk_scale : 0.0f;
-        mrun[cb] = -INFINITY;
-        lpart[cb] = 0.0f;
-    }
-    v4i acci[kCB][NT], cs[NT];
-    v4f accf[kCB][NT];
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-        cs[ct] = v4i{0, 0, 0, 0};
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb) {
-            acci[cb][ct] = v4i{0, 0, 0, 0};
-            accf[cb][ct] = v4f{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-    const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
-
-    const int ntiles = (N + kBC - 1) / kBC;
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int j0 = tile * kBC;
-        // ---- stage K operand, V^ operand, mu_k (and the relative-position window)
-        stage_k<KC>(kbh, N, d, W, j0, sK);
-        for (int id = tid; id < NT * 16 * 4; id += 256) {
-            const int c = id >> 2, gg = id & 3;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (c < d) val = *reinterpret_cast<const uint4*>(vqh + (int64_t)c * a.ldv + j0 + 16 * gg);
-            const int ln = (c & 15) + 16 * gg;
-            *reinterpret_cast<uint4*>(&sV[((c >> 4) * kWave + ln) * 4]) = val;
-        }
-        if (tid < kBC) sMu[tid] = (j0 + tid < N) ? kmuh[j0 + tid] : 0.0f;
-        int dr_lo = 0, row_len = 0;
-        if (BIAS == BK_RELPOS) {
-            const int gw = a.gw;
-            const int ri_min = q0 / gw, ri_max = (min(q0 + kBR, N) - 1) / gw;
-            const int rj_min = j0 / gw, rj_max = (min(j0 + kBC, N) - 1) / gw;
-            dr_lo = ri_min - rj_max + a.gh - 1;
-            const int rows = (ri_max - ri_min) + (rj_max - rj_min) + 1;
-            row_len = 2 * gw - 1;
-            const int64_t tsz = (int64_t)(2 * a.gh - 1) * row_len;
-            const int64_t base = (int64_t)h * tsz + (int64_t)dr_lo * row_len;
-            for (int id = tid; id < rows * row_len; id += 256)
-                sT[id] = a.bias_f32 ? ((const float*)a.bias)[base + id] : (float)((const _Float16*)a.bias)[base + id];
-        }
-        __syncthreads();
-
-        // ---- QK^T (exact integers), scale + bias, running max
-        v4i kop[KC][4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc)
-                kop[kc][t] = *reinterpret_cast<const v4i*>(&sK.w[((kc * 4 + t) * kWave + lane) * 4]);
-        float muk[16];
-#pragma unroll
-        for (int k = 0; k < 16; k += 4) {
-            const float4 m4 = *reinterpret_cast<const float4*>(&sMu[16 * g + k]);
-            muk[k] = m4.x; muk[k + 1] = m4.y; muk[k + 2] = m4.z; muk[k + 3] = m4.w;
-        }
-        const int jg = j0 + 16 * g;  // first key of this lane's run
-        const bool last = (tile == ntiles - 1);
-        float s[kCB][16];
-        float mnew[kCB];
-        bool any_up = false;
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb) {
-            v4i D[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                D[t] = v4i{0, 0, 0, 0};
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) D[t] = mfma_i8(kop[kc][t], qop[cb][kc], D[t]);
-            }
-            float bia[16];
-            if (BIAS == BK_DENSE_F16) {
-                const _Float16* br = (const _Float16*)a.bias + ((int64_t)h * N + qi[cb]) * a.bias_ld + jg;
-                const h8 zero8 = h8{0, 0, 0, 0, 0, 0, 0, 0};
-                const h8 lo = (jg < N) ? *reinterpret_cast<const h8*>(br) : zero8;
-                const h8 hi = (jg + 8 < N) ? *reinterpret_cast<const h8*>(br + 8) : zero8;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) { bia[k] = (float)lo[k]; bia[k + 8] = (float)hi[k]; }
-            } else if (BIAS == BK_DENSE_F32) {
-                const float* br = (const float*)a.bias + ((int64_t)h * N + qi[cb]) * a.bias_ld + jg;
-#pragma unroll
-                for (int k = 0; k < 16; k += 4) {
-                    const float4 f4 = (jg + k < N) ? *reinterpret_cast<const float4*>(br + k) : make_float4(0, 0, 0, 0);
-                    bia[k] = f4.x; bia[k + 1] = f4.y; bia[k + 2] = f4.z; bia[k + 3] = f4.w;
-                }
-            } else if (BIAS == BK_RELPOS) {
-                const int gw = a.gw;
-                const int ri = qi[cb] / gw, ci = qi[cb] % gw;
-                const int rj = jg / gw, cj = jg % gw;
-                const int idx0 = (ri - rj + a.gh - 1 - dr_lo) * row_len + (ci - cj + gw - 1);
-                if (jg < N) {
-#pragma unroll
-                    for (int k = 0; k < 16; ++k) bia[k] = sT[idx0 - k];
-                } else {
-#pragma unroll
-                    for (int k = 0; k < 16; ++k) bia[k] = 0.0f;
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < 16; ++k) bia[k] = 0.0f;
-            }
-            float mloc = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const float x = (float)D[k >> 2][k & 3] * muk[k];
-                float sv = __builtin_fmaf(x, cq[cb], bia[k]);
-                if (last && jg + k >= N) sv = -INFINITY;
-                s[cb][k] = sv;
-                mloc = fmaxf(mloc, sv);
-            }
-            mloc = quad_max(mloc);
-            mnew[cb] = fmaxf(mrun[cb], mloc);
-            any_up |= mnew[cb] > mrun[cb];
-        }
-
-        // ---- the row max moved somewhere in the wave: fold int32 partials into fp32, rescaled
-        if (__any(any_up)) {
-#pragma unroll
-            for (int cb = 0; cb < kCB; ++cb) {
-                const float alpha = fast_exp2((mrun[cb] - mnew[cb]) * kLog2e);  // 0 on the first tile
-                lpart[cb] *= alpha;
-                float ar[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r);
-#pragma unroll
-                for (int ct = 0; ct < NT; ++ct) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int tot = acci[cb][ct][r] + 128 * cs[ct][r];
-                        accf[cb][ct][r] = (accf[cb][ct][r] + (float)tot) * ar[r];
-                    }
-                    acci[cb][ct] = v4i{0, 0, 0, 0};
-                }
-            }
-#pragma unroll
-            for (int ct = 0; ct < NT; ++ct) cs[ct] = v4i{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb) mrun[cb] = mnew[cb];
-
-        // ---- P^ = rint(255 exp(S - m)) - 128 as int8, row sums, integer PV
-        v4i vop[NT];
+        st.live = qw0 < N;
+        st.qi = live ? i : N - 1;
+        const float seed = load_q<W>(a.qbits + ((int64_t)bh * N + st.qi) * W, live, d, g, st.qop);
+        st.dseed = v4f{seed, seed, seed, seed};
+        st.cq = live ? a.qmu[(int64_t)bh * N + i] * a.qk_scale : 0.0f;
+        st.mrun = -INFINITY;
+        st.lpart = 0.0f;
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
-            vop[ct] = *reinterpret_cast<const v4i*>(&sV[(ct * kWave + lane) * 4]);
-            cs[ct] = mfma_i8(ones, vop[ct], cs[ct]);
+            st.acci[ct] = v4i{0, 0, 0, 0};
+            st.accf[ct] = v4f{0.f, 0.f, 0.f, 0.f};
         }
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb) {
-            const float negm = kLog2_255 - mrun[cb] * kLog2e;
-            v4i pw;
-            float lsum = 0.0f;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                uint32_t word = 0;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = fast_exp2(__builtin_fmaf(s[cb][4 * t + r], kLog2e, negm));
-                    lsum += p;
-                    word = __builtin_amdgcn_cvt_pk_u8_f32(p, r, word);
-                }
-                pw[t] = (int)(word ^ 0x80808080u);
-            }
-            lpart[cb] += lsum;
-#pragma unroll
-            for (int ct = 0; ct < NT; ++ct) acci[cb][ct] = mfma_i8(pw, vop[ct], acci[cb][ct]);
-        }
+    }
+    // dense bias rows of this wave: row (h, qw0 + r) at offset r*ld elements; rows >= N read 0
+    const int esz = BIAS == BK_DENSE_F32 ? 4 : 2;
+    const char* brow = nullptr;
+    int brow_bytes = 0;
+    if (BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32) {
+        const int r0 = min(qw0, N);
+        brow = (const char*)a.bias + ((int64_t)h * N + r0) * a.bias_ld * esz;
+        brow_bytes = min(N - r0, 16) * (int)a.bias_ld * esz;  // at most 16 rows: far below 2^31
+    }
+    const int bvoff = (n16 * (int)a.bias_ld + 16 * g) * esz;
+
+    const int ntiles = (N + kBC - 1) / kBC;
+    Regs regs;
+    BiasRegs<BIAS> b0, b1;
+    zero_unused_groups<NT, BIAS>(lds[0]);
+    zero_unused_groups<NT, BIAS>(lds[1]);
+    load_tile<NT, BIAS>(regs, a, hp, q0, 0);
+    load_bias<BIAS>(b0, buffer_rsrc(brow, brow_bytes), bvoff);
+
+    // One pipeline step: stage tile `tile` into LDS, issue the loads of tile+1, compute tile.
+    // Unrolled by two so the two bias register sets alternate without copies.
+    auto step = [&](int tile, BiasRegs<BIAS>& bcur, BiasRegs<BIAS>& bnext) {
+        Lds& s = lds[tile & 1];
+        store_tile<NT, BIAS>(regs, s, d);
         __syncthreads();
+        if (tile + 1 < ntiles) {
+            const int jn = (tile + 1) * kBC;
+            load_tile<NT, BIAS>(regs, a, hp, q0, jn);
+            load_bias<BIAS>(bnext, buffer_rsrc(brow + jn * esz, brow_bytes - jn * esz), bvoff);
+        }
+        if (st.live) tile_body<NT, BIAS, DEFER>(a, s, st, bcur, tile, ntiles, q0);
+    };
+    for (int tile = 0; tile < ntiles; tile += 2) {
+        step(tile, b0, b1);
+        if (tile + 1 < ntiles) step(tile + 1, b1, b0);
     }
 
     // ---- epilogue: O = acc * vscale / sum(p)
+    if (!st.live) return;
+    const float L = rows4_sum(st.lpart);
+    float inv[4];
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-        const float L = quad_sum(lpart[cb]);
-        float inv[4];
+    for (int r = 0; r < 4; ++r) inv[r] = fast_rcp(__shfl(L, 4 * g + r));
+    const int ibase = qw0 + 4 * g;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) inv[r] = 1.0f / __shfl(L, 4 * g + r);
-        const int ibase = q0 + (wave * kCB + cb) * 16 + 4 * g;
+    for (int ct = 0; ct < NT; ++ct) {
+        const int c = ct * 16 + n16;
+        if (c >= d) continue;
+        const float sv = a.vscale[(int64_t)bh * d + c];
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-            const int c = ct * 16 + n16;
-            if (c >= d) continue;
-            const float sv = a.vscale[(int64_t)bh * d + c];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = ibase + r;
-                if (i >= N) continue;
-                const int tot = acci[cb][ct][r] + 128 * cs[ct][r];
-                const float o = (accf[cb][ct][r] + (float)tot) * sv * inv[r];
-                const int64_t off = ((int64_t)bh * N + i) * d + c;
-                if (a.out_f32)
-                    ((float*)a.out)[off] = o;
-                else
-                    ((_Float16*)a.out)[off] = (_Float16)o;
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int i = ibase + r;
+            if (i >= N) continue;
+            const float acc = DEFER ? st.accf[ct][r] + (float)st.acci[ct][r] : st.accf[ct][r];
+            const float o = acc * sv * inv[r];
+            const int64_t off = ((int64_t)bh * N + i) * d + c;
+            if (a.out_f32)
+                ((float*)a.out)[off] = o;
+            else
+                ((_Float16*)a.out)[off] = (_Float16)o;
         }
     }
 }
 
-// Integer score export through the same K staging and QK tile as the forward kernel.
-template <int KC>
-__global__ __launch_bounds__(256, 2) void binattn_scores_kernel(FwdArgs a) {
-    __shared__ __attribute__((aligned(16))) KTile<KC> sK;
-    const int N = a.N, d = a.d, W = a.W;
+// Integer score export through the same K staging, Q operand and QK tile as the forward kernel.
+template <int NT>
+__global__ __launch_bounds__(256) void binattn_scores_kernel(FwdArgs a) {
+    constexpr int W = (NT + 1) / 2;
+    typedef TileRegs<NT, BK_NONE> Regs;
+    typedef TileLds<NT, BK_NONE> Lds;
+    __shared__ Lds lds;
+    const int N = a.N, d = a.d;
     const int nqb = (N + kBR - 1) / kBR;
     const int nblk = a.B * a.H * nqb;
     const int lb = xcd_logical_block(blockIdx.x, nblk);
     const int bh = lb / nqb, qb = lb % nqb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, n16 = lane & 15;
     const int q0 = qb * kBR;
-    v4i qop[kCB][KC];
-    int qi[kCB];
-#pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-        const int i = q0 + (wave * kCB + cb) * 16 + n16;
-        qi[cb] = i;
-        load_q<KC>(a.qbits + ((int64_t)bh * N + (i < N ? i : N - 1)) * W, i < N, d, g, qop[cb]);
-    }
+    v8i qop;
+    const int i = q0 + wave * 16 + n16;
+    const float seed = load_q<W>(a.qbits + ((int64_t)bh * N + (i < N ? i : N - 1)) * W, i < N, d, g, qop);
+    const v4f dseed = v4f{seed, seed, seed, seed};
     const uint32_t* kbh = a.kbits + (int64_t)bh * N * W;
     const int ntiles = (N + kBC - 1) / kBC;
+    zero_unused_groups<NT, BK_NONE>(lds);
     for (int tile = 0; tile < ntiles; ++tile) {
         const int j0 = tile * kBC;
-        stage_k<KC>(kbh, N, d, W, j0, sK);
+        Regs r;
+        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbh + j0 * W, (N - j0) * W * 4);
+#pragma unroll
+        for (int u = 0; u < Regs::KT; ++u) r.kw[u] = __builtin_amdgcn_raw_buffer_load_b32(kr, (tid + 256 * u) * 4, 0, 0);
+#pragma unroll
+        for (int u = 0; u < Regs::VCH; ++u) r.v[u] = make_uint4(0, 0, 0, 0);
+        r.mu = 0.0f;
+        store_tile<NT, BK_NONE>(r, lds, d);
         __syncthreads();
+        v4f D[4];
 #pragma unroll
-        for (int cb = 0; cb < kCB; ++cb) {
-            v4i D[4];
-            qk_tile<KC>(sK, qop[cb], lane, D);
-            if (qi[cb] < N) {
-                int32_t* row = a.scores + ((int64_t)bh * N + qi[cb]) * N;
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t* src = &lds.k[((t * 4 + g) * 16 + n16) * 8];
+            const v4i lo = *reinterpret_cast<const v4i*>(src);
+            const v4i hi = *reinterpret_cast<const v4i*>(src + 4);
+            const v8i kop = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            D[t] = mfma_f8(kop, qop, dseed);
+        }
+        if (i < N) {
+            int32_t* row = a.scores + ((int64_t)bh * N + i) * N;
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < 4; ++t)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = j0 + 16 * g + 4 * t + r;
-                        if (j < N) row[j] = D[t][r];
-                    }
-            }
+                for (int r2 = 0; r2 < 4; ++r2) {
+                    const int j = j0 + 16 * g + 4 * t + r2;
+                    if (j < N) row[j] = (int32_t)D[t][r2];
+                }
         }
         __syncthreads();
     }
 }
 
+template <int NT, int BK>
+static void launch_fwd_bk(const FwdArgs& a, bool defer, dim3 grid, hipStream_t s) {
+    if (defer)
+        hipLaunchKernelGGL((binattn_fwd_kernel<NT, BK, true>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((binattn_fwd_kernel<NT, BK, false>), grid, dim3(256), 0, s, a);
+}
+
 template <int NT>
 static hipError_t launch_fwd_nt(const FwdArgs& a, int bk, hipStream_t s) {
     const int nqb = (a.N + kBR - 1) / kBR;
-    const dim3 grid((unsigned)(a.B * a.H * nqb)), block(256);
+    const dim3 grid((unsigned)(a.B * a.H * nqb));
+    const bool defer = (a.N + kBC - 1) / kBC >= kDeferTiles;
     switch (bk) {
-        case BK_NONE: hipLaunchKernelGGL((binattn_fwd_kernel<NT, BK_NONE>), grid, block, 0, s, a); break;
-        case BK_DENSE_F16: hipLaunchKernelGGL((binattn_fwd_kernel<NT, BK_DENSE_F16>), grid, block, 0, s, a); break;
-        case BK_DENSE_F32: hipLaunchKernelGGL((binattn_fwd_kernel<NT, BK_DENSE_F32>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((binattn_fwd_kernel<NT, BK_RELPOS>), grid, block, 0, s, a); break;
+        case BK_NONE: launch_fwd_bk<NT, BK_NONE>(a, defer, grid, s); break;
+        case BK_DENSE_F16: launch_fwd_bk<NT, BK_DENSE_F16>(a, defer, grid, s); break;
+        case BK_DENSE_F32: launch_fwd_bk<NT, BK_DENSE_F32>(a, defer, grid, s); break;
+        default: launch_fwd_bk<NT, BK_RELPOS>(a, defer, grid, s); break;
     }
     return hipGetLastError();
 }
@@ -431,11 +572,20 @@ hipError_t launch_forward(const FwdArgs& a, int bias_kind, hipStream_t s) {
 hipError_t launch_scores(const FwdArgs& a, hipStream_t s) {
     const int nqb = (a.N + kBR - 1) / kBR;
     const dim3 grid((unsigned)(a.B * a.H * nqb)), block(256);
-    if (a.d <= 64)
-        hipLaunchKernelGGL(binattn_scores_kernel<1>, grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL(binattn_scores_kernel<2>, grid, block, 0, s, a);
+    switch ((a.d + 31) / 32) {
+        case 1: hipLaunchKernelGGL(binattn_scores_kernel<2>, grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL(binattn_scores_kernel<4>, grid, block, 0, s, a); break;
+        case 3: hipLaunchKernelGGL(binattn_scores_kernel<6>, grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL(binattn_scores_kernel<8>, grid, block, 0, s, a); break;
+    }
     return hipGetLastError();
+}
+
+// Whether the relative-position window any tile of a forward launch stages fits on chip
+// (an upper bound on the table rows one query block and one key tile touch).
+bool relpos_window_fits(int gw) {
+    const int rows = (kBR - 1) / gw + 1 + (kBC - 1) / gw + 1 + 1;
+    return rows * (2 * gw - 1) <= kRelposWin;
 }
 
 }  // namespace binattn

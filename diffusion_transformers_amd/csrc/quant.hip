@@ -11,8 +11,8 @@
 // here, through LDS, once per call.
 //
 // Two schedules (the same arithmetic):
-//   fused  (N <= kFusedMaxN): one workgroup per head -- absmax pass, then the
-//          quantise/transpose pass re-reads the head from L2.
+//   fused  (a head fits): one workgroup per head; the head is read from HBM once
+//          into registers, reduced, quantised and transposed on chip.
 //   split  (long N): zero-fill, absmax over (head, chunk) with atomicMax on the
 //          fp32 bit pattern (valid since |v| >= 0), quantise over (head, 64-key
 //          block), then scale = a/127 in place.
@@ -21,7 +21,8 @@
 
 namespace binattn {
 
-constexpr int kFusedMaxN = 2048;
+constexpr int kFusedMaxTok = 24;       // tokens per thread held in registers by the fused schedule
+constexpr int kFusedMaxImg = 48 * 1024; // bytes of the channel-major LDS image of one head
 constexpr int kChunk = 1024;  // tokens per absmax workgroup in the split schedule
 constexpr int kTPad = 16;     // LDS row padding (bytes) of the transpose tile
 
@@ -98,24 +99,78 @@ __device__ void quant_block(const T* __restrict__ vh, int N, int d, int64_t ldv,
     __syncthreads();
 }
 
-template <typename T>
+// Fused schedule: every token of the head is loaded once into registers (thread
+// (part, grp) holds tokens grp, grp+G, ...; consecutive lanes read consecutive 16-byte
+// chunks), the channel absmax is reduced through LDS, the register copies are
+// quantised into a zeroed channel-major LDS image of the head, and the image is stored
+// with contiguous 16-byte writes.
+template <typename T, int MAXT>
 __global__ __launch_bounds__(256) void quant_v_fused_kernel(const T* __restrict__ v, int N, int d, int64_t ldv,
                                                             int8_t* __restrict__ vq, float* __restrict__ vscale) {
+    constexpr int VE = VecOf<T>::VE;
+    typedef typename VecOf<T>::type vecT;
+    extern __shared__ __attribute__((aligned(16))) uint8_t sImg[];  // [d][ldv] int8
     __shared__ float sRed[2048];
-    __shared__ float sAmax[128];
     __shared__ float sInv[128];
-    __shared__ __attribute__((aligned(16))) uint8_t sT[128 * (64 + kTPad)];
     const int64_t bh = blockIdx.x;
     const T* vh = v + bh * (int64_t)N * d;
-    head_absmax<T>(vh, 0, N, d, sRed, sAmax);
-    if ((int)threadIdx.x < d) {
-        const float a = sAmax[threadIdx.x];
-        vscale[bh * d + threadIdx.x] = a / 127.0f;
-        sInv[threadIdx.x] = a > 0.0f ? 127.0f / a : 0.0f;
+    const int P = d / VE, G = 256 / P, tid = threadIdx.x;
+    const int part = tid % P, grp = tid / P;
+    const bool active = grp < G;
+    vecT x[MAXT];
+#pragma unroll
+    for (int k = 0; k < MAXT; ++k) {
+        const int n = grp + G * k;
+        if (active && n < N) {
+            x[k] = *reinterpret_cast<const vecT*>(vh + (int64_t)n * d + part * VE);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) x[k][e] = (T)0;
+        }
+    }
+    // zero the image (tokens N .. ldv-1 stay zero) while the loads are in flight
+    const int nvec = (int)(d * ldv / 16);
+    for (int id = tid; id < nvec; id += 256) reinterpret_cast<uint4*>(sImg)[id] = make_uint4(0, 0, 0, 0);
+    float m[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) m[e] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < MAXT; ++k)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) m[e] = fmaxf(m[e], fabsf((float)x[k][e]));
+    if (active) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) sRed[grp * d + part * VE + e] = m[e];
+    }
+    __syncthreads();
+    if (tid < d) {
+        float a = 0.0f;
+        for (int g = 0; g < G; ++g) a = fmaxf(a, sRed[g * d + tid]);
+        vscale[bh * d + tid] = a / 127.0f;
+        sInv[tid] = a > 0.0f ? 127.0f / a : 0.0f;
+    }
+    __syncthreads();
+    if (active) {
+        float inv[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) inv[e] = sInv[part * VE + e];
+#pragma unroll
+        for (int k = 0; k < MAXT; ++k) {
+            const int n = grp + G * k;
+            if (n < N) {
+#pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    float r = __builtin_rintf((float)x[k][e] * inv[e]);
+                    r = fminf(fmaxf(r, -127.0f), 127.0f);
+                    sImg[(int64_t)(part * VE + e) * ldv + n] = (uint8_t)(int8_t)(int)r;
+                }
+            }
+        }
     }
     __syncthreads();
     int8_t* vqh = vq + bh * d * ldv;
-    for (int j0 = 0; j0 < (int)ldv; j0 += 64) quant_block<T>(vh, N, d, ldv, j0, sInv, sT, vqh);
+    for (int id = tid; id < nvec; id += 256)
+        reinterpret_cast<uint4*>(vqh)[id] = reinterpret_cast<const uint4*>(sImg)[id];
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
@@ -157,8 +212,17 @@ __global__ __launch_bounds__(256) void finalize_scale_kernel(float* p, int64_t n
 template <typename T>
 static hipError_t launch_quant_t(const T* v, int BH, int N, int d, int64_t ldv, int8_t* vq, float* vscale,
                                  hipStream_t s) {
-    if (N <= kFusedMaxN) {
-        hipLaunchKernelGGL(quant_v_fused_kernel<T>, dim3(BH), dim3(256), 0, s, v, N, d, ldv, vq, vscale);
+    constexpr int VE = VecOf<T>::VE;
+    const int G = 256 / (d / VE);
+    const int64_t img = (int64_t)d * ldv;
+    const int tpt = (N + G - 1) / G;  // tokens per thread
+    if (tpt <= kFusedMaxTok && img <= kFusedMaxImg) {
+        if (tpt <= 8)
+            hipLaunchKernelGGL((quant_v_fused_kernel<T, 8>), dim3(BH), dim3(256), (size_t)img, s, v, N, d, ldv, vq, vscale);
+        else if (tpt <= 16)
+            hipLaunchKernelGGL((quant_v_fused_kernel<T, 16>), dim3(BH), dim3(256), (size_t)img, s, v, N, d, ldv, vq, vscale);
+        else
+            hipLaunchKernelGGL((quant_v_fused_kernel<T, 24>), dim3(BH), dim3(256), (size_t)img, s, v, N, d, ldv, vq, vscale);
         return hipGetLastError();
     }
     const int64_t n = (int64_t)BH * d;

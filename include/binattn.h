@@ -120,7 +120,8 @@ int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t
  *                       bias_dtype; token n sits at (n / gw, n % gw) on a
  *                       gh x gw grid (gh*gw == N) and
  *                       b_ij = T[h, (r_i-r_j+gh-1)*(2gw-1) + (c_i-c_j+gw-1)].
- *                       Requires gw % 16 == 0 and gw <= 512.  bias_ld ignored.
+ *                       Requires gw % 16 == 0 and gw <= 160 (the rows of T one
+ *                       key tile touches are staged on chip).  bias_ld ignored.
  *   out             [B,H,N,d] of out_dtype
  *
  * Computes, per (b, h, query i):

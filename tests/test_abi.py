@@ -84,7 +84,8 @@ def test_forward_validation(lib):
     assert _fwd(lib, kind=1, bias=_a(4100), ld=256) == -3    # misaligned base
     assert _fwd(lib, kind=2, bias=_a(4096), gh=16, gw=15) == -1   # grid does not cover N
     assert _fwd(lib, kind=2, bias=_a(4096), N=240, gh=16, gw=15) == -2  # gw % 16 != 0
-    assert _fwd(lib, kind=2, bias=_a(4096), N=1024, gh=1, gw=1024) == -2  # gw > 512
+    assert _fwd(lib, kind=2, bias=_a(4096), N=1024, gh=1, gw=1024) == -2  # window of one tile too wide
+    assert _fwd(lib, kind=2, bias=_a(4096), N=1056, gh=6, gw=176) == -2
     assert _fwd(lib, kind=3, bias=_a(4096)) == -2
     assert _fwd(lib, odt=5) == -2
     assert _fwd(lib, d=72, out=_a(2056)) == -3

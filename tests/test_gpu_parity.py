@@ -147,7 +147,8 @@ SMALL = [
     (2, 2, 256, 72, "f16", "relpos", (16, 16)),
     (1, 2, 384, 64, "f16", "relpos", (12, 32)),
     (1, 1, 577, 128, "f16", "dense", ()),
-    (1, 2, 1024, 96, "f32", "relpos", (2, 512)),
+    (1, 2, 1024, 96, "f32", "relpos", (8, 128)),
+    (1, 1, 2400, 64, "f16", "relpos", (15, 160)),
     (1, 1, 2048, 64, "f16", "relpos", (16, 128)),
 ]
 
