@@ -99,15 +99,17 @@ def pack_qk(x: torch.Tensor, bits=None, mu=None):
     return bits, mu
 
 
-def quant_v(v: torch.Tensor, vq=None, vscale=None):
-    """v [B,H,N,d] -> (vq int8 [B,H,d,ldv] channel-major, vscale fp32 [B,H,d])."""
+def quant_v(v: torch.Tensor, vq=None, vamax=None):
+    """v [B,H,N,d] -> (vq int8 [B,H,d,ldv] channel-major, vamax fp32 [B,H,d] channel absmax).
+
+    The dequantisation scale of channel c is vamax[..., c] / 127 (fp32 division)."""
     B, H, N, d = v.shape
     if vq is None:
         vq = torch.empty((B, H, d, vq_ld(N)), dtype=torch.int8, device=v.device)
-    if vscale is None:
-        vscale = torch.empty((B, H, d), dtype=torch.float32, device=v.device)
-    _check("binattn_quant_v", _lib.binattn_quant_v(_p(v), _dt(v), B, H, N, d, _p(vq), _p(vscale), _stream()))
-    return vq, vscale
+    if vamax is None:
+        vamax = torch.empty((B, H, d), dtype=torch.float32, device=v.device)
+    _check("binattn_quant_v", _lib.binattn_quant_v(_p(v), _dt(v), B, H, N, d, _p(vq), _p(vamax), _stream()))
+    return vq, vamax
 
 
 def aligned_dense_bias(bias: torch.Tensor) -> torch.Tensor:
@@ -122,7 +124,7 @@ def aligned_dense_bias(bias: torch.Tensor) -> torch.Tensor:
     return out
 
 
-def forward(q_bits, q_mu, k_bits, k_mu, vq, vscale, d, bias=None, bias_kind=BIAS_NONE, grid=None,
+def forward(q_bits, q_mu, k_bits, k_mu, vq, vamax, d, bias=None, bias_kind=BIAS_NONE, grid=None,
             out_dtype=torch.float16, out=None):
     """BinaryAttention forward -> O [B,H,N,d].
 
@@ -139,7 +141,7 @@ def forward(q_bits, q_mu, k_bits, k_mu, vq, vscale, d, bias=None, bias_kind=BIAS
             ld = bias.shape[-1]
         elif bias_kind == BIAS_RELPOS:
             gh, gw = grid
-    rc = _lib.binattn_forward(_p(q_bits), _p(q_mu), _p(k_bits), _p(k_mu), _p(vq), _p(vscale), bias_kind, bdt,
+    rc = _lib.binattn_forward(_p(q_bits), _p(q_mu), _p(k_bits), _p(k_mu), _p(vq), _p(vamax), bias_kind, bdt,
                               _p(bias), ld, gh, gw, B, H, N, d, _p(out), _dt(out), _stream())
     _check("binattn_forward", rc)
     return out

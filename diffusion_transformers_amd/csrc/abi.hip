@@ -66,28 +66,28 @@ int binattn_pack_qk(const void* x, int dtype, int B, int H, int N, int d, uint32
     return launched(launch_pack_qk(x, dtype == BINATTN_F32, (int64_t)B * H * N, d, bits, mu, (hipStream_t)stream));
 }
 
-int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t* vq, float* vscale,
+int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t* vq, float* vamax,
                     void* stream) {
-    if (!v || !vq || !vscale) return BINATTN_EINVAL;
+    if (!v || !vq || !vamax) return BINATTN_EINVAL;
     int rc = check_dims(B, H, N, d);
     if (rc) return rc;
     if (!dtype_ok(dtype)) return BINATTN_EUNSUPPORTED;
-    if (!aligned16(v) || !aligned16(vq) || !aligned16(vscale)) return BINATTN_EALIGN;
+    if (!aligned16(v) || !aligned16(vq) || !aligned16(vamax)) return BINATTN_EALIGN;
     if ((rc = device_ready())) return rc;
-    return launched(launch_quant_v(v, dtype == BINATTN_F32, B * H, N, d, binattn_vq_ld(N), vq, vscale,
+    return launched(launch_quant_v(v, dtype == BINATTN_F32, B * H, N, d, binattn_vq_ld(N), vq, vamax,
                                    (hipStream_t)stream));
 }
 
 int binattn_forward(const uint32_t* q_bits, const float* q_mu, const uint32_t* k_bits, const float* k_mu,
-                    const int8_t* vq, const float* vscale, int bias_kind, int bias_dtype, const void* bias,
+                    const int8_t* vq, const float* vamax, int bias_kind, int bias_dtype, const void* bias,
                     int64_t bias_ld, int grid_h, int grid_w, int B, int H, int N, int d, void* out,
                     int out_dtype, void* stream) {
-    if (!q_bits || !q_mu || !k_bits || !k_mu || !vq || !vscale || !out) return BINATTN_EINVAL;
+    if (!q_bits || !q_mu || !k_bits || !k_mu || !vq || !vamax || !out) return BINATTN_EINVAL;
     int rc = check_dims(B, H, N, d);
     if (rc) return rc;
     if (!dtype_ok(out_dtype)) return BINATTN_EUNSUPPORTED;
     if (!aligned16(q_bits) || !aligned16(q_mu) || !aligned16(k_bits) || !aligned16(k_mu) || !aligned16(vq) ||
-        !aligned16(vscale) || !aligned16(out))
+        !aligned16(vamax) || !aligned16(out))
         return BINATTN_EALIGN;
     switch (bias_kind) {
         case BINATTN_BIAS_NONE:
@@ -113,7 +113,7 @@ int binattn_forward(const uint32_t* q_bits, const float* q_mu, const uint32_t* k
     }
     if ((rc = device_ready())) return rc;
     FwdArgs a = {};
-    a.qbits = q_bits; a.qmu = q_mu; a.kbits = k_bits; a.kmu = k_mu; a.vq = vq; a.vscale = vscale;
+    a.qbits = q_bits; a.qmu = q_mu; a.kbits = k_bits; a.kmu = k_mu; a.vq = vq; a.vamax = vamax;
     a.bias = bias; a.bias_ld = bias_ld; a.bias_f32 = bias_dtype == BINATTN_F32;
     a.gh = grid_h; a.gw = grid_w;
     a.B = B; a.H = H; a.N = N; a.d = d; a.W = binattn_words(d); a.ldv = binattn_vq_ld(N);

@@ -31,7 +31,7 @@
 //    Short rows fold each tile's int32 result into the fp32 accumulator (with the
 //    running-max rescale); long rows keep accumulating in int32 across tiles and
 //    fold only when some row max in the wave moves.
-//  * Epilogue: O = acc * vscale_c / sum(p).
+//  * Epilogue: O = acc * s_c / sum(p), s_c = a_c / 127 from the channel absmax a_c.
 #include "common.h"
 #include "internal.h"
 
@@ -42,6 +42,7 @@ constexpr int kBR = kWaves * 16;            // queries per workgroup (16 per wav
 constexpr int kBC = 64;                     // keys per tile
 constexpr int kRelposWin = 1024;            // fp32 entries of the per-tile relative-position window
 constexpr int kDeferTiles = 16;             // rows of at least this many tiles accumulate in int32
+constexpr int kResTiles = 4;                // rows of at most this many tiles are staged whole in the prologue
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2_255 = 7.99435343685886f;
 
@@ -71,8 +72,7 @@ struct TileRegs {
 template <int NT, int BIAS>
 struct alignas(16) TileLds {
     static constexpr int W = (NT + 1) / 2;
-    uint32_t k[4 * 4 * 16 * 8];            // [t][group][row] x 32 B: A operand of QK MFMA t, lane (row, group);
-                                           // groups >= W stay zero
+    uint32_t k[4 * W * 16 * 8];            // [t][group][row] x 32 B: A operand of QK MFMA t, lane (row, group)
     uint32_t v[NT * kWave * 4];            // [ct][lane] x 16 B: B operand of PV MFMA ct
     float mu[kBC];
     float tw[BIAS == BK_RELPOS ? kRelposWin : 4];
@@ -158,7 +158,7 @@ __device__ __forceinline__ void store_tile(const TileRegs<NT, BIAS>& r, TileLds<
             unpack_bits32_f8(word, o);
             int t;
             const int m = key_slot(j, t);
-            uint32_t* dst = &s.k[((t * 4 + w) * 16 + m) * 8];
+            uint32_t* dst = &s.k[((t * R::W + w) * 16 + m) * 8];
             *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
             *reinterpret_cast<uint4*>(dst + 4) = make_uint4(o[4], o[5], o[6], o[7]);
         }
@@ -175,19 +175,6 @@ __device__ __forceinline__ void store_tile(const TileRegs<NT, BIAS>& r, TileLds<
     if (BIAS == BK_RELPOS) {
 #pragma unroll
         for (int i = 0; i < r.TW; ++i) s.tw[tid + 256 * i] = r.tw[i];
-    }
-}
-
-// Zero the K-operand rows of channel groups >= W (they are never written by store_tile).
-template <int NT, int BIAS>
-__device__ __forceinline__ void zero_unused_groups(TileLds<NT, BIAS>& s) {
-    constexpr int W = (NT + 1) / 2;
-    if (W < 4) {
-        for (int id = threadIdx.x; id < 4 * (4 - W) * 16 * 2; id += 256) {
-            const int half = id & 1, m = (id >> 1) & 15, tg = id >> 5;
-            const int t = tg / (4 - W), gg = W + tg % (4 - W);
-            *reinterpret_cast<uint4*>(&s.k[((t * 4 + gg) * 16 + m) * 8 + 4 * half]) = make_uint4(0, 0, 0, 0);
-        }
     }
 }
 
@@ -252,9 +239,11 @@ struct WaveState {
     v4f accf[NT];
 };
 
+// zk: 16 rows x 32 zero bytes, the A operand of lanes whose channel group is past d.
 template <int NT, int BIAS, bool DEFER>
-__device__ __forceinline__ void tile_body(const FwdArgs& a, TileLds<NT, BIAS>& s, WaveState<NT>& st,
-                                          const BiasRegs<BIAS>& bcur, int tile, int ntiles, int q0) {
+__device__ __forceinline__ void tile_body(const FwdArgs& a, TileLds<NT, BIAS>& s, const uint32_t* zk,
+                                          WaveState<NT>& st, const BiasRegs<BIAS>& bcur, int tile, int ntiles,
+                                          int q0) {
     constexpr int W = (NT + 1) / 2;
     const int N = a.N;
     const int lane = threadIdx.x & 63, g = lane >> 4, m16 = lane & 15;
@@ -265,7 +254,7 @@ __device__ __forceinline__ void tile_body(const FwdArgs& a, TileLds<NT, BIAS>& s
     v4f D[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const uint32_t* src = &s.k[((t * 4 + g) * 16 + m16) * 8];
+        const uint32_t* src = g < W ? &s.k[((t * W + g) * 16 + m16) * 8] : zk + m16 * 8;
         const v4i lo = *reinterpret_cast<const v4i*>(src);
         const v4i hi = *reinterpret_cast<const v4i*>(src + 4);
         const v8i kop = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -357,12 +346,15 @@ __device__ __forceinline__ void tile_body(const FwdArgs& a, TileLds<NT, BIAS>& s
     }
 }
 
-template <int NT, int BIAS, bool DEFER>
+template <int NT, int BIAS, bool DEFER, bool RES>
 __global__ __launch_bounds__(256) void binattn_fwd_kernel(FwdArgs a) {
     constexpr int W = (NT + 1) / 2;
     typedef TileRegs<NT, BIAS> Regs;
     typedef TileLds<NT, BIAS> Lds;
-    __shared__ Lds lds[2];
+    // RES: one LDS stage per tile of the whole (short) row; otherwise a two-stage ring
+    __shared__ Lds lds[RES ? kResTiles : 2];
+    __shared__ __attribute__((aligned(16))) uint32_t zk[16 * 8];
+    if (threadIdx.x < 16 * 8) zk[threadIdx.x] = 0u;
 
     const int N = a.N, d = a.d;
     const int nqb = (N + kBR - 1) / kBR;
@@ -424,32 +416,65 @@ __global__ __launch_bounds__(256) void binattn_fwd_kernel(FwdArgs a) {
     const int bvoff = (n16 * (int)a.bias_ld + 16 * g) * esz;
 
     const int ntiles = (N + kBC - 1) / kBC;
-    Regs regs;
+    // the scales of this lane's output channels, needed only at the end
+    float vsc[NT];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+        const int c = ct * 16 + n16;
+        vsc[ct] = c < d ? a.vamax[(int64_t)bh * d + c] / 127.0f : 0.0f;  // dequantisation scale, as fp32 a/127
+    }
     BiasRegs<BIAS> b0, b1;
-    zero_unused_groups<NT, BIAS>(lds[0]);
-    zero_unused_groups<NT, BIAS>(lds[1]);
-    load_tile<NT, BIAS>(regs, a, hp, q0, 0);
-    load_bias<BIAS>(b0, buffer_rsrc(brow, brow_bytes), bvoff);
-
-    // One pipeline step: stage tile `tile` into LDS, issue the loads of tile+1, compute tile.
-    // Unrolled by two so the two bias register sets alternate without copies.
-    auto step = [&](int tile, BiasRegs<BIAS>& bcur, BiasRegs<BIAS>& bnext) {
-        Lds& s = lds[tile & 1];
-        store_tile<NT, BIAS>(regs, s, d);
+    if (RES) {
+        // whole row on chip: every tile's loads in flight at once, then one barrier
+        Regs regs[kResTiles];
+#pragma unroll
+        for (int t = 0; t < kResTiles; ++t)
+            if (t < ntiles) load_tile<NT, BIAS>(regs[t], a, hp, q0, t * kBC);
+        load_bias<BIAS>(b0, buffer_rsrc(brow, brow_bytes), bvoff);
+#pragma unroll
+        for (int t = 0; t < kResTiles; ++t)
+            if (t < ntiles) store_tile<NT, BIAS>(regs[t], lds[t], d);
         __syncthreads();
-        if (tile + 1 < ntiles) {
-            const int jn = (tile + 1) * kBC;
-            load_tile<NT, BIAS>(regs, a, hp, q0, jn);
-            load_bias<BIAS>(bnext, buffer_rsrc(brow + jn * esz, brow_bytes - jn * esz), bvoff);
+        if (st.live) {
+            // compute, with the next tile's bias in flight (two register sets, no copies)
+            auto body = [&](int tile, BiasRegs<BIAS>& bcur, BiasRegs<BIAS>& bnext) {
+                if (tile + 1 < ntiles) {
+                    const int jn = (tile + 1) * kBC;
+                    load_bias<BIAS>(bnext, buffer_rsrc(brow + jn * esz, brow_bytes - jn * esz), bvoff);
+                }
+                tile_body<NT, BIAS, DEFER>(a, lds[tile], zk, st, bcur, tile, ntiles, q0);
+            };
+#pragma unroll
+            for (int tile = 0; tile < kResTiles; tile += 2) {
+                if (tile < ntiles) body(tile, b0, b1);
+                if (tile + 1 < ntiles) body(tile + 1, b1, b0);
+            }
         }
-        if (st.live) tile_body<NT, BIAS, DEFER>(a, s, st, bcur, tile, ntiles, q0);
-    };
-    for (int tile = 0; tile < ntiles; tile += 2) {
-        step(tile, b0, b1);
-        if (tile + 1 < ntiles) step(tile + 1, b1, b0);
+    } else {
+        Regs regs;
+        load_tile<NT, BIAS>(regs, a, hp, q0, 0);
+        load_bias<BIAS>(b0, buffer_rsrc(brow, brow_bytes), bvoff);
+
+        // One pipeline step: stage tile `tile` into LDS, issue the loads of tile+1, compute tile.
+        // Unrolled by two so the two bias register sets alternate without copies.
+        auto step = [&](int tile, BiasRegs<BIAS>& bcur, BiasRegs<BIAS>& bnext) {
+            Lds& s = lds[tile & 1];
+            store_tile<NT, BIAS>(regs, s, d);
+            __syncthreads();
+            if (tile + 1 < ntiles) {
+                const int jn = (tile + 1) * kBC;
+                load_tile<NT, BIAS>(regs, a, hp, q0, jn);
+                load_bias<BIAS>(bnext, buffer_rsrc(brow + jn * esz, brow_bytes - jn * esz), bvoff);
+            }
+            if (st.live) tile_body<NT, BIAS, DEFER>(a, s, zk, st, bcur, tile, ntiles, q0);
+        };
+        for (int tile = 0; tile < ntiles; tile += 2) {
+            step(tile, b0, b1);
+            if (tile + 1 < ntiles) step(tile + 1, b1, b0);
+        }
     }
 
-    // ---- epilogue: O = acc * vscale / sum(p)
+    // ---- epilogue: O = acc * s_c / sum(p)
     if (!st.live) return;
     const float L = rows4_sum(st.lpart);
     float inv[4];
@@ -460,7 +485,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_kernel(FwdArgs a) {
     for (int ct = 0; ct < NT; ++ct) {
         const int c = ct * 16 + n16;
         if (c >= d) continue;
-        const float sv = a.vscale[(int64_t)bh * d + c];
+        const float sv = vsc[ct];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = ibase + r;
@@ -483,6 +508,8 @@ __global__ __launch_bounds__(256) void binattn_scores_kernel(FwdArgs a) {
     typedef TileRegs<NT, BK_NONE> Regs;
     typedef TileLds<NT, BK_NONE> Lds;
     __shared__ Lds lds;
+    __shared__ __attribute__((aligned(16))) uint32_t zk[16 * 8];
+    if (threadIdx.x < 16 * 8) zk[threadIdx.x] = 0u;
     const int N = a.N, d = a.d;
     const int nqb = (N + kBR - 1) / kBR;
     const int nblk = a.B * a.H * nqb;
@@ -496,7 +523,6 @@ __global__ __launch_bounds__(256) void binattn_scores_kernel(FwdArgs a) {
     const v4f dseed = v4f{seed, seed, seed, seed};
     const uint32_t* kbh = a.kbits + (int64_t)bh * N * W;
     const int ntiles = (N + kBC - 1) / kBC;
-    zero_unused_groups<NT, BK_NONE>(lds);
     for (int tile = 0; tile < ntiles; ++tile) {
         const int j0 = tile * kBC;
         Regs r;
@@ -511,7 +537,7 @@ __global__ __launch_bounds__(256) void binattn_scores_kernel(FwdArgs a) {
         v4f D[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const uint32_t* src = &lds.k[((t * 4 + g) * 16 + n16) * 8];
+            const uint32_t* src = g < W ? &lds.k[((t * W + g) * 16 + n16) * 8] : zk + n16 * 8;
             const v4i lo = *reinterpret_cast<const v4i*>(src);
             const v4i hi = *reinterpret_cast<const v4i*>(src + 4);
             const v8i kop = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -532,23 +558,25 @@ __global__ __launch_bounds__(256) void binattn_scores_kernel(FwdArgs a) {
 }
 
 template <int NT, int BK>
-static void launch_fwd_bk(const FwdArgs& a, bool defer, dim3 grid, hipStream_t s) {
-    if (defer)
-        hipLaunchKernelGGL((binattn_fwd_kernel<NT, BK, true>), grid, dim3(256), 0, s, a);
+static void launch_fwd_bk(const FwdArgs& a, dim3 grid, hipStream_t s) {
+    const int ntiles = (a.N + kBC - 1) / kBC;
+    if (ntiles <= kResTiles)
+        hipLaunchKernelGGL((binattn_fwd_kernel<NT, BK, false, true>), grid, dim3(256), 0, s, a);
+    else if (ntiles >= kDeferTiles)
+        hipLaunchKernelGGL((binattn_fwd_kernel<NT, BK, true, false>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((binattn_fwd_kernel<NT, BK, false>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((binattn_fwd_kernel<NT, BK, false, false>), grid, dim3(256), 0, s, a);
 }
 
 template <int NT>
 static hipError_t launch_fwd_nt(const FwdArgs& a, int bk, hipStream_t s) {
     const int nqb = (a.N + kBR - 1) / kBR;
     const dim3 grid((unsigned)(a.B * a.H * nqb));
-    const bool defer = (a.N + kBC - 1) / kBC >= kDeferTiles;
     switch (bk) {
-        case BK_NONE: launch_fwd_bk<NT, BK_NONE>(a, defer, grid, s); break;
-        case BK_DENSE_F16: launch_fwd_bk<NT, BK_DENSE_F16>(a, defer, grid, s); break;
-        case BK_DENSE_F32: launch_fwd_bk<NT, BK_DENSE_F32>(a, defer, grid, s); break;
-        default: launch_fwd_bk<NT, BK_RELPOS>(a, defer, grid, s); break;
+        case BK_NONE: launch_fwd_bk<NT, BK_NONE>(a, grid, s); break;
+        case BK_DENSE_F16: launch_fwd_bk<NT, BK_DENSE_F16>(a, grid, s); break;
+        case BK_DENSE_F32: launch_fwd_bk<NT, BK_DENSE_F32>(a, grid, s); break;
+        default: launch_fwd_bk<NT, BK_RELPOS>(a, grid, s); break;
     }
     return hipGetLastError();
 }

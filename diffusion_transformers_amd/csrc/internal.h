@@ -12,7 +12,7 @@ struct FwdArgs {
     const uint32_t* kbits;
     const float* kmu;
     const int8_t* vq;
-    const float* vscale;
+    const float* vamax;    // channel absmax of V; the dequantisation scale is vamax / 127
     const void* bias;
     int64_t bias_ld;      // dense: row stride in elements
     int bias_f32;         // bias / table stored as fp32 (else fp16)
@@ -27,7 +27,7 @@ struct FwdArgs {
 
 hipError_t launch_pack_qk(const void* x, int f32, int64_t ntok, int d, uint32_t* bits, float* mu,
                           hipStream_t s);
-hipError_t launch_quant_v(const void* v, int f32, int BH, int N, int d, int64_t ldv, int8_t* vq, float* vscale,
+hipError_t launch_quant_v(const void* v, int f32, int BH, int N, int d, int64_t ldv, int8_t* vq, float* vamax,
                           hipStream_t s);
 hipError_t launch_forward(const FwdArgs& a, int bias_kind, hipStream_t s);
 hipError_t launch_scores(const FwdArgs& a, hipStream_t s);

@@ -92,13 +92,13 @@ int binattn_pack_qk(const void* x, int dtype, int B, int H, int N, int d, uint32
  *   vq     [B,H,d,ldv] int8, ldv = binattn_vq_ld(N) (channel-major: the N
  *                      tokens of one channel are contiguous); entries for
  *                      tokens n >= N are written as 0
- *   vscale [B,H,d]     fp32
+ *   vamax  [B,H,d]     fp32 channel absmax a; the dequantisation scale of the
+ *                      channel is the fp32 quotient a / 127
  * Per (b, h, channel c), in fp32 with IEEE division and round-half-even:
- *   a = max_n |v[n,c]|;  vscale = a / 127;  inv = 127 / a;
- *   vq[c,n] = clamp(rint(v[n,c] * inv), -127, 127);  a == 0 -> vscale = 0, vq = 0.
- * vscale doubles as scratch while the call runs.
+ *   a = max_n |v[n,c]|;  inv = 127 / a;
+ *   vq[c,n] = clamp(rint(v[n,c] * inv), -127, 127);  a == 0 -> vq = 0.
  */
-int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t* vq, float* vscale,
+int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t* vq, float* vamax,
                     void* stream);
 
 /*
@@ -111,7 +111,7 @@ int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t
  *   q_bits, k_bits  [B,H,N,W] uint32   from binattn_pack_qk
  *   q_mu, k_mu      [B,H,N]   fp32     from binattn_pack_qk
  *   vq              [B,H,d,ldv] int8   from binattn_quant_v
- *   vscale          [B,H,d]   fp32     from binattn_quant_v
+ *   vamax           [B,H,d]   fp32     from binattn_quant_v (scale s_c = vamax_c / 127)
  *   bias_kind       BINATTN_BIAS_NONE:   bias must be NULL.
  *                   BINATTN_BIAS_DENSE:  bias [H,N,bias_ld] of bias_dtype, entry
  *                       (h,i,j) = b_ij for every batch item; bias_ld >= N and
@@ -129,13 +129,13 @@ int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t
  *   S_ij = q_mu_i * k_mu_j * D_ij / sqrt(d) + b_ij             (fp32)
  *   streamed over key tiles with a running row max m and row sum l:
  *   P^_ij = rint(255 * exp(S_ij - m)) in [0,255], l = sum exp(S_ij - m) (fp32),
- *   O_ic = vscale_c * sum_j P^_ij vq_cj / (255 * l_i)
+ *   O_ic = s_c * sum_j P^_ij vq_cj / (255 * l_i)
  * (integer PV; the max used for a key tile is the running max after that tile,
  * so P^ may differ by the rounding of an earlier tile from a two-pass exact-max
  * result).
  */
 int binattn_forward(const uint32_t* q_bits, const float* q_mu, const uint32_t* k_bits, const float* k_mu,
-                    const int8_t* vq, const float* vscale, int bias_kind, int bias_dtype, const void* bias,
+                    const int8_t* vq, const float* vamax, int bias_kind, int bias_dtype, const void* bias,
                     int64_t bias_ld, int grid_h, int grid_w, int B, int H, int N, int d, void* out,
                     int out_dtype, void* stream);
 

@@ -58,7 +58,7 @@ def _load():
     lib.oracle_threads.restype = i32
     lib.oracle_set_threads.argtypes = [i32]
     lib.oracle_pack_qk.argtypes = [vp, i64, i32, vp, vp]
-    lib.oracle_quant_v.argtypes = [vp, i64, i64, i32, vp, vp]
+    lib.oracle_quant_v.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     lib.oracle_scores_i32.argtypes = [vp, vp, i64, i64, i32, vp]
     lib.oracle_scores_rows.argtypes = [vp, vp, i64, i64, i32, vp, i64, vp]
     lib.oracle_forward.argtypes = [vp, vp, vp, i32, vp, i32, i32, i64, i64, i64, i32, i32, vp, vp, vp, vp]
@@ -101,14 +101,17 @@ def pack_qk(x):
     return bits, mu
 
 
-def quant_v(v):
-    """Channel-wise int8 V of v [B,H,N,d] -> (vq int8 [B,H,N,d], scale fp32 [B,H,d])."""
+def quant_v(v, with_amax: bool = False):
+    """Channel-wise int8 V of v [B,H,N,d] -> (vq int8 [B,H,N,d], scale fp32 [B,H,d]).
+
+    with_amax=True also returns the fp32 channel absmax a [B,H,d] (scale = a / 127)."""
     v = _f64(v)
     B, H, N, d = v.shape
     vq = np.zeros((B, H, N, d), dtype=np.int8)
     s = np.zeros((B, H, d), dtype=np.float32)
-    _load().oracle_quant_v(_ptr(v), B * H, N, d, _ptr(vq), _ptr(s))
-    return vq, s
+    a = np.zeros((B, H, d), dtype=np.float32)
+    _load().oracle_quant_v(_ptr(v), B * H, N, d, _ptr(vq), _ptr(s), _ptr(a))
+    return (vq, s, a) if with_amax else (vq, s)
 
 
 def scores_i32(qbits, kbits, d: int):

@@ -85,7 +85,7 @@ void oracle_pack_qk(const double* x, int64_t ntok, int d, uint32_t* bits, float*
 
 /* Key design 3, V half: symmetric channel-wise int8 with one fp32 scale per
  * (batch, head, channel).  vq is [nheads, N, d] row-major. */
-void oracle_quant_v(const double* v, int64_t nheads, int64_t N, int d, int8_t* vq, float* scale) {
+void oracle_quant_v(const double* v, int64_t nheads, int64_t N, int d, int8_t* vq, float* scale, float* amax) {
 #pragma omp parallel for schedule(static)
     for (int64_t bh = 0; bh < nheads; ++bh) {
         const double* vh = v + bh * N * d;
@@ -96,6 +96,7 @@ void oracle_quant_v(const double* v, int64_t nheads, int64_t N, int d, int8_t* v
                 float x = fabsf((float)vh[j * d + c]);
                 if (x > a) a = x;
             }
+            if (amax) amax[bh * d + c] = a;
             if (a == 0.0f) {
                 scale[bh * d + c] = 0.0f;
                 for (int64_t j = 0; j < N; ++j) qh[j * d + c] = 0;
@@ -238,7 +239,7 @@ static int ctx_init(fwd_ctx* c, const double* q, const double* k, const double* 
     if (!c->qb || !c->kb || !c->qmu || !c->kmu || !c->vq || !c->vs) return -2;
     oracle_pack_qk(q, ntok, d, c->qb, c->qmu);
     oracle_pack_qk(k, ntok, d, c->kb, c->kmu);
-    oracle_quant_v(v, B * H, N, d, c->vq, c->vs);
+    oracle_quant_v(v, B * H, N, d, c->vq, c->vs, NULL);
     return 0;
 }
 

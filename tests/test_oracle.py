@@ -133,10 +133,12 @@ def test_quant_v_invariants():
     v = rng.standard_normal((2, 3, 50, 72)).astype(np.float16).astype(np.float64)
     v[0, 1, :, 7] = 0.0  # an all-zero channel
     v[1, 2, :, 3] *= 8.0  # an outlier channel
-    vq, s = oracle.quant_v(v)
-    assert vq.dtype == np.int8 and s.dtype == np.float32
+    vq, s, a = oracle.quant_v(v, with_amax=True)
+    assert vq.dtype == np.int8 and s.dtype == np.float32 and a.dtype == np.float32
     assert np.all(np.abs(vq.astype(int)) <= 127)
     amax = np.max(np.abs(v), axis=2)
+    # the absmax output is the channel max of |v| (exact in fp32 for fp16 inputs)
+    np.testing.assert_array_equal(a, amax.astype(np.float32))
     nz = amax > 0
     assert np.all(np.max(np.abs(vq.astype(int)), axis=2)[nz] == 127)
     assert np.all(s[~nz] == 0) and np.all(vq[0, 1, :, 7] == 0)
