@@ -105,6 +105,36 @@ def cpu_baseline(inp, w, seconds: float):
                       f"{nb} of {w.B} batch items of {w.name}, {el:.1f} s wall"}
 
 
+def qk_ab(w, W, b, dev, steps):
+    """Time the QK-tile probe with each method on the workload's packed Q/K (same launch grid,
+    same LDS staging of K, same per-row reduction; only the way D is computed differs)."""
+    import torch
+    inp = W.make(w, seed=W.WORKLOADS.index(w))
+    qb, _ = b.pack_qk(torch.from_numpy(inp["q"]).to(dev))
+    kb, _ = b.pack_qk(torch.from_numpy(inp["k"]).to(dev))
+    res = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "steps": steps}
+    outs = {}
+    for name, method in (("mfma", b.QK_MFMA), ("popcount", b.QK_POPCOUNT)):
+        m, s = b.qk_rowstats(qb, kb, w.d, method)
+        for _ in range(3):
+            b.qk_rowstats(qb, kb, w.d, method, m, s)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            b.qk_rowstats(qb, kb, w.d, method, m, s)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / steps
+        outs[name] = (m.clone(), s.clone())
+        res[name + "_us"] = us
+        res[name + "_tops_qk"] = 2.0 * w.B * w.H * w.N * w.N * w.d / (us * 1e-6) / 1e12
+    res["identical"] = bool(torch.equal(outs["mfma"][0], outs["popcount"][0]) and
+                            torch.equal(outs["mfma"][1], outs["popcount"][1]))
+    res["popcount_over_mfma"] = res["popcount_us"] / res["mfma_us"]
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +144,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=8, help="input sets cycled through the timed steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--qk-ab", action="store_true",
+                    help="only time the binary QK tile by its two methods (fp8 MFMA, VALU XOR+popcount) and exit")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (PMC scaling reference) and exit")
     args = ap.parse_args()
@@ -145,6 +177,9 @@ def main():
         return
 
     w = W.BY_NAME[args.workload]
+    if args.qk_ab:
+        qk_ab(w, W, b, dev, max(1, args.steps))
+        return
     sets = []
     for r in range(max(1, args.rotate)):
         inp = W.make(w, seed=W.WORKLOADS.index(w) + 1000 * r)

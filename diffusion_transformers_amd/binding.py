@@ -47,12 +47,15 @@ def _load():
     lib.binattn_forward.restype = i32
     lib.binattn_scores_i32.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
     lib.binattn_scores_i32.restype = i32
+    lib.binattn_qk_rowstats.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.binattn_qk_rowstats.restype = i32
     return lib
 
 
 _lib = _load()
 EXPORTS = ["binattn_abi_version", "binattn_strerror", "binattn_words", "binattn_vq_ld", "binattn_pack_qk",
-           "binattn_quant_v", "binattn_forward", "binattn_scores_i32"]
+           "binattn_quant_v", "binattn_forward", "binattn_scores_i32", "binattn_qk_rowstats"]
+QK_MFMA, QK_POPCOUNT = 0, 1
 
 
 def lib():
@@ -154,3 +157,15 @@ def scores_i32(q_bits, k_bits, d, D=None):
         D = torch.empty((B, H, N, N), dtype=torch.int32, device=q_bits.device)
     _check("binattn_scores_i32", _lib.binattn_scores_i32(_p(q_bits), _p(k_bits), B, H, N, d, _p(D), _stream()))
     return D
+
+
+def qk_rowstats(q_bits, k_bits, d, method=QK_MFMA, rowmax=None, rowsum=None):
+    """Binary QK tile probe: (max_j D_ij, sum_j D_ij) per query row, fp32 [B,H,N] each."""
+    B, H, N, _ = q_bits.shape
+    if rowmax is None:
+        rowmax = torch.empty((B, H, N), dtype=torch.float32, device=q_bits.device)
+    if rowsum is None:
+        rowsum = torch.empty((B, H, N), dtype=torch.float32, device=q_bits.device)
+    _check("binattn_qk_rowstats", _lib.binattn_qk_rowstats(_p(q_bits), _p(k_bits), B, H, N, d, method, _p(rowmax),
+                                                           _p(rowsum), _stream()))
+    return rowmax, rowsum

@@ -136,4 +136,18 @@ int binattn_scores_i32(const uint32_t* q_bits, const uint32_t* k_bits, int B, in
     return launched(launch_scores(a, (hipStream_t)stream));
 }
 
+int binattn_qk_rowstats(const uint32_t* q_bits, const uint32_t* k_bits, int B, int H, int N, int d, int method,
+                       float* rowmax, float* rowsum, void* stream) {
+    if (!q_bits || !k_bits || !rowmax || !rowsum) return BINATTN_EINVAL;
+    int rc = check_dims(B, H, N, d);
+    if (rc) return rc;
+    if (method != BINATTN_QK_MFMA && method != BINATTN_QK_POPCOUNT) return BINATTN_EUNSUPPORTED;
+    if (!aligned16(q_bits) || !aligned16(k_bits) || !aligned16(rowmax) || !aligned16(rowsum)) return BINATTN_EALIGN;
+    if ((rc = device_ready())) return rc;
+    FwdArgs a = {};
+    a.qbits = q_bits; a.kbits = k_bits;
+    a.B = B; a.H = H; a.N = N; a.d = d; a.W = binattn_words(d);
+    return launched(launch_qk_stats(a, method, rowmax, rowsum, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -760,6 +760,99 @@ __global__ __launch_bounds__(256) void binattn_scores_kernel(FwdArgs a) {
     }
 }
 
+// QK-tile probe: D_ij for every (query, key) by one of two methods, reduced per query row to
+// max_j D_ij and sum_j D_ij (fp32, exact for these integer ranges), so that the cost of the
+// tile itself is measured rather than the N^2 score writes.
+//   METHOD 0: the forward's tile, fp8 MFMA on LDS-staged fp8 K operands;
+//   METHOD 1: VALU XOR + v_bcnt on LDS-staged sign words, D = d - 2 popcount(q XOR k).
+// Both hand D to the softmax stage as fp32 in the same lane layout (query n, keys 16g..16g+15).
+template <int NT, int METHOD>
+__global__ __launch_bounds__(256) void binattn_qk_stats_kernel(FwdArgs a, float* rowmax, float* rowsum) {
+    constexpr int W = (NT + 1) / 2;
+    typedef TileRegs<NT, 4> Regs;
+    typedef TileLds<NT, 4> Lds;
+    __shared__ Lds lds;
+    __shared__ __attribute__((aligned(16))) uint32_t kraw[kBC * W];
+    __shared__ __attribute__((aligned(16))) uint32_t zk[16 * 8];
+    if (threadIdx.x < 16 * 8) zk[threadIdx.x] = 0u;
+    const int N = a.N, d = a.d;
+    const int nqb = (N + kBR - 1) / kBR;
+    const int lb = xcd_logical_block(blockIdx.x, a.B * a.H * nqb);
+    const int bh = lb / nqb, qb = lb % nqb;
+    const int tid = threadIdx.x, wave = tid >> 6, g = (tid & 63) >> 4, n16 = tid & 15;
+    const int i = qb * kBR + wave * 16 + n16;
+    const bool live = i < N;
+    const uint32_t* qrow = a.qbits + ((int64_t)bh * N + (live ? i : N - 1)) * W;
+    v8i qop;
+    v4f dseed = v4f{0.f, 0.f, 0.f, 0.f};
+    uint32_t qw[W];
+    if (METHOD == 0) {
+        const float seed = load_q<W>(qrow, live, d, g, qop);
+        dseed = v4f{seed, seed, seed, seed};
+    } else {
+#pragma unroll
+        for (int w = 0; w < W; ++w) qw[w] = live ? qrow[w] : 0u;
+    }
+    const uint32_t* kbh = a.kbits + (int64_t)bh * N * W;
+    const int ntiles = (N + kBC - 1) / kBC;
+    float mloc = -INFINITY, ssum = 0.0f;
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int j0 = tile * kBC, jg = j0 + 16 * g;
+        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbh + j0 * W, (N - j0) * W * 4);
+        if (METHOD == 0) {
+            Regs r;
+#pragma unroll
+            for (int u = 0; u < Regs::KT; ++u) r.kw[u] = __builtin_amdgcn_raw_buffer_load_b32(kr, (tid + 256 * u) * 4, 0, 0);
+#pragma unroll
+            for (int u = 0; u < Regs::VCH; ++u) r.v[u] = make_uint4(0, 0, 0, 0);
+            r.mu = 0.0f;
+            store_tile<NT, 4>(r, lds, d);
+        } else {
+            if (tid < kBC * W) kraw[tid] = __builtin_amdgcn_raw_buffer_load_b32(kr, tid * 4, 0, 0);
+        }
+        __syncthreads();
+        float D[16];
+        if (METHOD == 0) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t* src = g < W ? &lds.k[((t * W + g) * 16 + n16) * 8] : zk + n16 * 8;
+                const v4i lo = *reinterpret_cast<const v4i*>(src);
+                const v4i hi = *reinterpret_cast<const v4i*>(src + 4);
+                const v4f x = mfma_f8(v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, qop, dseed);
+#pragma unroll
+                for (int r2 = 0; r2 < 4; ++r2) D[4 * t + r2] = x[r2];
+            }
+        } else {
+            uint32_t kw[16 * W];
+#pragma unroll
+            for (int u = 0; u < 4 * W; ++u) {
+                const uint4 x = *reinterpret_cast<const uint4*>(&kraw[16 * g * W + 4 * u]);
+                kw[4 * u] = x.x; kw[4 * u + 1] = x.y; kw[4 * u + 2] = x.z; kw[4 * u + 3] = x.w;
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                uint32_t c = 0;
+#pragma unroll
+                for (int w = 0; w < W; ++w) c += __builtin_popcount(qw[w] ^ kw[k * W + w]);  // v_xor + v_bcnt (accumulating)
+                D[k] = (float)(d - 2 * (int)c);
+            }
+        }
+        const int nvalid = N - jg;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const bool ok = k < nvalid;
+            mloc = fmaxf(mloc, ok ? D[k] : -INFINITY);
+            ssum += ok ? D[k] : 0.0f;
+        }
+        __syncthreads();
+    }
+    const float m = rows4_max(mloc), sm = rows4_sum(ssum);
+    if (live && g == 0) {
+        rowmax[(int64_t)bh * N + i] = m;
+        rowsum[(int64_t)bh * N + i] = sm;
+    }
+}
+
 // Whether the relative-position window of a whole short row (queries of one block, every key)
 // fits the staged window; false sends the launch to the streaming kernel.
 static bool keep_window_fits(const FwdArgs& a) {
@@ -844,6 +937,26 @@ hipError_t launch_scores(const FwdArgs& a, hipStream_t s) {
         case 2: hipLaunchKernelGGL(binattn_scores_kernel<4>, grid, block, 0, s, a); break;
         case 3: hipLaunchKernelGGL(binattn_scores_kernel<6>, grid, block, 0, s, a); break;
         default: hipLaunchKernelGGL(binattn_scores_kernel<8>, grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+template <int NTV>
+static void launch_qk_stats_nt(const FwdArgs& a, int method, float* rowmax, float* rowsum, dim3 grid, hipStream_t s) {
+    if (method)
+        hipLaunchKernelGGL((binattn_qk_stats_kernel<NTV, 1>), grid, dim3(256), 0, s, a, rowmax, rowsum);
+    else
+        hipLaunchKernelGGL((binattn_qk_stats_kernel<NTV, 0>), grid, dim3(256), 0, s, a, rowmax, rowsum);
+}
+
+hipError_t launch_qk_stats(const FwdArgs& a, int method, float* rowmax, float* rowsum, hipStream_t s) {
+    const int nqb = (a.N + kBR - 1) / kBR;
+    const dim3 grid((unsigned)(a.B * a.H * nqb));
+    switch ((a.d + 31) / 32) {
+        case 1: launch_qk_stats_nt<2>(a, method, rowmax, rowsum, grid, s); break;
+        case 2: launch_qk_stats_nt<4>(a, method, rowmax, rowsum, grid, s); break;
+        case 3: launch_qk_stats_nt<6>(a, method, rowmax, rowsum, grid, s); break;
+        default: launch_qk_stats_nt<8>(a, method, rowmax, rowsum, grid, s); break;
     }
     return hipGetLastError();
 }

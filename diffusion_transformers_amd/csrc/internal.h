@@ -31,6 +31,7 @@ hipError_t launch_quant_v(const void* v, int f32, int BH, int N, int d, int64_t 
                           hipStream_t s);
 hipError_t launch_forward(const FwdArgs& a, int bias_kind, hipStream_t s);
 hipError_t launch_scores(const FwdArgs& a, hipStream_t s);
+hipError_t launch_qk_stats(const FwdArgs& a, int method, float* rowmax, float* rowsum, hipStream_t s);
 bool relpos_window_fits(int gw);
 
 }  // namespace binattn

@@ -149,6 +149,24 @@ int binattn_forward(const uint32_t* q_bits, const float* q_mu, const uint32_t* k
 int binattn_scores_i32(const uint32_t* q_bits, const uint32_t* k_bits, int B, int H, int N, int d, int32_t* D,
                        void* stream);
 
+/*
+ * binattn_qk_rowstats -- probe of the binary QK tile alone (measurement and test export).
+ * Passage: key design 1 computes s_i.t_j with XOR and popcount; the hardware-implementation
+ * bullet runs it on binary tensor-core MMAs.  This entry computes every D_ij of a forward
+ * launch's tiling with the chosen method and reduces each query row, so the two ways of
+ * computing the tile on gfx950 can be timed against each other on identical work:
+ *   method BINATTN_QK_MFMA     (0): fp8 MFMA on unpacked LDS operands (what binattn_forward uses);
+ *   method BINATTN_QK_POPCOUNT (1): VALU XOR + v_bcnt on LDS-staged sign words.
+ *
+ *   q_bits, k_bits [B,H,N,W] uint32
+ *   rowmax [B,H,N] fp32 = max_j D_ij;  rowsum [B,H,N] fp32 = sum_j D_ij (both exact)
+ * Errors as binattn_scores_i32; an unknown method is BINATTN_EUNSUPPORTED.
+ */
+#define BINATTN_QK_MFMA 0
+#define BINATTN_QK_POPCOUNT 1
+int binattn_qk_rowstats(const uint32_t* q_bits, const uint32_t* k_bits, int B, int H, int N, int d, int method,
+                        float* rowmax, float* rowsum, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -90,6 +90,9 @@ def test_forward_validation(lib):
     assert _fwd(lib, odt=5) == -2
     assert _fwd(lib, d=72, out=_a(2056)) == -3
     assert lib.binattn_scores_i32(_a(256), None, 1, 1, 4, 64, _a(512), None) == -1
+    assert lib.binattn_qk_rowstats(_a(256), _a(512), 1, 1, 4, 64, 0, None, _a(768), None) == -1
+    assert lib.binattn_qk_rowstats(_a(256), _a(512), 1, 1, 4, 64, 2, _a(1024), _a(768), None) == -2
+    assert lib.binattn_qk_rowstats(_a(256), _a(516), 1, 1, 4, 64, 1, _a(1024), _a(768), None) == -3
 
 
 def test_valid_arguments_without_a_device_report_enodevice(lib):

@@ -135,6 +135,25 @@ def test_scores_bit_exact(d, N):
     np.testing.assert_array_equal(D.cpu().numpy(), oracle.scores_i32(oq, ok, d))
 
 
+@pytest.mark.parametrize("method", ["mfma", "popcount"])
+@pytest.mark.parametrize("d,N", [(64, 1), (64, 17), (8, 64), (72, 65), (128, 197), (64, 577), (72, 256)])
+def test_qk_tile_probe_both_methods(method, d, N):
+    """The QK-tile probe reduces every D_ij of the forward's tiling; both ways of computing the
+    tile (fp8 MFMA, VALU XOR + popcount) give the oracle's row max and row sum exactly."""
+    _say(f"qk probe {method} d={d} N={N}")
+    inp = W.custom(2, 3, N, d, "f16", "none", seed=5 * N + d)
+    b = _b()
+    qb, _ = b.pack_qk(_t(inp["q"]))
+    kb, _ = b.pack_qk(_t(inp["k"]))
+    m, s = b.qk_rowstats(qb, kb, d, b.QK_MFMA if method == "mfma" else b.QK_POPCOUNT)
+    torch.cuda.synchronize()
+    oq, _ = oracle.pack_qk(inp["q"].astype(np.float64))
+    ok, _ = oracle.pack_qk(inp["k"].astype(np.float64))
+    D = oracle.scores_i32(oq, ok, d).astype(np.int64)
+    np.testing.assert_array_equal(m.cpu().numpy(), D.max(axis=-1).astype(np.float32))
+    np.testing.assert_array_equal(s.cpu().numpy(), D.sum(axis=-1).astype(np.float32))
+
+
 # ---------------------------------------------------------------- forward, small and ragged
 
 SMALL = [
