@@ -49,12 +49,20 @@ def _load():
     lib.binattn_scores_i32.restype = i32
     lib.binattn_qk_rowstats.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.binattn_qk_rowstats.restype = i32
+    lib.binattn_prepare.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.binattn_prepare.restype = i32
+    lib.binattn_attention_workspace.argtypes = [i32, i32, i32, i32]
+    lib.binattn_attention_workspace.restype = i64
+    lib.binattn_attention.argtypes = [vp, vp, vp, i32, i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, vp, i32, vp,
+                                      i64, vp]
+    lib.binattn_attention.restype = i32
     return lib
 
 
 _lib = _load()
 EXPORTS = ["binattn_abi_version", "binattn_strerror", "binattn_words", "binattn_vq_ld", "binattn_pack_qk",
-           "binattn_quant_v", "binattn_forward", "binattn_scores_i32", "binattn_qk_rowstats"]
+           "binattn_quant_v", "binattn_forward", "binattn_scores_i32", "binattn_qk_rowstats",
+           "binattn_prepare", "binattn_attention_workspace", "binattn_attention"]
 QK_MFMA, QK_POPCOUNT = 0, 1
 
 
@@ -169,3 +177,47 @@ def qk_rowstats(q_bits, k_bits, d, method=QK_MFMA, rowmax=None, rowsum=None):
     _check("binattn_qk_rowstats", _lib.binattn_qk_rowstats(_p(q_bits), _p(k_bits), B, H, N, d, method, _p(rowmax),
                                                            _p(rowsum), _stream()))
     return rowmax, rowsum
+
+
+def prepare(q, k, v, qbits=None, qmu=None, kbits=None, kmu=None, vq=None, vamax=None):
+    """The three input-side steps in one call: (q_bits, q_mu, k_bits, k_mu, vq, vamax)."""
+    B, H, N, d = q.shape
+    dev = q.device
+    if qbits is None:
+        qbits = torch.empty((B, H, N, words(d)), dtype=torch.int32, device=dev)
+        kbits = torch.empty_like(qbits)
+        qmu = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        kmu = torch.empty_like(qmu)
+        vq = torch.empty((B, H, d, vq_ld(N)), dtype=torch.int8, device=dev)
+        vamax = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    _check("binattn_prepare", _lib.binattn_prepare(_p(q), _p(k), _p(v), _dt(q), B, H, N, d, _p(qbits), _p(qmu), _p(kbits), _p(kmu),
+                                                   _p(vq), _p(vamax), _stream()))
+    return qbits, qmu, kbits, kmu, vq, vamax
+
+
+def attention_workspace(B, H, N, d, device):
+    """Caller-owned workspace for attention() (uint8 tensor; torch allocations are 256-byte aligned)."""
+    n = _lib.binattn_attention_workspace(B, H, N, d)
+    if n < 0:
+        raise BinAttnError("binattn_attention_workspace", -2)
+    return torch.empty((n,), dtype=torch.uint8, device=device)
+
+
+def attention(q, k, v, bias=None, bias_kind=BIAS_NONE, grid=None, out_dtype=None, out=None, workspace=None):
+    """Whole BinaryAttention forward from q, k, v [B,H,N,d] (fp16/fp32) -> O [B,H,N,d]."""
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype or q.dtype, device=q.device)
+    if workspace is None:
+        workspace = attention_workspace(B, H, N, d, q.device)
+    bdt, ld, gh, gw = F16, 0, 0, 0
+    if bias is not None:
+        bdt = _dt(bias)
+        if bias_kind == BIAS_DENSE:
+            ld = bias.shape[-1]
+        elif bias_kind == BIAS_RELPOS:
+            gh, gw = grid
+    rc = _lib.binattn_attention(_p(q), _p(k), _p(v), _dt(q), bias_kind, bdt, _p(bias), ld, gh, gw, B, H, N, d, _p(out),
+                                _dt(out), _p(workspace), workspace.numel(), _stream())
+    _check("binattn_attention", rc)
+    return out

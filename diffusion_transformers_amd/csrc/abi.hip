@@ -33,6 +33,65 @@ int device_ready() {
 
 int launched(hipError_t e) { return e == hipSuccess ? BINATTN_OK : BINATTN_ELAUNCH; }
 
+int check_bias(int bias_kind, int bias_dtype, const void* bias, int64_t bias_ld, int grid_h, int grid_w, int N) {
+    switch (bias_kind) {
+        case BINATTN_BIAS_NONE:
+            if (bias) return BINATTN_EINVAL;
+            break;
+        case BINATTN_BIAS_DENSE: {
+            if (!bias) return BINATTN_EINVAL;
+            if (!dtype_ok(bias_dtype)) return BINATTN_EUNSUPPORTED;
+            if (bias_ld < N) return BINATTN_EINVAL;
+            const int64_t row_bytes = bias_ld * (bias_dtype == BINATTN_F32 ? 4 : 2);
+            if (row_bytes % 16 != 0 || !aligned16(bias)) return BINATTN_EALIGN;
+            break;
+        }
+        case BINATTN_BIAS_RELPOS:
+            if (!bias) return BINATTN_EINVAL;
+            if (!dtype_ok(bias_dtype)) return BINATTN_EUNSUPPORTED;
+            if (grid_h <= 0 || grid_w <= 0 || (int64_t)grid_h * grid_w != N) return BINATTN_EINVAL;
+            if (grid_w % 16 != 0 || !relpos_window_fits(grid_w)) return BINATTN_EUNSUPPORTED;
+            if (!aligned16(bias)) return BINATTN_EALIGN;
+            break;
+        default:
+            return BINATTN_EUNSUPPORTED;
+    }
+    return BINATTN_OK;
+}
+
+
+FwdArgs forward_args(const uint32_t* q_bits, const float* q_mu, const uint32_t* k_bits, const float* k_mu,
+                     const int8_t* vq, const float* vamax, int bias_dtype, const void* bias, int64_t bias_ld,
+                     int grid_h, int grid_w, int B, int H, int N, int d, void* out, int out_dtype) {
+    FwdArgs a = {};
+    a.qbits = q_bits; a.qmu = q_mu; a.kbits = k_bits; a.kmu = k_mu; a.vq = vq; a.vamax = vamax;
+    a.bias = bias; a.bias_ld = bias_ld; a.bias_f32 = bias_dtype == BINATTN_F32;
+    a.gh = grid_h; a.gw = grid_w;
+    a.B = B; a.H = H; a.N = N; a.d = d; a.W = (d + 31) / 32; a.ldv = ((int64_t)N + 63) / 64 * 64;
+    a.out = out; a.out_f32 = out_dtype == BINATTN_F32;
+    a.qk_scale = (float)(1.0 / sqrt((double)d));
+    return a;
+}
+
+// Byte offsets of the packed inputs inside a workspace (each region 256-byte aligned).
+struct WorkspaceLayout {
+    int64_t qbits, kbits, qmu, kmu, vq, vamax, total;
+};
+
+WorkspaceLayout workspace_layout(int B, int H, int N, int d) {
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t tok = (int64_t)B * H * N, W = (d + 31) / 32, ldv = ((int64_t)N + 63) / 64 * 64;
+    WorkspaceLayout l;
+    l.qbits = 0;
+    l.kbits = l.qbits + up(tok * W * 4);
+    l.qmu = l.kbits + up(tok * W * 4);
+    l.kmu = l.qmu + up(tok * 4);
+    l.vq = l.kmu + up(tok * 4);
+    l.vamax = l.vq + up((int64_t)B * H * d * ldv);
+    l.total = l.vamax + up((int64_t)B * H * d * 4);
+    return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -89,36 +148,10 @@ int binattn_forward(const uint32_t* q_bits, const float* q_mu, const uint32_t* k
     if (!aligned16(q_bits) || !aligned16(q_mu) || !aligned16(k_bits) || !aligned16(k_mu) || !aligned16(vq) ||
         !aligned16(vamax) || !aligned16(out))
         return BINATTN_EALIGN;
-    switch (bias_kind) {
-        case BINATTN_BIAS_NONE:
-            if (bias) return BINATTN_EINVAL;
-            break;
-        case BINATTN_BIAS_DENSE: {
-            if (!bias) return BINATTN_EINVAL;
-            if (!dtype_ok(bias_dtype)) return BINATTN_EUNSUPPORTED;
-            if (bias_ld < N) return BINATTN_EINVAL;
-            const int64_t row_bytes = bias_ld * (bias_dtype == BINATTN_F32 ? 4 : 2);
-            if (row_bytes % 16 != 0 || !aligned16(bias)) return BINATTN_EALIGN;
-            break;
-        }
-        case BINATTN_BIAS_RELPOS:
-            if (!bias) return BINATTN_EINVAL;
-            if (!dtype_ok(bias_dtype)) return BINATTN_EUNSUPPORTED;
-            if (grid_h <= 0 || grid_w <= 0 || (int64_t)grid_h * grid_w != N) return BINATTN_EINVAL;
-            if (grid_w % 16 != 0 || !relpos_window_fits(grid_w)) return BINATTN_EUNSUPPORTED;
-            if (!aligned16(bias)) return BINATTN_EALIGN;
-            break;
-        default:
-            return BINATTN_EUNSUPPORTED;
-    }
+    if ((rc = check_bias(bias_kind, bias_dtype, bias, bias_ld, grid_h, grid_w, N))) return rc;
     if ((rc = device_ready())) return rc;
-    FwdArgs a = {};
-    a.qbits = q_bits; a.qmu = q_mu; a.kbits = k_bits; a.kmu = k_mu; a.vq = vq; a.vamax = vamax;
-    a.bias = bias; a.bias_ld = bias_ld; a.bias_f32 = bias_dtype == BINATTN_F32;
-    a.gh = grid_h; a.gw = grid_w;
-    a.B = B; a.H = H; a.N = N; a.d = d; a.W = binattn_words(d); a.ldv = binattn_vq_ld(N);
-    a.out = out; a.out_f32 = out_dtype == BINATTN_F32;
-    a.qk_scale = (float)(1.0 / sqrt((double)d));
+    const FwdArgs a = forward_args(q_bits, q_mu, k_bits, k_mu, vq, vamax, bias_dtype, bias, bias_ld, grid_h, grid_w,
+                                   B, H, N, d, out, out_dtype);
     return launched(launch_forward(a, bias_kind, (hipStream_t)stream));
 }
 
@@ -148,6 +181,55 @@ int binattn_qk_rowstats(const uint32_t* q_bits, const uint32_t* k_bits, int B, i
     a.qbits = q_bits; a.kbits = k_bits;
     a.B = B; a.H = H; a.N = N; a.d = d; a.W = binattn_words(d);
     return launched(launch_qk_stats(a, method, rowmax, rowsum, (hipStream_t)stream));
+}
+
+int binattn_prepare(const void* q, const void* k, const void* v, int dtype, int B, int H, int N, int d,
+                    uint32_t* q_bits, float* q_mu, uint32_t* k_bits, float* k_mu, int8_t* vq, float* vamax,
+                    void* stream) {
+    if (!q || !k || !v || !q_bits || !q_mu || !k_bits || !k_mu || !vq || !vamax) return BINATTN_EINVAL;
+    int rc = check_dims(B, H, N, d);
+    if (rc) return rc;
+    if (!dtype_ok(dtype)) return BINATTN_EUNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_bits) || !aligned16(q_mu) ||
+        !aligned16(k_bits) || !aligned16(k_mu) || !aligned16(vq) || !aligned16(vamax))
+        return BINATTN_EALIGN;
+    if ((rc = device_ready())) return rc;
+    return launched(launch_prepare(q, k, v, dtype == BINATTN_F32, B * H, N, d, binattn_vq_ld(N), q_bits, q_mu,
+                                   k_bits, k_mu, vq, vamax, (hipStream_t)stream));
+}
+
+int64_t binattn_attention_workspace(int B, int H, int N, int d) {
+    if (check_dims(B, H, N, d)) return -1;
+    return workspace_layout(B, H, N, d).total;
+}
+
+int binattn_attention(const void* q, const void* k, const void* v, int dtype, int bias_kind, int bias_dtype,
+                      const void* bias, int64_t bias_ld, int grid_h, int grid_w, int B, int H, int N, int d,
+                      void* out, int out_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !out || !workspace) return BINATTN_EINVAL;
+    int rc = check_dims(B, H, N, d);
+    if (rc) return rc;
+    if (!dtype_ok(dtype) || !dtype_ok(out_dtype)) return BINATTN_EUNSUPPORTED;
+    const WorkspaceLayout l = workspace_layout(B, H, N, d);
+    if (workspace_bytes < l.total) return BINATTN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return BINATTN_EALIGN;
+    if ((rc = check_bias(bias_kind, bias_dtype, bias, bias_ld, grid_h, grid_w, N))) return rc;
+    if ((rc = device_ready())) return rc;
+    char* ws = static_cast<char*>(workspace);
+    uint32_t* qb = reinterpret_cast<uint32_t*>(ws + l.qbits);
+    uint32_t* kb = reinterpret_cast<uint32_t*>(ws + l.kbits);
+    float* qm = reinterpret_cast<float*>(ws + l.qmu);
+    float* km = reinterpret_cast<float*>(ws + l.kmu);
+    int8_t* vq = reinterpret_cast<int8_t*>(ws + l.vq);
+    float* va = reinterpret_cast<float*>(ws + l.vamax);
+    hipError_t e = launch_prepare(q, k, v, dtype == BINATTN_F32, B * H, N, d, binattn_vq_ld(N), qb, qm, kb, km, vq,
+                                  va, (hipStream_t)stream);
+    if (e != hipSuccess) return BINATTN_ELAUNCH;
+    const FwdArgs a = forward_args(qb, qm, kb, km, vq, va, bias_dtype, bias, bias_ld, grid_h, grid_w, B, H, N, d,
+                                   out, out_dtype);
+    return launched(launch_forward(a, bias_kind, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,225 @@
+// prep.h -- device bodies of the input-side steps, shared by the single-purpose kernels and
+// the one-launch preparation kernel.
+//
+// "BinaryAttention" paper notes (CVPR 2026), Method details:
+//   key design 1: each channel of Q and K keeps only its sign; a per-token scale mu
+//                 (mean |x| over the d channels) keeps the magnitude;
+//   key design 3: V is quantised channel-wise to int8 with scale a_c / 127, a_c the
+//                 channel's absmax over the tokens of one (batch, head).
+#pragma once
+
+#include "common.h"
+
+namespace binattn {
+
+// Sign words and mu of the tokens of workgroup `blk`: kPackSub contiguous spans of
+// floor(256 / (d/8)) tokens, one 8-channel chunk (16 or 32 bytes) per thread and span.  All of
+// a thread's chunk loads are issued first (enough bytes in flight per compute unit to stream
+// at HBM rate); then per span each chunk yields one sign byte and a partial |x| sum, which meet
+// in LDS, where thread t assembles token t's words and mu in channel order.
+// sBits: 256*16 bytes, sSum: 256 floats.
+constexpr int kPackSub = 16;
+
+template <typename T>
+__host__ __device__ inline int64_t pack_blocks(int64_t ntok, int d) {
+    const int ntw = 256 / (d / 8);
+    return (ntok + (int64_t)ntw * kPackSub - 1) / ((int64_t)ntw * kPackSub);
+}
+
+template <typename T>
+__device__ __forceinline__ void pack_block(const T* __restrict__ x, int64_t ntok, int d, int W,
+                                           uint32_t* __restrict__ bits, float* __restrict__ mu, int64_t blk,
+                                           uint8_t* sBits, float* sSum) {
+    typedef T vec8 __attribute__((ext_vector_type(8)));  // one chunk: 8 channels
+    const int tid = threadIdx.x;
+    const int cpt = d >> 3;                               // chunks per token
+    const int ntw = 256 / cpt;                            // tokens per span
+    const int t = tid / cpt, part = tid - t * cpt;
+    vec8 v[kPackSub];
+#pragma unroll
+    for (int u = 0; u < kPackSub; ++u) {
+        const int64_t tok = (blk * kPackSub + u) * ntw + t;
+        if (t < ntw && tok < ntok) {
+            v[u] = *reinterpret_cast<const vec8*>(x + tok * d + 8 * part);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[u][e] = (T)0;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kPackSub; ++u) {
+        const int64_t t0 = (blk * kPackSub + u) * ntw;
+        uint32_t byte = 0;
+        float sum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float f = (float)v[u][e];
+            byte |= (f >= 0.0f ? 1u : 0u) << e;  // -0.0 >= 0 holds: zero counts as +1
+            sum += fabsf(f);
+        }
+        // bytes past the token's d channels read as zero
+        reinterpret_cast<uint4*>(sBits)[tid] = make_uint4(0, 0, 0, 0);
+        __syncthreads();
+        if (t < ntw) {
+            sBits[t * 16 + part] = (uint8_t)byte;
+            sSum[tid] = sum;  // tid == t * cpt + part
+        }
+        __syncthreads();
+        if (tid < ntw && t0 + tid < ntok) {
+            const int64_t o = t0 + tid;
+            const uint4 w = reinterpret_cast<const uint4*>(sBits)[tid];
+            uint32_t* out = bits + o * W;
+            out[0] = w.x;
+            if (W > 1) out[1] = w.y;
+            if (W > 2) out[2] = w.z;
+            if (W > 3) out[3] = w.w;
+            float acc = 0.0f;
+            for (int p = 0; p < cpt; ++p) acc += sSum[tid * cpt + p];
+            mu[o] = acc / (float)d;
+        }
+        __syncthreads();  // the LDS is reused by the next span
+    }
+}
+
+constexpr int kQuantTS = 64 + 4;  // LDS row stride (bytes) of the 64-token transpose tile: 17 dwords, so
+                                  // rows of consecutive channels fall in different banks
+
+template <typename T>
+struct QuantVec {
+    static constexpr int VE = 16 / sizeof(T);  // elements per 16-byte chunk
+    typedef T type __attribute__((ext_vector_type(VE)));
+};
+
+// Chunks (one token x VE channels) per thread when thread (part, grp) of one head holds the
+// 4-token groups grp, grp + G, ... (G = 256 / (d / VE)) of its channel part.
+template <typename T>
+__host__ __device__ inline int quant_chunks_per_thread(int N, int d) {
+    const int G = 256 / (d / QuantVec<T>::VE);
+    return 4 * (((N + 3) / 4 + G - 1) / G);
+}
+
+// 4 tokens x 4 channels of int8 (dword t = token t, byte c = channel c) -> dword c = channel c,
+// byte t = token t.
+__device__ __forceinline__ void transpose4x4(const uint32_t (&in)[4], uint32_t (&out)[4]) {
+    const uint32_t ab_lo = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);  // a0 b0 a1 b1
+    const uint32_t ab_hi = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);  // a2 b2 a3 b3
+    const uint32_t cd_lo = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
+    const uint32_t cd_hi = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
+    out[0] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);  // a0 b0 c0 d0
+    out[1] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);  // a1 b1 c1 d1
+    out[2] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
+}
+
+// Channel-wise int8 quantisation of one head with its V held in registers (MAXC chunks per
+// thread, in groups of 4 consecutive tokens): absmax per channel (registers, then LDS across
+// thread groups), IEEE 127 / a, rint, clamp to +-127 -- every chunk quantised in registers --
+// then per 64-token block each 4-token group is transposed in registers (v_perm) into one
+// dword per channel, written to an LDS tile of channel rows, and stored as 16-byte rows of
+// ldv keys; tokens >= N are written as 0.  sRed: 256*VE floats, sAmax: 128 floats,
+// sT: 128 * kQuantTS bytes (16-byte aligned).
+template <typename T, int MAXC>
+__device__ __forceinline__ void quant_head_regs(const T* __restrict__ v, int N, int d, int64_t ldv, int64_t bh,
+                                                int8_t* __restrict__ vq, float* __restrict__ vamax, float* sRed,
+                                                float* sAmax, uint8_t* sT) {
+    constexpr int VE = QuantVec<T>::VE;
+    constexpr int VW = VE / 4;  // dwords of quantised bytes per chunk
+    constexpr int MAXU = MAXC / 4;
+    typedef typename QuantVec<T>::type vecT;
+    const int tid = threadIdx.x;
+    const int P = d / VE, G = 256 / P;
+    const int part = tid % P, grp = tid / P;
+    const T* vh = v + bh * (int64_t)N * d;
+    vecT x[MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int n = 4 * (grp + G * (i >> 2)) + (i & 3);
+        if (grp < G && n < N) {
+            x[i] = *reinterpret_cast<const vecT*>(vh + (int64_t)n * d + part * VE);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) x[i][e] = (T)0;
+        }
+    }
+    // absmax in the input precision (exact: max and |.| do not round)
+    vecT mv;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) mv[e] = (T)0;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) mv = __builtin_elementwise_max(mv, __builtin_elementwise_abs(x[i]));
+    if (grp < G) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) sRed[grp * d + part * VE + e] = (float)mv[e];
+    }
+    __syncthreads();
+    if (tid < d) {
+        float a = 0.0f;
+        for (int g = 0; g < G; ++g) a = fmaxf(a, sRed[g * d + tid]);
+        vamax[bh * d + tid] = a;
+        sAmax[tid] = a;
+    }
+    __syncthreads();
+    float inv[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+        const float a = grp < G ? sAmax[part * VE + e] : 0.0f;
+        inv[e] = a > 0.0f ? 127.0f / a : 0.0f;
+    }
+    // quantise every chunk and transpose each 4-token group: qt[u][e] = channel part*VE+e,
+    // bytes = tokens 4*(grp+G*u) .. +3
+    uint32_t qt[MAXU][VE];
+#pragma unroll
+    for (int u = 0; u < MAXU; ++u) {
+        uint32_t qb[4][VW];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int w = 0; w < VW; ++w) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    float q = __builtin_rintf((float)x[4 * u + r][4 * w + b] * inv[4 * w + b]);
+                    q = fminf(fmaxf(q, -127.0f), 127.0f);
+                    word = __builtin_amdgcn_cvt_pk_u8_f32(q + 128.0f, b, word);  // exact: q is an integer
+                }
+                qb[r][w] = word ^ 0x80808080u;  // back to two's-complement int8
+            }
+#pragma unroll
+        for (int w = 0; w < VW; ++w) {
+            const uint32_t in[4] = {qb[0][w], qb[1][w], qb[2][w], qb[3][w]};
+            uint32_t out[4];
+            transpose4x4(in, out);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) qt[u][4 * w + c] = out[c];
+        }
+    }
+    int8_t* vqh = vq + bh * d * ldv;
+    const int nblk = (int)(ldv / 64);
+    for (int jb = 0; jb < nblk; ++jb) {
+        const int j0 = jb * 64;
+        if (j0 + 64 > N) {  // ragged last block: positions past N stay 0
+            for (int id = tid; id < 128 * kQuantTS / 16; id += 256) reinterpret_cast<uint4*>(sT)[id] = make_uint4(0, 0, 0, 0);
+            __syncthreads();
+        }
+        if (grp < G) {
+#pragma unroll
+            for (int u = 0; u < MAXU; ++u) {
+                const int n0 = 4 * (grp + G * u);  // first token of the group (tokens past N hold 0)
+                if (n0 >= j0 && n0 < j0 + 64 && n0 < N) {
+#pragma unroll
+                    for (int e = 0; e < VE; ++e)
+                        *reinterpret_cast<uint32_t*>(sT + (part * VE + e) * kQuantTS + (n0 - j0)) = qt[u][e];
+                }
+            }
+        }
+        __syncthreads();
+        for (int id = tid; id < d * 16; id += 256) {  // one dword per thread: c = id / 16, keys 4*(id%16)..
+            const int c = id >> 4, q = id & 15;
+            *reinterpret_cast<uint32_t*>(vqh + (int64_t)c * ldv + j0 + 4 * q) =
+                *reinterpret_cast<const uint32_t*>(sT + c * kQuantTS + 4 * q);
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace binattn

@@ -1,0 +1,80 @@
+// prep.hip -- the input side of the forward in one launch: sign words and mu of Q and of K
+// ([notes] key design 1) and the channel-wise int8 V ([notes] key design 3), where
+// [notes] is the "BinaryAttention" paper notes page (CVPR 2026), Method details.
+//
+// One grid, two kinds of workgroup: B*H quantise one head each with its V held in registers,
+// the rest pack contiguous spans of Q tokens and then of K tokens.  The two kinds are
+// interleaved in launch order (one head every R blocks), so the compute units always hold a
+// mix: packing streams HBM while the quantisers compute.  Heads whose V does not fit the register budget take the general path:
+// the pack kernel, then the absmax and quantise kernels.
+#include "common.h"
+#include "internal.h"
+#include "prep.h"
+
+namespace binattn {
+
+template <typename T, int MAXC>
+__global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                   const T* __restrict__ v, int BH, int N, int d, int W,
+                                                   int64_t ldv, int64_t npack, int R, uint32_t* __restrict__ qbits,
+                                                   float* __restrict__ qmu, uint32_t* __restrict__ kbits,
+                                                   float* __restrict__ kmu, int8_t* __restrict__ vq,
+                                                   float* __restrict__ vamax) {
+    // LDS shared by the two roles: quantise uses sRed (8 KB) + sAmax + the transpose tile,
+    // pack uses the sign bytes and partial sums.
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2048 * 4 + 128 * 4 + 128 * kQuantTS];
+    const int64_t b = blockIdx.x;
+    const int64_t span = (int64_t)R * BH;  // blocks [0, span): head b / R where b % R == 0
+    if (b < span && b % R == 0) {
+        quant_head_regs<T, MAXC>(v, N, d, ldv, b / R, vq, vamax, reinterpret_cast<float*>(smem),
+                                 reinterpret_cast<float*>(smem + 2048 * 4), smem + 2048 * 4 + 128 * 4);
+        return;
+    }
+    const int64_t ntok = (int64_t)BH * N;
+    uint8_t* sBits = smem;
+    float* sSum = reinterpret_cast<float*>(smem + 256 * 16);
+    const int64_t pb = b < span ? b - (b + R - 1) / R : b - BH;  // minus the heads placed before b
+    if (pb < npack)
+        pack_block<T>(q, ntok, d, W, qbits, qmu, pb, sBits, sSum);
+    else
+        pack_block<T>(k, ntok, d, W, kbits, kmu, pb - npack, sBits, sSum);
+}
+
+template <typename T>
+static hipError_t launch_prepare_t(const T* q, const T* k, const T* v, int BH, int N, int d, int64_t ldv,
+                                   uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu, int8_t* vq,
+                                   float* vamax, hipStream_t s) {
+    const int W = (d + 31) / 32;
+    const int64_t ntok = (int64_t)BH * N;
+    const int64_t npack = pack_blocks<T>(ntok, d);
+    const int nc = quant_chunks_per_thread<T>(N, d);
+    const int64_t nblocks = BH + 2 * npack;
+    if (nblocks <= 0x7fffffff && nc <= 20) {
+        const dim3 grid((unsigned)nblocks), block(256);
+        const int R = (int)(nblocks / BH);
+        if (nc <= 8)
+            hipLaunchKernelGGL((prep_kernel<T, 8>), grid, block, 0, s, q, k, v, BH, N, d, W, ldv, npack, R, qbits, qmu,
+                               kbits, kmu, vq, vamax);
+        else
+            hipLaunchKernelGGL((prep_kernel<T, 20>), grid, block, 0, s, q, k, v, BH, N, d, W, ldv, npack, R, qbits,
+                               qmu, kbits, kmu, vq, vamax);
+        return hipGetLastError();
+    }
+    const int f32 = sizeof(T) == 4;
+    hipError_t e = launch_pack_qk(q, f32, ntok, d, qbits, qmu, s);
+    if (e == hipSuccess) e = launch_pack_qk(k, f32, ntok, d, kbits, kmu, s);
+    if (e == hipSuccess) e = launch_quant_v(v, f32, BH, N, d, ldv, vq, vamax, s);
+    return e;
+}
+
+hipError_t launch_prepare(const void* q, const void* k, const void* v, int f32, int BH, int N, int d, int64_t ldv,
+                          uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu, int8_t* vq, float* vamax,
+                          hipStream_t s) {
+    if (f32)
+        return launch_prepare_t<float>((const float*)q, (const float*)k, (const float*)v, BH, N, d, ldv, qbits, qmu,
+                                       kbits, kmu, vq, vamax, s);
+    return launch_prepare_t<_Float16>((const _Float16*)q, (const _Float16*)k, (const _Float16*)v, BH, N, d, ldv,
+                                      qbits, qmu, kbits, kmu, vq, vamax, s);
+}
+
+}  // namespace binattn

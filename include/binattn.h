@@ -127,12 +127,13 @@ int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t
  * Computes, per (b, h, query i):
  *   D_ij = d - 2 popcount(q_bits_i XOR k_bits_j)                (exact integer)
  *   S_ij = q_mu_i * k_mu_j * D_ij / sqrt(d) + b_ij             (fp32)
- *   streamed over key tiles with a running row max m and row sum l:
- *   P^_ij = rint(255 * exp(S_ij - m)) in [0,255], l = sum exp(S_ij - m) (fp32),
- *   O_ic = s_c * sum_j P^_ij vq_cj / (255 * l_i)
- * (integer PV; the max used for a key tile is the running max after that tile,
- * so P^ may differ by the rounding of an earlier tile from a two-pass exact-max
- * result).
+ *   m = row max of S, l = sum_j exp(S_ij - m) (fp32),
+ *   P^_ij = rint(255 * exp(S_ij - m)) in [0,255],
+ *   O_ic = s_c * sum_j P^_ij vq_cj / (255 * l_i)                (integer PV)
+ * For N <= 256 m is the exact row max (two passes).  Longer rows are streamed over
+ * key tiles with a running max: a tile is quantised against the max known after it
+ * and earlier tiles are rescaled, so P^ may differ by one rounding from the
+ * exact-max result.
  */
 int binattn_forward(const uint32_t* q_bits, const float* q_mu, const uint32_t* k_bits, const float* k_mu,
                     const int8_t* vq, const float* vamax, int bias_kind, int bias_dtype, const void* bias,
@@ -162,6 +163,36 @@ int binattn_scores_i32(const uint32_t* q_bits, const uint32_t* k_bits, int B, in
  *   rowmax [B,H,N] fp32 = max_j D_ij;  rowsum [B,H,N] fp32 = sum_j D_ij (both exact)
  * Errors as binattn_scores_i32; an unknown method is BINATTN_EUNSUPPORTED.
  */
+/*
+ * binattn_prepare -- the three input-side calls in one launch where it fits: identical
+ * results to binattn_pack_qk(q), binattn_pack_qk(k) and binattn_quant_v(v) (same
+ * arguments, same outputs, same errors).  Passages: key designs 1 and 3.
+ */
+int binattn_prepare(const void* q, const void* k, const void* v, int dtype, int B, int H, int N, int d,
+                    uint32_t* q_bits, float* q_mu, uint32_t* k_bits, float* k_mu, int8_t* vq, float* vamax,
+                    void* stream);
+
+/*
+ * binattn_attention -- the whole forward from fp16/fp32 Q, K, V: binattn_prepare into
+ * the caller's workspace, then binattn_forward.  The pages present the method as a
+ * drop-in replacement of attention; this is that call.
+ *
+ *   q, k, v    [B,H,N,d] of dtype (contiguous)
+ *   bias...    as binattn_forward
+ *   out        [B,H,N,d] of out_dtype
+ *   workspace  device memory of at least binattn_attention_workspace(B,H,N,d) bytes,
+ *              256-byte aligned, owned by the caller; it receives the packed Q/K and
+ *              the quantised V (contents unspecified after the call).  Calls that
+ *              share a workspace must be ordered on one stream.
+ * binattn_attention_workspace returns -1 for unsupported sizes.  Errors as the two
+ * calls it makes; a workspace smaller than required is BINATTN_EINVAL, a misaligned
+ * one BINATTN_EALIGN.
+ */
+int64_t binattn_attention_workspace(int B, int H, int N, int d);
+int binattn_attention(const void* q, const void* k, const void* v, int dtype, int bias_kind, int bias_dtype,
+                      const void* bias, int64_t bias_ld, int grid_h, int grid_w, int B, int H, int N, int d,
+                      void* out, int out_dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
 #define BINATTN_QK_MFMA 0
 #define BINATTN_QK_POPCOUNT 1
 int binattn_qk_rowstats(const uint32_t* q_bits, const uint32_t* k_bits, int B, int H, int N, int d, int method,

@@ -95,6 +95,36 @@ def test_forward_validation(lib):
     assert lib.binattn_qk_rowstats(_a(256), _a(516), 1, 1, 4, 64, 1, _a(1024), _a(768), None) == -3
 
 
+def test_prepare_and_attention_validation(lib):
+    import ctypes as C
+    lib.binattn_attention_workspace.restype = C.c_int64
+    ws = lib.binattn_attention_workspace(2, 3, 197, 64)
+    # bits (2 x 1182 tokens x 2 words), mu (2 x 1182), V^ (6 x 64 x 256), absmax, each 256-aligned
+    up = lambda x: (x + 255) // 256 * 256
+    assert ws == 2 * up(1182 * 8) + 2 * up(1182 * 4) + up(6 * 64 * 256) + up(6 * 64 * 4)
+    assert lib.binattn_attention_workspace(2, 3, 197, 60) == -1
+    P = C.c_void_p
+    i64 = C.c_int64
+    pre = [P(256), P(512), P(768), 1, 2, 3, 197, 64, P(1024), P(1280), P(1536), P(1792), P(2048), P(2304), None]
+    bad = list(pre); bad[0] = None
+    assert lib.binattn_prepare(*bad) == -1
+    bad = list(pre); bad[3] = 9
+    assert lib.binattn_prepare(*bad) == -2
+    bad = list(pre); bad[8] = P(1028)
+    assert lib.binattn_prepare(*bad) == -3
+    att = [P(256), P(512), P(768), 1, 0, 1, None, i64(0), 0, 0, 2, 3, 197, 64, P(4096), 1, P(1 << 20), i64(ws), None]
+    lib.binattn_attention.argtypes = [P, P, P, C.c_int, C.c_int, C.c_int, P, C.c_int64, C.c_int, C.c_int, C.c_int,
+                                      C.c_int, C.c_int, C.c_int, P, C.c_int, P, C.c_int64, P]
+    bad = list(att); bad[17] = i64(ws - 1)
+    assert lib.binattn_attention(*bad) == -1          # workspace too small
+    bad = list(att); bad[16] = P((1 << 20) + 16)
+    assert lib.binattn_attention(*bad) == -3          # workspace not 256-byte aligned
+    bad = list(att); bad[16] = None
+    assert lib.binattn_attention(*bad) == -1
+    bad = list(att); bad[4] = 1                        # dense bias kind without data
+    assert lib.binattn_attention(*bad) == -1
+
+
 def test_valid_arguments_without_a_device_report_enodevice(lib):
     import torch
     if torch.cuda.is_available():
@@ -102,3 +132,5 @@ def test_valid_arguments_without_a_device_report_enodevice(lib):
     assert lib.binattn_pack_qk(_a(256), 1, 2, 3, 5, 64, _a(512), _a(1024), None) == -4
     assert _fwd(lib) == -4
     assert _fwd(lib, kind=2, bias=_a(4096), gh=16, gw=16) == -4
+    assert lib.binattn_prepare(_a(256), _a(512), _a(768), 1, 2, 3, 197, 64, _a(1024), _a(1280), _a(1536),
+                               _a(1792), _a(2048), _a(2304), None) == -4

@@ -77,3 +77,45 @@ def test_graph_replays_split_quant_path():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(vq, ref_q) and torch.equal(vs, ref_s), f"replay {rep}"
+
+
+@pytest.mark.parametrize("name", ["deit_s_224", "dit_xl2_256"])
+def test_graph_replays_attention(name):
+    """binattn_attention (one preparation launch + forward) captured in a graph, as bench.py
+    replays it: every replay equals the eager result."""
+    from diffusion_transformers_amd import binding as b
+    dev = "cuda:0"
+    w = W.BY_NAME[name]
+    inp = W.custom(4, w.H, w.N, w.d, w.dtype, w.bias, w.grid, seed=33)
+    q, k, v = (torch.from_numpy(inp[n]).to(dev) for n in ("q", "k", "v"))
+    bias, kind, grid = None, b.BIAS_NONE, None
+    if w.bias == "dense":
+        bias, kind = b.aligned_dense_bias(torch.from_numpy(inp["bias"]).to(dev)), b.BIAS_DENSE
+    elif w.bias == "relpos":
+        bias, kind, grid = torch.from_numpy(inp["bias"]).to(dev), b.BIAS_RELPOS, w.grid
+    ws = b.attention_workspace(4, w.H, w.N, w.d, dev)
+    out = torch.empty((4, w.H, w.N, w.d), dtype=torch.float16, device=dev)
+
+    def step():
+        b.attention(q, k, v, bias, kind, grid, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        out.zero_()
+        ws.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep} differs from eager"
+        _ = (q.float() * 2).sum().item()  # unrelated eager work between replays

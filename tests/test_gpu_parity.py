@@ -154,6 +154,46 @@ def test_qk_tile_probe_both_methods(method, d, N):
     np.testing.assert_array_equal(s.cpu().numpy(), D.sum(axis=-1).astype(np.float32))
 
 
+# ---------------------------------------------------------------- one-launch preparation and whole attention
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("B,H,N,d", [(1, 1, 1, 64), (2, 3, 197, 64), (1, 2, 577, 64), (2, 2, 256, 72),
+                                     (1, 1, 65, 128), (1, 2, 33, 8), (1, 1, 2049, 64)])
+def test_prepare_equals_separate_calls(dtype, B, H, N, d):
+    """binattn_prepare (one launch where V fits registers, else the general kernels) gives the
+    same bits, mu, V^ and absmax as the three separate calls, bit for bit."""
+    _say(f"prepare {dtype} {B}x{H}x{N}x{d}")
+    inp = W.custom(B, H, N, d, dtype, "none", seed=7 * N + d)
+    b = _b()
+    q, k, v = _t(inp["q"]), _t(inp["k"]), _t(inp["v"])
+    got = b.prepare(q, k, v)
+    ref = (*b.pack_qk(q), *b.pack_qk(k), *b.quant_v(v))
+    torch.cuda.synchronize()
+    for name, x, y in zip(("qbits", "qmu", "kbits", "kmu", "vq", "vamax"), got, ref):
+        assert torch.equal(x, y), name
+
+
+@pytest.mark.parametrize("name", ["deit_t_toy", "deit_s_224", "dit_xl2_256"])
+def test_attention_equals_pipeline(name):
+    """binattn_attention gives exactly the output of the four separate calls, and the oracle's."""
+    _say(f"attention {name}")
+    w = W.BY_NAME[name]
+    inp = W.make(w, seed=3)
+    b = _b()
+    g = gpu_pipeline(inp)
+    bias, kind, grid = None, b.BIAS_NONE, None
+    if w.bias == "dense":
+        bias, kind = b.aligned_dense_bias(_t(inp["bias"])), b.BIAS_DENSE
+    elif w.bias == "relpos":
+        bias, kind, grid = _t(inp["bias"]), b.BIAS_RELPOS, w.grid
+    o = b.attention(_t(inp["q"]), _t(inp["k"]), _t(inp["v"]), bias, kind, grid)
+    torch.cuda.synchronize()
+    assert torch.equal(o, g["o"])
+    rows = _sample_rows(w.B, w.H, w.N, 256, seed=2)
+    ref = oracle.forward_rows(inp["q"], inp["k"], inp["v"], rows, inp["bias"], oracle_kind(w), grid=grid)
+    assert_o(o.cpu().numpy().reshape(-1, w.d)[rows], ref, float(np.abs(inp["v"].astype(np.float64)).max()), name)
+
+
 # ---------------------------------------------------------------- forward, small and ragged
 
 SMALL = [
