@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbinattn.so")
-SOURCES = ["pack.hip", "quant.hip", "prep.hip", "forward.hip", "abi.hip"]
+SOURCES = ["pack.hip", "quant.hip", "prep.hip", "forward.hip", "attention.hip", "abi.hip"]
 ARCH = "gfx950"
 
 

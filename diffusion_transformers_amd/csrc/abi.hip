@@ -217,6 +217,15 @@ int binattn_attention(const void* q, const void* k, const void* v, int dtype, in
         return BINATTN_EALIGN;
     if ((rc = check_bias(bias_kind, bias_dtype, bias, bias_ld, grid_h, grid_w, N))) return rc;
     if ((rc = device_ready())) return rc;
+    if (dtype == BINATTN_F16) {  // short rows: one kernel straight from Q, K, V
+        FwdArgs f = forward_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, bias_dtype, bias, bias_ld,
+                                 grid_h, grid_w, B, H, N, d, out, out_dtype);
+        f.q_raw = static_cast<const _Float16*>(q);
+        f.k_raw = static_cast<const _Float16*>(k);
+        f.v_raw = static_cast<const _Float16*>(v);
+        const hipError_t e = launch_attention_fused(f, bias_kind, (hipStream_t)stream);
+        if (e != hipErrorNotSupported) return launched(e);
+    }
     char* ws = static_cast<char*>(workspace);
     uint32_t* qb = reinterpret_cast<uint32_t*>(ws + l.qbits);
     uint32_t* kb = reinterpret_cast<uint32_t*>(ws + l.kbits);

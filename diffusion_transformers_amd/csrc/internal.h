@@ -23,6 +23,9 @@ struct FwdArgs {
     int out_f32;
     float qk_scale;       // 1 / sqrt(d)
     int32_t* scores;      // scores export only
+    const _Float16* q_raw;  // whole-attention path: fp16 Q, K, V [B,H,N,d] (packed inputs above unused)
+    const _Float16* k_raw;
+    const _Float16* v_raw;
 };
 
 hipError_t launch_pack_qk(const void* x, int f32, int64_t ntok, int d, uint32_t* bits, float* mu,
@@ -33,6 +36,9 @@ hipError_t launch_prepare(const void* q, const void* k, const void* v, int f32, 
                           uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu, int8_t* vq, float* vamax,
                           hipStream_t s);
 hipError_t launch_forward(const FwdArgs& a, int bias_kind, hipStream_t s);
+// Whole attention from fp16 Q, K, V in one kernel where the shape allows it (short rows);
+// returns hipErrorNotSupported, launching nothing, where it does not.
+hipError_t launch_attention_fused(const FwdArgs& a, int bias_kind, hipStream_t s);
 hipError_t launch_scores(const FwdArgs& a, hipStream_t s);
 hipError_t launch_qk_stats(const FwdArgs& a, int method, float* rowmax, float* rowsum, hipStream_t s);
 bool relpos_window_fits(int gw);

@@ -1,0 +1,778 @@
+// tile.h -- device building blocks of the BinaryAttention forward kernels (tile staging,
+// Q operand, bias, score tile, quantised probabilities, epilogue) and the short-row kernel,
+// shared by the forward from packed inputs and the whole-attention path.
+#pragma once
+
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+#include "prep.h"
+
+namespace binattn {
+
+constexpr int kWaves = 4;
+constexpr int kBR = kWaves * 16;            // queries per workgroup (16 per wave)
+constexpr int kBC = 64;                     // keys per tile
+constexpr int kRelposWin = 1024;            // fp32 entries of a staged relative-position window
+constexpr int kKeepTiles = 4;               // rows of at most this many tiles: exact max, scores in registers
+constexpr int kDeferTiles = 16;             // streamed rows of at least this many tiles accumulate in int32
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLog2_255 = 7.99435343685886f;
+
+enum { BK_NONE = 0, BK_DENSE_F16 = 1, BK_DENSE_F32 = 2, BK_RELPOS = 3 };
+
+// Keys of one 64-key tile as A-operand rows: MFMA tile t, row m <-> key 16*(m/4) + 4t + (m%4).
+// After the MFMA, lane (n, g) register r of tile t holds key 16g + 4t + r.
+__device__ __forceinline__ int key_slot(int j, int& t) {
+    t = (j & 15) >> 2;
+    return 4 * (j >> 4) + (j & 3);
+}
+
+// V^ channels as A-operand rows of the PV MFMA: tile ct, row m <-> channel 4*NT*(m/4) + 4*ct + (m%4).
+// After the MFMA, lane (query n, group g) register r of tile ct holds channel 4*NT*g + 4*ct + r.
+template <int NT>
+__device__ __forceinline__ int chan_slot(int c, int& ct) {
+    const int q = c / (4 * NT), rem = c - q * (4 * NT);
+    ct = rem >> 2;
+    return 4 * q + (rem & 3);
+}
+
+// Raw global data of one tile held in registers between its load and its LDS store.
+template <int NT, int TW>
+struct TileRegs {
+    static constexpr int W = (NT + 1) / 2;                 // sign words per key
+    static constexpr int KT = (kBC * W + 255) / 256;       // K word tasks per thread
+    static constexpr int VCH = (NT * 64 + 255) / 256;      // 16-byte V^ chunks per thread
+    uint32_t kw[KT];
+    uint4 v[VCH];
+    float mu;
+    float tw[TW / 256 > 0 ? TW / 256 : 1];
+};
+
+// LDS of one tile (a multiple of 16 bytes, so consecutive tiles keep 16-byte alignment).
+// TW: fp32 entries of the tile's relative-position window (streamed rows), else 4.
+template <int NT, int TW>
+struct alignas(16) TileLds {
+    static constexpr int W = (NT + 1) / 2;
+    uint32_t k[4 * W * 16 * 8];            // [t][group][row] x 32 B: A operand of QK MFMA t, lane (row, group)
+    uint32_t v[NT * kWave * 4];            // [ct][lane] x 16 B: A operand of PV MFMA ct
+    float mu[kBC];
+    float tw[TW];
+};
+
+struct RelposWin {
+    int dr_lo, row_len, count;
+};
+
+// Rows of the relative-position table touched by queries [q0, q0+kBR) and keys [j0, j1).
+__device__ __forceinline__ RelposWin relpos_window(int q0, int j0, int j1, int N, int gh, int gw) {
+    const int ri_min = q0 / gw, ri_max = (min(q0 + kBR, N) - 1) / gw;
+    const int rj_min = j0 / gw, rj_max = (min(j1, N) - 1) / gw;
+    RelposWin w;
+    w.dr_lo = ri_min - rj_max + gh - 1;
+    w.row_len = 2 * gw - 1;
+    w.count = ((ri_max - ri_min) + (rj_max - rj_min) + 1) * w.row_len;
+    return w;
+}
+
+// Per-workgroup pointers of one (b, h).
+struct HeadPtrs {
+    const uint32_t* kb;
+    const float* kmu;
+    const int8_t* vq;
+    const void* table;  // relative-position table of head h
+};
+
+// Loads PER window entries per thread (entry tid + 256 i) of a head's relative-position table,
+// starting at element off, as fp32.  Entries past the table read as 0.
+template <int PER>
+__device__ __forceinline__ void load_window(float (&dst)[PER], const FwdArgs& a, const void* table, int off) {
+    const int tid = threadIdx.x;
+    const int tsz = (2 * a.gh - 1) * (2 * a.gw - 1);
+    if (a.bias_f32) {
+        const __amdgpu_buffer_rsrc_t tr = buffer_rsrc((const float*)table + off, (tsz - off) * 4);
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            dst[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(tr, (tid + 256 * i) * 4, 0, 0));
+    } else {
+        const __amdgpu_buffer_rsrc_t tr = buffer_rsrc((const _Float16*)table + off, (tsz - off) * 2);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const uint16_t hbits = __builtin_amdgcn_raw_buffer_load_b16(tr, (tid + 256 * i) * 2, 0, 0);
+            dst[i] = (float)__builtin_bit_cast(_Float16, hbits);
+        }
+    }
+}
+
+template <int NT, int TW>
+__device__ __forceinline__ void load_tile(TileRegs<NT, TW>& r, const FwdArgs& a, const HeadPtrs& hp, int q0,
+                                          int j0) {
+    typedef TileRegs<NT, TW> R;
+    const int tid = threadIdx.x, N = a.N, d = a.d;
+    // sign words of keys j0.. (keys >= N read as 0)
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(hp.kb + j0 * R::W, (N - j0) * R::W * 4);
+#pragma unroll
+    for (int i = 0; i < R::KT; ++i)
+        r.kw[i] = __builtin_amdgcn_raw_buffer_load_b32(kr, (tid + 256 * i) * 4, 0, 0);
+    // V^ keys j0 .. j0+63 of every channel slot (channels >= d read as 0)
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(hp.vq + j0, d * (int)a.ldv - j0);
+#pragma unroll
+    for (int i = 0; i < R::VCH; ++i) {
+        const int id = tid + 256 * i;
+        const int c = id >> 2, gg = id & 3;
+        const v4i x = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(vr, (int)(c * a.ldv) + 16 * gg, 0, 0));
+        r.v[i] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
+    const __amdgpu_buffer_rsrc_t mr = buffer_rsrc(hp.kmu + j0, (N - j0) * 4);
+    r.mu = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mr, (tid & 63) * 4, 0, 0));
+    if constexpr (TW >= 256) {
+        const RelposWin w = relpos_window(q0, j0, j0 + kBC, N, a.gh, a.gw);
+        load_window<TW / 256>(r.tw, a, hp.table, w.dr_lo * w.row_len);
+    }
+}
+
+template <int NT, int TW>
+__device__ __forceinline__ void store_tile(const TileRegs<NT, TW>& r, TileLds<NT, TW>& s, int d) {
+    typedef TileRegs<NT, TW> R;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < R::KT; ++i) {
+        const int id = tid + 256 * i;
+        if (id < kBC * R::W) {
+            const int j = id / R::W, w = id % R::W;
+            uint32_t word = r.kw[i];
+            const int left = d - 32 * w;  // channels >= d contribute nothing
+            if (left < 32) word &= (1u << left) - 1u;
+            uint32_t o[8];
+            unpack_bits32_f8(word, o);
+            int t;
+            const int m = key_slot(j, t);
+            uint32_t* dst = &s.k[((t * R::W + w) * 16 + m) * 8];
+            *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<uint4*>(dst + 4) = make_uint4(o[4], o[5], o[6], o[7]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < R::VCH; ++i) {
+        const int id = tid + 256 * i;
+        if (id < NT * 64) {
+            const int c = id >> 2, gg = id & 3;
+            int ct;
+            const int m = chan_slot<NT>(c, ct);
+            *reinterpret_cast<uint4*>(&s.v[(ct * kWave + m + 16 * gg) * 4]) = r.v[i];
+        }
+    }
+    if (tid < kBC) s.mu[tid] = r.mu;
+    if constexpr (TW >= 256) {
+#pragma unroll
+        for (int i = 0; i < TW / 256; ++i) s.tw[tid + 256 * i] = r.tw[i];
+    }
+}
+
+// Q operand (B of the QK MFMA) for one lane: fp8 2*sign of channels 32g .. 32g+31 (0 past d);
+// returns -sum of the query's d signs (the accumulator seed), 0 for a query past N.
+template <int W>
+__device__ __forceinline__ float load_q(const uint32_t* __restrict__ qrow, bool live, int d, int g, v8i& q) {
+    uint32_t o[8];
+    const uint32_t word = (live && g < W) ? qrow[g] : 0u;
+    unpack_signs32_f8x2(word, o);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) q[c] = (live && g < W && 32 * g + 4 * c < d) ? (int)o[c] : 0;
+    int pos = 0;
+    if (live) {
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const int left = d - 32 * w;
+            const uint32_t mask = left >= 32 ? 0xFFFFFFFFu : ((1u << left) - 1u);
+            pos += __builtin_popcount(qrow[w] & mask);
+        }
+    }
+    return live ? (float)(d - 2 * pos) : 0.0f;  // -(pos - (d - pos))
+}
+
+// Dense bias of one lane for one tile: its query row, keys jg .. jg+15 (raw fp16 or fp32 words).
+template <int BIAS>
+struct BiasRegs {
+    static constexpr int NV = BIAS == BK_DENSE_F32 ? 4 : (BIAS == BK_DENSE_F16 ? 2 : 1);
+    v4i w[NV];
+};
+
+// rows: buffer over this wave's 16 query rows starting at key column j0 (rows past N read 0).
+template <int BIAS>
+__device__ __forceinline__ void load_bias(BiasRegs<BIAS>& b, __amdgpu_buffer_rsrc_t rows, int voff) {
+    if (BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32) {
+#pragma unroll
+        for (int k = 0; k < BiasRegs<BIAS>::NV; ++k)
+            b.w[k] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rows, voff + 16 * k, 0, 0));
+    }
+}
+
+template <int BIAS>
+__device__ __forceinline__ float bias_at(const BiasRegs<BIAS>& b, int k) {
+    if (BIAS == BK_DENSE_F16) {
+        const uint32_t word = (uint32_t)b.w[k >> 3][(k >> 1) & 3];
+        const uint16_t bits16 = (k & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
+        return (float)__builtin_bit_cast(_Float16, bits16);
+    } else {
+        return __int_as_float(b.w[k >> 2][k & 3]);
+    }
+}
+
+// The lane's query: Q operand, accumulator seed and scale.
+struct LaneQ {
+    v8i qop;
+    v4f dseed;  // -sum of the query's signs
+    float cq;   // mu_q / sqrt(d); 0 for a query past N
+    int qi;     // query index (clamped to N-1)
+    bool live;  // query < N
+};
+
+// Workgroup coordinates: (b*H + h, first query), with the XCD-aware block order.
+template <int BIAS>
+__device__ __forceinline__ void block_coords(const FwdArgs& a, int& bh, int& q0) {
+    const int N = a.N;
+    const int nqb = (N + kBR - 1) / kBR;
+    const int nblk = a.B * a.H * nqb;
+    const int lb = xcd_logical_block(blockIdx.x, nblk);
+    int qb;
+    if (BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32) {
+        // the dense bias is shared over the batch: keep the batch items of one (h, query block) together
+        const int b = lb % a.B, hq = lb / a.B;
+        qb = hq % nqb;
+        bh = b * a.H + hq / nqb;
+    } else {
+        bh = lb / nqb;
+        qb = lb % nqb;
+    }
+    q0 = qb * kBR;
+}
+
+template <int NT>
+__device__ __forceinline__ LaneQ lane_query(const FwdArgs& a, int bh, int qw0, int g, int n16) {
+    constexpr int W = (NT + 1) / 2;
+    LaneQ lq;
+    const int N = a.N;
+    const int i = qw0 + n16;
+    lq.live = i < N;
+    lq.qi = lq.live ? i : N - 1;
+    const float seed = load_q<W>(a.qbits + ((int64_t)bh * N + lq.qi) * W, lq.live, a.d, g, lq.qop);
+    lq.dseed = v4f{seed, seed, seed, seed};
+    lq.cq = lq.live ? a.qmu[(int64_t)bh * N + i] * a.qk_scale : 0.0f;
+    return lq;
+}
+
+// Scores of one tile for one lane: S[k] for keys jg + k, k = 0..15, in natural units, keys >= N
+// (k >= nvalid on the tail tile) set to -inf, and the running lane max mloc over them.
+// sk/smu: the staged tile; zk: 16 rows x 32 zero bytes, the K operand of lanes whose channel
+// group is past d.  win/idx0: relative-position window and the lane's index of key jg in it
+// (the run's bias is win[idx0 - k]).
+template <int NT, int BIAS>
+__device__ __forceinline__ void tile_scores(const uint32_t* __restrict__ sk, const float* __restrict__ smu,
+                                            const uint32_t* zk, const LaneQ& lq, const BiasRegs<BIAS>& bias,
+                                            const float* win, int idx0, bool tail, int nvalid, float (&S)[16],
+                                            float& mloc) {
+    constexpr int W = (NT + 1) / 2;
+    const int lane = threadIdx.x & 63, g = lane >> 4, m16 = lane & 15;
+    v4f D[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t* src = g < W ? &sk[((t * W + g) * 16 + m16) * 8] : zk + m16 * 8;
+        const v4i lo = *reinterpret_cast<const v4i*>(src);
+        const v4i hi = *reinterpret_cast<const v4i*>(src + 4);
+        const v8i kop = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        D[t] = mfma_f8(kop, lq.qop, lq.dseed);
+    }
+    float muk[16];
+#pragma unroll
+    for (int k = 0; k < 16; k += 4) {
+        const float4 m4 = *reinterpret_cast<const float4*>(&smu[16 * g + k]);
+        muk[k] = m4.x; muk[k + 1] = m4.y; muk[k + 2] = m4.z; muk[k + 3] = m4.w;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        float b = 0.0f;
+        if (BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32) b = bias_at<BIAS>(bias, k);
+        if (BIAS == BK_RELPOS) b = win[idx0 - k];
+        S[k] = __builtin_fmaf(D[k >> 2][k & 3] * muk[k], lq.cq, b);
+    }
+    // The max is taken separately on the two paths: on the common one every S is an fma
+    // result and needs no NaN canonicalisation before v_max3.
+    if (tail) {  // ragged end: keys >= N take no weight
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            if (k >= nvalid) S[k] = -INFINITY;
+#pragma unroll
+        for (int k = 15; k > 0; k -= 2) mloc = fmaxf(fmaxf(mloc, S[k]), S[k - 1]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; k += 2) mloc = fmaxf(fmaxf(mloc, S[k]), S[k + 1]);
+    }
+}
+
+// Quantised probabilities of one tile as the B operand of the PV MFMA (bytes P^ - 128) and
+// their unquantised sum: p = 255 exp(S - m) with negm = log2(255) - m log2(e).
+__device__ __forceinline__ v4i tile_probs(const float (&S)[16], float negm, float& lsum) {
+    v4i pw;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float p = fast_exp2(__builtin_fmaf(S[4 * t + r], kLog2e, negm));
+            lsum += p;
+            word = __builtin_amdgcn_cvt_pk_u8_f32(p, r, word);
+        }
+        pw[t] = (int)(word ^ 0x80808080u);
+    }
+    return pw;
+}
+
+constexpr v4i kC64 = v4i{0x40404040, 0x40404040, 0x40404040, 0x40404040};
+
+// Dequantise, normalise and store the lane's 4*NT channels of its query.
+template <int NT>
+__device__ __forceinline__ void store_out(const FwdArgs& a, int bh, const LaneQ& lq, const float* sScale,
+                                          const float (&acc)[NT][4], float L) {
+    if (!lq.live) return;
+    const int lane = threadIdx.x & 63, g = lane >> 4;
+    const int d = a.d, c0 = 4 * NT * g;
+    const float inv = fast_rcp(L);
+    const int64_t row = ((int64_t)bh * a.N + lq.qi) * d;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+        const int c = c0 + 4 * ct;
+        if (c >= d) continue;
+        const float4 s4 = *reinterpret_cast<const float4*>(&sScale[c]);
+        const float o0 = acc[ct][0] * s4.x * inv, o1 = acc[ct][1] * s4.y * inv;
+        const float o2 = acc[ct][2] * s4.z * inv, o3 = acc[ct][3] * s4.w * inv;
+        if (a.out_f32) {
+            *reinterpret_cast<float4*>((float*)a.out + row + c) = make_float4(o0, o1, o2, o3);
+        } else {
+            typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+            const h4 hv = h4{(_Float16)o0, (_Float16)o1, (_Float16)o2, (_Float16)o3};
+            *reinterpret_cast<h4*>((_Float16*)a.out + row + c) = hv;
+        }
+    }
+}
+
+// Per-workgroup set-up shared by both kernels: the K zero block and the dequantisation
+// scales s_c = a_c / 127 (IEEE division, as the oracle), 0 for channel slots past d.
+__device__ __forceinline__ void stage_common(const FwdArgs& a, int bh, uint32_t* zk, float* sScale) {
+    const int tid = threadIdx.x;
+    if (tid < 16 * 8) zk[tid] = 0u;
+    if (tid < 128) sScale[tid] = tid < a.d ? a.vamax[(int64_t)bh * a.d + tid] / 127.0f : 0.0f;
+}
+
+// Whole-attention staging of one (b, h) from fp16 Q, K, V, done by the short-row kernel itself:
+// K -> sign bits as fp8 operand rows and mu_k (one key per thread); V -> channel absmax,
+// dequantisation scales and int8 V^ written straight into the operand rows (V held in
+// registers in groups of 4 tokens, transposed with v_perm); the Q of the workgroup's query
+// blocks -> sign word g and mu_q per lane (sQw, sQmu).  The arithmetic is that of
+// pack_block and quant_head_regs -- the same comparisons, the same fp32 summation order for
+// mu, the same IEEE 127/a and rint -- so the results equal the separate path bit for bit.
+// sRed: 2048 floats; sInv: 128 floats.
+template <int NT, int NTL>
+__device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo, int nitems, TileLds<NT, 4>* lds,
+                                            float* sScale, uint32_t* zk, uint32_t* sQw, float* sQmu, float* sRed,
+                                            float* sInv) {
+    constexpr int W = (NT + 1) / 2;
+    constexpr int MAXCK = 2 * NT;  // 8-channel chunks of one key (d <= 16 NT)
+    constexpr int MAXC = 16;       // V chunks per thread: 4 * ceil(64 / G) with G = 256 / (d/8) >= 16
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    const int N = a.N, d = a.d, tid = threadIdx.x;
+    const int cpt = d >> 3;
+    // operand padding (keys >= N, channel slots >= d) stays zero
+    for (int id = tid; id < NTL * NT * 64; id += 256)
+        reinterpret_cast<uint4*>(lds[id / (NT * 64)].v)[id % (NT * 64)] = make_uint4(0, 0, 0, 0);
+    if (tid < 16 * 8) zk[tid] = 0u;
+
+    // ---- all K and V loads of the head in flight together
+    const _Float16* kh = a.k_raw + (int64_t)bh * N * d;
+    const _Float16* vh = a.v_raw + (int64_t)bh * N * d;
+    const int j = tid;  // this thread's key
+    h8 kx[MAXCK];
+#pragma unroll
+    for (int c = 0; c < MAXCK; ++c) {
+        if (c < cpt && j < N) {
+            kx[c] = *reinterpret_cast<const h8*>(kh + (int64_t)j * d + 8 * c);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kx[c][e] = (_Float16)0;
+        }
+    }
+    const int P = cpt, G = 256 / P;
+    const int part = tid % P, grp = tid / P;
+    h8 vx[MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int n = 4 * (grp + G * (i >> 2)) + (i & 3);
+        if (grp < G && n < N) {
+            vx[i] = *reinterpret_cast<const h8*>(vh + (int64_t)n * d + part * 8);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vx[i][e] = (_Float16)0;
+        }
+    }
+    __syncthreads();  // the zero fill is complete before any operand row is written
+
+    // ---- K: sign bytes and partial |x| sums per chunk, words, mu_k (pack_block's order)
+    if (j < NTL * kBC) {
+        uint32_t words[W];
+#pragma unroll
+        for (int w = 0; w < W; ++w) words[w] = 0u;
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < MAXCK; ++c) {
+            if (c < cpt) {
+                uint32_t byte = 0;
+                float sum = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float f = (float)kx[c][e];
+                    byte |= (f >= 0.0f ? 1u : 0u) << e;  // -0.0 >= 0 holds: zero counts as +1
+                    sum += fabsf(f);
+                }
+                acc += sum;
+                words[c >> 2] |= byte << (8 * (c & 3));
+            }
+        }
+        const bool live = j < N;
+        int t;
+        const int jj = j & (kBC - 1), m = key_slot(jj, t);
+        TileLds<NT, 4>& s = lds[j / kBC];
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            uint32_t o[8];
+            unpack_bits32_f8(live ? words[w] : 0u, o);
+            uint32_t* dst = &s.k[((t * W + w) * 16 + m) * 8];
+            *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<uint4*>(dst + 4) = make_uint4(o[4], o[5], o[6], o[7]);
+        }
+        s.mu[jj] = live ? acc / (float)d : 0.0f;
+    }
+
+    // ---- V: channel absmax (input precision), scales, quantise, transpose, scatter
+    h8 mv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mv[e] = (_Float16)0;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) mv = __builtin_elementwise_max(mv, __builtin_elementwise_abs(vx[i]));
+    if (grp < G) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sRed[grp * d + part * 8 + e] = (float)mv[e];
+    }
+    __syncthreads();
+    if (tid < 128) {
+        float av = 0.0f;
+        if (tid < d)
+            for (int gi = 0; gi < G; ++gi) av = fmaxf(av, sRed[gi * d + tid]);
+        sScale[tid] = tid < d ? av / 127.0f : 0.0f;  // dequantisation scale, as fp32 a/127
+        sInv[tid] = av > 0.0f ? 127.0f / av : 0.0f;
+    }
+    __syncthreads();
+    if (grp < G) {
+        float inv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) inv[e] = sInv[part * 8 + e];
+#pragma unroll
+        for (int u = 0; u < MAXC / 4; ++u) {
+            const int n0 = 4 * (grp + G * u);
+            if (n0 < N) {
+                uint32_t qb[4][2];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int w = 0; w < 2; ++w) {
+                        uint32_t word = 0;
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            float q = __builtin_rintf((float)vx[4 * u + r][4 * w + b] * inv[4 * w + b]);
+                            q = fminf(fmaxf(q, -127.0f), 127.0f);
+                            word = __builtin_amdgcn_cvt_pk_u8_f32(q + 128.0f, b, word);  // exact: q is an integer
+                        }
+                        qb[r][w] = word ^ 0x80808080u;
+                    }
+                const int t = n0 >> 6, jj = n0 & (kBC - 1), gg = jj >> 4, ii = jj & 15;
+                char* vbase = reinterpret_cast<char*>(lds[t].v);
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    const uint32_t in[4] = {qb[0][w], qb[1][w], qb[2][w], qb[3][w]};
+                    uint32_t out[4];
+                    transpose4x4(in, out);
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) {
+                        int ct;
+                        const int m = chan_slot<NT>(part * 8 + 4 * w + cc, ct);
+                        *reinterpret_cast<uint32_t*>(vbase + ((ct * kWave + m + 16 * gg) * 16 + ii)) = out[cc];
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- Q of every query block of this workgroup: word g of the signs and mu_q per lane
+    const int lane = tid & 63, g = lane >> 4, n16 = lane & 15, wave = tid >> 6;
+    const _Float16* qh = a.q_raw + (int64_t)bh * N * d;
+    for (int it = 0; it < nitems; ++it) {
+        const int i = (qb_lo + it) * kBR + wave * 16 + n16;
+        const bool live = i < N;
+        h8 qx[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (live && 4 * g + c < cpt) {
+                qx[c] = *reinterpret_cast<const h8*>(qh + (int64_t)i * d + 32 * g + 8 * c);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qx[c][e] = (_Float16)0;
+            }
+        }
+        uint32_t word = 0;
+        float psum[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint32_t byte = 0;
+            float sum = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float f = (float)qx[c][e];
+                byte |= (f >= 0.0f ? 1u : 0u) << e;
+                sum += fabsf(f);
+            }
+            psum[c] = sum;
+            if (4 * g + c < cpt) word |= byte << (8 * c);
+        }
+        // mu = (sum over the query's chunks in channel order) / d: lanes g = 0, 1, .. add theirs in turn
+        float acc = 0.0f;
+#pragma unroll
+        for (int gg = 0; gg < W; ++gg) {
+            if (g == gg) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (4 * g + c < cpt) acc += psum[c];
+            }
+            acc = __shfl(acc, 16 * gg + n16);
+        }
+        sQw[(it * kWaves + wave) * kWave + lane] = (live && g < W) ? word : 0u;
+        if (g == 0) sQmu[(it * kWaves + wave) * 16 + n16] = live ? acc / (float)d : 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Rows of NTL <= kKeepTiles tiles (N <= 256): exact row max in two passes over register-resident
+// scores.  A workgroup stages the K bits, mu_k and V^ of one (b, h) once and then loops over the
+// query blocks [qb_lo, qb_hi) of that head (nsplit workgroups per head).  The next block's query
+// words, dense-bias rows and relative-position window are loaded while the current block is
+// computed, into registers the current block no longer needs.
+template <int NT, int BIAS, int NTL, bool FUSED>
+__global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int nsplit) {
+    constexpr int W = (NT + 1) / 2;
+    constexpr bool DENSE = BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32;
+    typedef TileRegs<NT, 4> Regs;
+    typedef TileLds<NT, 4> Lds;
+    __shared__ Lds lds[NTL];
+    __shared__ __attribute__((aligned(16))) float sWin[BIAS == BK_RELPOS ? kRelposWin : 4];
+    __shared__ __attribute__((aligned(16))) float sScale[128];
+    __shared__ __attribute__((aligned(16))) uint32_t zk[16 * 8];
+    // whole-attention path only: the prepared Q of every query block, and staging scratch
+    __shared__ __attribute__((aligned(16))) uint32_t sQw[FUSED ? kKeepTiles * kWaves * kWave : 1];
+    __shared__ __attribute__((aligned(16))) float sQmu[FUSED ? kKeepTiles * kWaves * 16 : 1];
+    __shared__ __attribute__((aligned(16))) float sRed[FUSED ? 2048 : 1];
+    __shared__ __attribute__((aligned(16))) float sInv[FUSED ? 128 : 1];
+
+    const int N = a.N, d = a.d;
+    const int nqb = (N + kBR - 1) / kBR;
+    const int lb = xcd_logical_block(blockIdx.x, a.B * a.H * nsplit);
+    const int bh = lb / nsplit, split = lb % nsplit;
+    const int qb_lo = split * nqb / nsplit, qb_hi = (split + 1) * nqb / nsplit;
+    const int h = bh % a.H;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: keeps row pointers scalar
+
+    HeadPtrs hp;
+    hp.kb = a.kbits + (int64_t)bh * N * W;
+    hp.kmu = a.kmu + (int64_t)bh * N;
+    hp.vq = a.vq + (int64_t)bh * d * a.ldv;
+    hp.table = nullptr;
+    if (BIAS == BK_RELPOS) {
+        const int64_t tsz = (int64_t)(2 * a.gh - 1) * (2 * a.gw - 1);
+        hp.table = a.bias_f32 ? (const void*)((const float*)a.bias + h * tsz)
+                              : (const void*)((const _Float16*)a.bias + h * tsz);
+    }
+    const int esz = BIAS == BK_DENSE_F32 ? 4 : 2;
+    const int bvoff = (n16 * (int)a.bias_ld + 16 * g) * esz;
+
+    // Per-block inputs of this lane: word g of its query's signs (0 past d or N) and mu_q.
+    auto load_query = [&](int qb, uint32_t& qword, float& qmu) {
+        if constexpr (FUSED) {
+            const int it = qb - qb_lo;
+            qword = sQw[(it * kWaves + wave) * kWave + lane];
+            qmu = sQmu[(it * kWaves + wave) * 16 + n16];
+        } else {
+            const int i = qb * kBR + wave * 16 + n16;
+            const bool live = i < N;
+            qword = (live && g < W) ? a.qbits[((int64_t)bh * N + i) * W + g] : 0u;
+            qmu = live ? a.qmu[(int64_t)bh * N + i] : 0.0f;
+        }
+    };
+    // Dense bias rows of this wave's 16 queries of block qb, key tile t (rows >= N read 0).
+    auto load_bias_tile = [&](int qb, int t, BiasRegs<BIAS>& bias_t) {
+        const int r0 = min(qb * kBR + wave * 16, N);
+        const char* brow = (const char*)a.bias + ((int64_t)h * N + r0) * a.bias_ld * esz;
+        const int brow_bytes = min(N - r0, 16) * (int)a.bias_ld * esz;  // at most 16 rows: far below 2^31
+        const int j0 = t * kBC;
+        load_bias<BIAS>(bias_t, buffer_rsrc(brow + j0 * esz, brow_bytes - j0 * esz), bvoff);
+    };
+    // First table row of the relative-position window of block qb (every key touched).
+    auto window_lo = [&](int qb) { return relpos_window(qb * kBR, 0, N, N, a.gh, a.gw).dr_lo; };
+
+    // ---- stage the head once (all loads in flight together), then the first block's inputs
+    if constexpr (FUSED) {
+        fused_stage<NT, NTL>(a, bh, qb_lo, qb_hi - qb_lo, lds, sScale, zk, sQw, sQmu, sRed, sInv);
+        __syncthreads();  // the prepared query words are read by load_query below
+    } else {
+        Regs regs[NTL];
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) load_tile<NT, 4>(regs[t], a, hp, 0, t * kBC);
+        stage_common(a, bh, zk, sScale);
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) store_tile<NT, 4>(regs[t], lds[t], d);
+    }
+    float wv[kRelposWin / 256];
+    if (BIAS == BK_RELPOS) {
+        load_window<kRelposWin / 256>(wv, a, hp.table, window_lo(qb_lo) * (2 * a.gw - 1));
+#pragma unroll
+        for (int i = 0; i < kRelposWin / 256; ++i) sWin[tid + 256 * i] = wv[i];
+    }
+    uint32_t qword;
+    float qmu;
+    load_query(qb_lo, qword, qmu);
+    BiasRegs<BIAS> bias[NTL];
+    if (DENSE) {
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) load_bias_tile(qb_lo, t, bias[t]);
+    }
+    __syncthreads();
+
+    for (int qb = qb_lo; qb < qb_hi; ++qb) {
+        const int q0 = qb * kBR, qw0 = q0 + wave * 16;
+        const bool live = qw0 < N;  // some query of this wave is < N (wave-uniform)
+        const bool more = qb + 1 < qb_hi;
+        if (BIAS == BK_RELPOS && more) load_window<kRelposWin / 256>(wv, a, hp.table, window_lo(qb + 1) * (2 * a.gw - 1));
+
+        // the lane's query: Q operand (fp8 2*sign of channels 32g..32g+31, 0 past d) and seed
+        LaneQ lq;
+        {
+            const int i = qw0 + n16;
+            lq.live = i < N;
+            lq.qi = lq.live ? i : N - 1;
+            uint32_t o[8];
+            unpack_signs32_f8x2(qword, o);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) lq.qop[c] = (lq.live && g < W && 32 * g + 4 * c < d) ? (int)o[c] : 0;
+            const float pos = rows4_sum((float)__builtin_popcount(qword));  // sign bits set over the query
+            const float seed = lq.live ? (float)d - 2.0f * pos : 0.0f;
+            lq.dseed = v4f{seed, seed, seed, seed};
+            lq.cq = qmu * a.qk_scale;
+        }
+        int ri = 0, ci = 0, win_lo = 0;
+        if (BIAS == BK_RELPOS) {
+            ri = lq.qi / a.gw;
+            ci = lq.qi % a.gw;
+            win_lo = window_lo(qb);
+        }
+
+        // ---- pass 1: scores, row max, and the V^ column-sum term (128 * sum V^ per channel)
+        float S[NTL][16];
+        float mloc = -INFINITY;
+        v4i acc[NT];
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) acc[ct] = v4i{0, 0, 0, 0};
+        if (live) {
+#pragma unroll
+            for (int t = 0; t < NTL; ++t) {
+                const int jg = t * kBC + 16 * g;
+                int idx0 = 0;
+                if (BIAS == BK_RELPOS) {
+                    const int rj = jg / a.gw, cj = jg % a.gw;
+                    idx0 = (ri - rj + a.gh - 1 - win_lo) * (2 * a.gw - 1) + (ci - cj + a.gw - 1);
+                    if (jg >= N) idx0 = 15;  // the whole run is past N and masked; keep reads in the window
+                }
+                tile_scores<NT, BIAS>(lds[t].k, lds[t].mu, zk, lq, bias[t], sWin, idx0, t == NTL - 1, N - jg,
+                                      S[t], mloc);
+#pragma unroll
+                for (int ct = 0; ct < NT; ++ct) {
+                    const v4i vop = *reinterpret_cast<const v4i*>(&lds[t].v[(ct * kWave + lane) * 4]);
+                    acc[ct] = mfma_i8(vop, kC64, acc[ct]);
+                    acc[ct] = mfma_i8(vop, kC64, acc[ct]);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // one tile's operands live at a time
+            }
+        }
+        // the next block's query words and bias rows, into registers pass 1 has released
+        if (more) {
+            load_query(qb + 1, qword, qmu);
+            if (DENSE) {
+#pragma unroll
+                for (int t = 0; t < NTL; ++t) load_bias_tile(qb + 1, t, bias[t]);
+            }
+        }
+        if (BIAS == BK_RELPOS) {
+            __syncthreads();  // every wave is done with this block's window
+            if (more) {
+#pragma unroll
+                for (int i = 0; i < kRelposWin / 256; ++i) sWin[tid + 256 * i] = wv[i];
+            }
+        }
+
+        // ---- pass 2: P^ = rint(255 exp(S - m)), row sums, integer PV (no rescaling)
+        if (live) {
+            const float m = rows4_max(mloc);
+            const float negm = kLog2_255 - m * kLog2e;
+            float lsum = 0.0f;
+#pragma unroll
+            for (int t = 0; t < NTL; ++t) {
+                const v4i pw = tile_probs(S[t], negm, lsum);
+#pragma unroll
+                for (int ct = 0; ct < NT; ++ct) {
+                    const v4i vop = *reinterpret_cast<const v4i*>(&lds[t].v[(ct * kWave + lane) * 4]);
+                    acc[ct] = mfma_i8(vop, pw, acc[ct]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            float accf[NT][4];
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) accf[ct][r] = (float)acc[ct][r];
+            store_out<NT>(a, bh, lq, sScale, accf, rows4_sum(lsum));
+        }
+        if (BIAS == BK_RELPOS) __syncthreads();  // the next block's window is in place
+    }
+}
+
+// Whether the relative-position window of a whole short row (queries of one block, every key)
+// fits the staged window; false sends the launch to the streaming kernel.
+inline bool keep_window_fits(const FwdArgs& a) {
+    const int N = a.N, gw = a.gw, gh = a.gh;
+    for (int q0 = 0; q0 < N; q0 += kBR) {
+        const int ri_min = q0 / gw, ri_max = (min(q0 + kBR, N) - 1) / gw;
+        if ((ri_max - ri_min + gh) * (2 * gw - 1) > kRelposWin) return false;
+    }
+    return true;
+}
+
+// Compute units of the current device (cached per device; 256 on MI355X).
+inline int device_cus() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+}  // namespace binattn

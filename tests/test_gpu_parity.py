@@ -194,6 +194,27 @@ def test_attention_equals_pipeline(name):
     assert_o(o.cpu().numpy().reshape(-1, w.d)[rows], ref, float(np.abs(inp["v"].astype(np.float64)).max()), name)
 
 
+@pytest.mark.parametrize("B,H,N,d,bias,grid", [(1, 1, 1, 64, "dense", ()), (2, 3, 17, 64, "none", ()),
+                                                (1, 2, 65, 72, "dense", ()), (2, 2, 130, 128, "none", ()),
+                                                (2, 3, 197, 64, "dense", ()), (1, 4, 256, 72, "relpos", (16, 16)),
+                                                (1, 2, 192, 64, "relpos", (12, 16)), (3, 1, 256, 128, "relpos", (8, 32))])
+def test_attention_short_rows_one_kernel(B, H, N, d, bias, grid):
+    """Short rows from fp16 inputs run as one kernel that stages K, V and Q itself; its output
+    equals the four-call pipeline bit for bit (same comparisons, summation orders, divisions)."""
+    _say(f"attention one kernel {B}x{H}x{N}x{d} {bias}")
+    inp = W.custom(B, H, N, d, "f16", bias, grid, seed=N + 3 * d)
+    b = _b()
+    g = gpu_pipeline(inp)
+    bt, kind = None, b.BIAS_NONE
+    if bias == "dense":
+        bt, kind = b.aligned_dense_bias(_t(inp["bias"])), b.BIAS_DENSE
+    elif bias == "relpos":
+        bt, kind = _t(inp["bias"]), b.BIAS_RELPOS
+    o = b.attention(_t(inp["q"]), _t(inp["k"]), _t(inp["v"]), bt, kind, grid or None)
+    torch.cuda.synchronize()
+    assert torch.equal(o, g["o"])
+
+
 # ---------------------------------------------------------------- forward, small and ragged
 
 SMALL = [
