@@ -11,9 +11,10 @@ template <int NT, int BK>
 static hipError_t launch_fused_bk(const FwdArgs& a, hipStream_t s) {
     const int ntiles = (a.N + kBC - 1) / kBC;
     const int nqb = (a.N + kBR - 1) / kBR;
-    const int64_t heads = (int64_t)a.B * a.H;
-    const int64_t want = 3 * (int64_t)device_cus();
-    const int nsplit = (int)std::min<int64_t>(nqb, std::max<int64_t>(1, (want + heads - 1) / heads));
+    // one workgroup per head (each stages its head once) unless there are too few heads to
+    // give every compute unit one
+    const int64_t heads = (int64_t)a.B * a.H, cus = device_cus();
+    const int nsplit = (int)std::min<int64_t>(nqb, std::max<int64_t>(1, (cus + heads - 1) / heads));
     const dim3 grid((unsigned)(heads * nsplit));
     switch (ntiles) {
         case 1: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 1, true>), grid, dim3(256), 0, s, a, nsplit); break;

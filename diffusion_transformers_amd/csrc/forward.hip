@@ -126,7 +126,8 @@ __global__ __launch_bounds__(256) void binattn_fwd_stream_kernel(FwdArgs a) {
             if (jg >= N) idx0 = 15;
         }
         float S[16], mloc = -INFINITY;
-        tile_scores<NT, BIAS>(s.k, s.mu, zk, lq, bcur, s.tw, idx0, tile == ntiles - 1, N - jg, S, mloc);
+        tile_scores<NT, BIAS>(s.k, s.mu, zk, lq, bcur, s.tw, idx0, tile == ntiles - 1 && (N & (kBC - 1)) != 0, N - jg,
+                              S, mloc);
         const float mnew = fmaxf(mrun, rows4_max(mloc));
         if (__any(mnew > mrun)) {
             const float alpha = fast_exp2((mrun - mnew) * kLog2e);  // 0 on the first tile

@@ -12,6 +12,38 @@
 
 namespace binattn {
 
+// One 8-channel fp16 chunk: the sign byte (bit e = x_e >= 0, so -0.0 counts as +1) and the
+// fp32 sum of |x_e| (a fixed chain of v_dot2_f32_f16 against 1.0, so every caller gets the same
+// rounding).  Packed: +0.0 is added to both halves (turning -0.0 into +0.0), the four sign-carrying
+// high bytes of each half are gathered with v_perm and compressed with one multiply.
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t sign_nibble(uint32_t hw0, uint32_t hw1) {
+    // bytes 1 and 3 of each word hold the signs of its two halves (bit 7 of each byte)
+    const uint32_t z = __builtin_amdgcn_perm(hw1, hw0, 0x07050301u);
+    const uint32_t pos = (~z >> 7) & 0x01010101u;  // 1 where the sign bit is clear
+    return (pos * 0x01020408u) >> 24;              // byte k -> bit 24 + k
+}
+
+__device__ __forceinline__ void chunk_sign_abs(const h8& x, uint32_t& byte, float& sum) {
+    uint32_t w[4];
+    const h2 zero = h2{(_Float16)0, (_Float16)0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const h2 pair = h2{x[2 * i], x[2 * i + 1]} + zero;  // -0.0 + 0.0 = +0.0
+        w[i] = __builtin_bit_cast(uint32_t, pair);
+    }
+    byte = sign_nibble(w[0], w[1]) | (sign_nibble(w[2], w[3]) << 4);
+    const h2 one = h2{(_Float16)1, (_Float16)1};
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const h2 a = __builtin_bit_cast(h2, __builtin_bit_cast(uint32_t, h2{x[2 * i], x[2 * i + 1]}) & 0x7FFF7FFFu);
+        acc = __builtin_amdgcn_fdot2(a, one, acc, false);
+    }
+    sum = acc;
+}
+
 // Sign words and mu of the tokens of workgroup `blk`: kPackSub contiguous spans of
 // floor(256 / (d/8)) tokens, one 8-channel chunk (16 or 32 bytes) per thread and span.  All of
 // a thread's chunk loads are issued first (enough bytes in flight per compute unit to stream
@@ -51,11 +83,15 @@ __device__ __forceinline__ void pack_block(const T* __restrict__ x, int64_t ntok
         const int64_t t0 = (blk * kPackSub + u) * ntw;
         uint32_t byte = 0;
         float sum = 0.0f;
+        if constexpr (sizeof(T) == 2) {
+            chunk_sign_abs(v[u], byte, sum);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float f = (float)v[u][e];
-            byte |= (f >= 0.0f ? 1u : 0u) << e;  // -0.0 >= 0 holds: zero counts as +1
-            sum += fabsf(f);
+            for (int e = 0; e < 8; ++e) {
+                const float f = (float)v[u][e];
+                byte |= (f >= 0.0f ? 1u : 0u) << e;  // -0.0 >= 0 holds: zero counts as +1
+                sum += fabsf(f);
+            }
         }
         // bytes past the token's d channels read as zero
         reinterpret_cast<uint4*>(sBits)[tid] = make_uint4(0, 0, 0, 0);
@@ -178,8 +214,8 @@ __device__ __forceinline__ void quant_head_regs(const T* __restrict__ v, int N, 
                 uint32_t word = 0;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    float q = __builtin_rintf((float)x[4 * u + r][4 * w + b] * inv[4 * w + b]);
-                    q = fminf(fmaxf(q, -127.0f), 127.0f);
+                    // |x| <= a gives |x * fl32(127/a)| < 127.0001, so rint is already within +-127
+                    const float q = __builtin_rintf((float)x[4 * u + r][4 * w + b] * inv[4 * w + b]);
                     word = __builtin_amdgcn_cvt_pk_u8_f32(q + 128.0f, b, word);  // exact: q is an integer
                 }
                 qb[r][w] = word ^ 0x80808080u;  // back to two's-complement int8

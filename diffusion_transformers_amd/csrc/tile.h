@@ -379,7 +379,6 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
     constexpr int W = (NT + 1) / 2;
     constexpr int MAXCK = 2 * NT;  // 8-channel chunks of one key (d <= 16 NT)
     constexpr int MAXC = 16;       // V chunks per thread: 4 * ceil(64 / G) with G = 256 / (d/8) >= 16
-    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
     const int N = a.N, d = a.d, tid = threadIdx.x;
     const int cpt = d >> 3;
     // operand padding (keys >= N, channel slots >= d) stays zero
@@ -387,32 +386,36 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
         reinterpret_cast<uint4*>(lds[id / (NT * 64)].v)[id % (NT * 64)] = make_uint4(0, 0, 0, 0);
     if (tid < 16 * 8) zk[tid] = 0u;
 
-    // ---- all K and V loads of the head in flight together
-    const _Float16* kh = a.k_raw + (int64_t)bh * N * d;
-    const _Float16* vh = a.v_raw + (int64_t)bh * N * d;
+    // ---- all K, V and Q loads of the head in flight together.  Buffer loads: rows past N read
+    // as zero and no load sits under a lane-dependent branch (so no load is waited for early).
+    const int hbytes = N * d * 2;  // at most 256 * 128 * 2
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(a.k_raw + (int64_t)bh * N * d, hbytes);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(a.v_raw + (int64_t)bh * N * d, hbytes);
+    const __amdgpu_buffer_rsrc_t qr = buffer_rsrc(a.q_raw + (int64_t)bh * N * d, hbytes);
+    auto load16 = [](__amdgpu_buffer_rsrc_t r, int off) {
+        return __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    };
     const int j = tid;  // this thread's key
     h8 kx[MAXCK];
 #pragma unroll
-    for (int c = 0; c < MAXCK; ++c) {
-        if (c < cpt && j < N) {
-            kx[c] = *reinterpret_cast<const h8*>(kh + (int64_t)j * d + 8 * c);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kx[c][e] = (_Float16)0;
-        }
-    }
+    for (int c = 0; c < MAXCK; ++c)
+        if (c < cpt) kx[c] = load16(kr, j * d * 2 + 16 * c);  // uniform condition
     const int P = cpt, G = 256 / P;
     const int part = tid % P, grp = tid / P;
     h8 vx[MAXC];
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
         const int n = 4 * (grp + G * (i >> 2)) + (i & 3);
-        if (grp < G && n < N) {
-            vx[i] = *reinterpret_cast<const h8*>(vh + (int64_t)n * d + part * 8);
-        } else {
+        vx[i] = load16(vr, grp < G ? n * d * 2 + part * 16 : hbytes);  // past N (or idle thread): 0
+    }
+    const int lane = tid & 63, g = lane >> 4, n16 = lane & 15, wave = tid >> 6;
+    h8 qx[kKeepTiles][4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vx[i][e] = (_Float16)0;
-        }
+    for (int it = 0; it < kKeepTiles; ++it) {
+        const int i = (qb_lo + it) * kBR + wave * 16 + n16;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)  // chunks past d belong to the next query: masked where used
+            if (it < nitems) qx[it][c] = load16(qr, min(i, N) * d * 2 + 64 * g + 16 * c);
     }
     __syncthreads();  // the zero fill is complete before any operand row is written
 
@@ -425,14 +428,9 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
 #pragma unroll
         for (int c = 0; c < MAXCK; ++c) {
             if (c < cpt) {
-                uint32_t byte = 0;
-                float sum = 0.0f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float f = (float)kx[c][e];
-                    byte |= (f >= 0.0f ? 1u : 0u) << e;  // -0.0 >= 0 holds: zero counts as +1
-                    sum += fabsf(f);
-                }
+                uint32_t byte;
+                float sum;
+                chunk_sign_abs(kx[c], byte, sum);
                 acc += sum;
                 words[c >> 2] |= byte << (8 * (c & 3));
             }
@@ -487,8 +485,8 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
                         uint32_t word = 0;
 #pragma unroll
                         for (int b = 0; b < 4; ++b) {
-                            float q = __builtin_rintf((float)vx[4 * u + r][4 * w + b] * inv[4 * w + b]);
-                            q = fminf(fmaxf(q, -127.0f), 127.0f);
+                            // |v| <= a keeps rint(v * fl32(127/a)) within +-127 (no clamp needed)
+                            const float q = __builtin_rintf((float)vx[4 * u + r][4 * w + b] * inv[4 * w + b]);
                             word = __builtin_amdgcn_cvt_pk_u8_f32(q + 128.0f, b, word);  // exact: q is an integer
                         }
                         qb[r][w] = word ^ 0x80808080u;
@@ -512,33 +510,18 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
     }
 
     // ---- Q of every query block of this workgroup: word g of the signs and mu_q per lane
-    const int lane = tid & 63, g = lane >> 4, n16 = lane & 15, wave = tid >> 6;
-    const _Float16* qh = a.q_raw + (int64_t)bh * N * d;
-    for (int it = 0; it < nitems; ++it) {
+#pragma unroll
+    for (int it = 0; it < kKeepTiles; ++it) {
+        if (it >= nitems) break;
         const int i = (qb_lo + it) * kBR + wave * 16 + n16;
         const bool live = i < N;
-        h8 qx[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            if (live && 4 * g + c < cpt) {
-                qx[c] = *reinterpret_cast<const h8*>(qh + (int64_t)i * d + 32 * g + 8 * c);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qx[c][e] = (_Float16)0;
-            }
-        }
         uint32_t word = 0;
         float psum[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            uint32_t byte = 0;
-            float sum = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float f = (float)qx[c][e];
-                byte |= (f >= 0.0f ? 1u : 0u) << e;
-                sum += fabsf(f);
-            }
+            uint32_t byte;
+            float sum;
+            chunk_sign_abs(qx[it][c], byte, sum);
             psum[c] = sum;
             if (4 * g + c < cpt) word |= byte << (8 * c);
         }
@@ -655,6 +638,10 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
     __syncthreads();
 
     for (int qb = qb_lo; qb < qb_hi; ++qb) {
+        // The staged tiles do not change across query blocks; reading them through an offset the
+        // compiler cannot see is zero keeps it from hoisting every tile's operands out of this
+        // loop (which would hold them all in registers and halve the occupancy).
+        Lds* const L = lds + opaque_zero();
         const int q0 = qb * kBR, qw0 = q0 + wave * 16;
         const bool live = qw0 < N;  // some query of this wave is < N (wave-uniform)
         const bool more = qb + 1 < qb_hi;
@@ -698,11 +685,11 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
                     idx0 = (ri - rj + a.gh - 1 - win_lo) * (2 * a.gw - 1) + (ci - cj + a.gw - 1);
                     if (jg >= N) idx0 = 15;  // the whole run is past N and masked; keep reads in the window
                 }
-                tile_scores<NT, BIAS>(lds[t].k, lds[t].mu, zk, lq, bias[t], sWin, idx0, t == NTL - 1, N - jg,
+                tile_scores<NT, BIAS>(L[t].k, L[t].mu, zk, lq, bias[t], sWin, idx0, t == NTL - 1, N - jg,
                                       S[t], mloc);
 #pragma unroll
                 for (int ct = 0; ct < NT; ++ct) {
-                    const v4i vop = *reinterpret_cast<const v4i*>(&lds[t].v[(ct * kWave + lane) * 4]);
+                    const v4i vop = *reinterpret_cast<const v4i*>(&L[t].v[(ct * kWave + lane) * 4]);
                     acc[ct] = mfma_i8(vop, kC64, acc[ct]);
                     acc[ct] = mfma_i8(vop, kC64, acc[ct]);
                 }
@@ -735,7 +722,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
                 const v4i pw = tile_probs(S[t], negm, lsum);
 #pragma unroll
                 for (int ct = 0; ct < NT; ++ct) {
-                    const v4i vop = *reinterpret_cast<const v4i*>(&lds[t].v[(ct * kWave + lane) * 4]);
+                    const v4i vop = *reinterpret_cast<const v4i*>(&L[t].v[(ct * kWave + lane) * 4]);
                     acc[ct] = mfma_i8(vop, pw, acc[ct]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
