@@ -146,7 +146,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--qk-ab", action="store_true",
-                    help="only time the binary QK tile by its two methods (fp8 MFMA, VALU XOR+popcount) and exit")
+                    help="only time the binary QK tile by its two methods (fp4 MFMA, VALU XOR+popcount) and exit")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (PMC scaling reference) and exit")
     args = ap.parse_args()

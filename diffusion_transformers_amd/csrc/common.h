@@ -22,45 +22,36 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nblk) {
     return xcd < rem ? xcd * (full + 1) + slot : rem * (full + 1) + (xcd - rem) * full + slot;
 }
 
-// Four bits (bit k = channel k) -> four bytes 0/1 (byte k = bit k).  The multiply by
-// 0x204081 = 1 + 2^7 + 2^14 + 2^21 moves bit k to bit 8k without carries.
-__device__ __forceinline__ uint32_t spread4(uint32_t nib) { return (nib * 0x00204081u) & 0x01010101u; }
-
-// 16 sign bits -> 16 int8 values {0, 1} in four dwords (byte k = bit k).
-__device__ __forceinline__ void unpack_bits16(uint32_t bits16, uint32_t out[4]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) out[q] = spread4((bits16 >> (4 * q)) & 0xFu);
-}
-
-// 16 sign bits -> 16 int8 values {+2, -2} in four dwords (0x02 where the bit is set, 0xFE where clear).
-__device__ __forceinline__ void unpack_signs16_x2(uint32_t bits16, uint32_t out[4]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) out[q] = spread4((~bits16 >> (4 * q)) & 0xFu) * 0xFCu + 0x02020202u;
-}
-
 __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// 16x16x128 MFMA on fp8 (E4M3) operands, fp32 accumulate, no block scaling.
-__device__ __forceinline__ v4f mfma_f8(v8i a, v8i b, v4f c) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+// 16x16x128 MFMA on fp4 (E2M1) operands, fp32 accumulate, no block scaling.  Lane (row r,
+// group g) holds k = 32g .. 32g+31 of its row as four dwords of eight 4-bit codes: dword i,
+// nibble j is k = 32g + 8i + j (the upper half of the 8-dword operand is unused for fp4).
+__device__ __forceinline__ v4f mfma_f4(v4i a, v4i b, v4f c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(v8i{a[0], a[1], a[2], a[3], 0, 0, 0, 0},
+                                                           v8i{b[0], b[1], b[2], b[3], 0, 0, 0, 0}, c, 4, 4, 0,
+                                                           0, 0, 0);
 }
 
-// fp8 E4M3 encodings used as exact small integers: 1.0, 2.0 and -2.0.
-constexpr uint32_t kF8One = 0x38u, kF8Two = 0x40u, kF8MinusTwo = 0xC0u;
-
-// 32 sign bits -> 32 fp8 values {0, 1.0} (byte k = bit k ? 1.0 : 0), eight dwords.
-__device__ __forceinline__ void unpack_bits32_f8(uint32_t w, uint32_t out[8]) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) out[q] = __builtin_amdgcn_perm(0u, kF8One << 8, spread4((w >> (4 * q)) & 0xFu));
+// Eight bits -> bit 0 of eight nibbles: bit k (k < 4) to nibble 2k, bit 4 + k to nibble 2k + 1.
+// The channel order inside a dword is immaterial as long as both MFMA operands use the same one.
+__device__ __forceinline__ uint32_t spread8_nib(uint32_t x) {
+    return ((x & 0xFu) * 0x00204081u & 0x01010101u) | (((x >> 4) & 0xFu) * 0x00204081u & 0x01010101u) << 4;
 }
 
-// 32 sign bits -> 32 fp8 values {+2.0, -2.0} (byte k = bit k ? 2.0 : -2.0), eight dwords.
-__device__ __forceinline__ void unpack_signs32_f8x2(uint32_t w, uint32_t out[8]) {
+// E2M1 codes used as exact small integers: 1.0 = 0x2, 2.0 = 0x4, -2.0 = 0xC.
+// 32 sign bits -> 32 fp4 values {0, 1.0} (bit set: 1.0), four dwords (dword i: bits 8i .. 8i+7).
+__device__ __forceinline__ void unpack_bits32_f4(uint32_t w, uint32_t out[4]) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-        out[q] = __builtin_amdgcn_perm(0u, (kF8MinusTwo << 8) | kF8Two, spread4((~w >> (4 * q)) & 0xFu));
+    for (int i = 0; i < 4; ++i) out[i] = spread8_nib((w >> (8 * i)) & 0xFFu) << 1;
+}
+
+// 32 sign bits -> 32 fp4 values {+2.0, -2.0} (bit set: +2.0), four dwords, same order.
+__device__ __forceinline__ void unpack_signs32_f4x2(uint32_t w, uint32_t out[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = 0xCCCCCCCCu ^ (spread8_nib((w >> (8 * i)) & 0xFFu) << 3);
 }
 
 // Raw buffer resource over [base, base + bytes): loads past the end read as zero.

@@ -8,9 +8,10 @@
 //   hardware implementation bullet: one FlashAttention2-style tiled kernel.
 //
 // gfx950 design (one workgroup = 4 waves x 16 queries of one (b,h); key tiles of 64):
-//  * QK^T on the fp8 MFMA (v_mfma_f32_16x16x128_f8f6f4; one instruction covers d <= 128).
+//  * QK^T on the block-scaled MFMA with fp4 (E2M1) operands (v_mfma_f32_16x16x128_f8f6f4,
+//    cbsz = blgp = 4; one instruction covers d <= 128, 16 bytes of operand per lane).
 //    With s = +-1 query signs and b = 0/1 key bits, s.t = sum s (2b - 1) = 2 s.b - sum(s):
-//    the K operand is the bits as fp8 {0, 1}, the Q operand is fp8 {+-2}, and the
+//    the K operand is the bits as fp4 {0, 1}, the Q operand is fp4 {+-2}, and the
 //    accumulator is seeded with -sum(s) of the lane's query.  Every product and partial
 //    sum is a small integer, so the fp32 result is D exactly, already in float.
 //  * The score tile is computed transposed (keys are MFMA rows, queries columns) with the
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_stream_kernel(FwdArgs a) {
     typedef TileLds<NT, TW> Lds;
     __shared__ Lds lds[2];
     __shared__ __attribute__((aligned(16))) float sScale[128];
-    __shared__ __attribute__((aligned(16))) uint32_t zk[16 * 8];
+    __shared__ __attribute__((aligned(16))) uint32_t zk[kZkWords];
 
     const int N = a.N, d = a.d;
     int bh, q0;
@@ -180,8 +181,8 @@ __global__ __launch_bounds__(256) void binattn_scores_kernel(FwdArgs a) {
     typedef TileRegs<NT, 4> Regs;
     typedef TileLds<NT, 4> Lds;
     __shared__ Lds lds;
-    __shared__ __attribute__((aligned(16))) uint32_t zk[16 * 8];
-    if (threadIdx.x < 16 * 8) zk[threadIdx.x] = 0u;
+    __shared__ __attribute__((aligned(16))) uint32_t zk[kZkWords];
+    if (threadIdx.x < kZkWords) zk[threadIdx.x] = 0u;
     const int N = a.N, d = a.d;
     const int nqb = (N + kBR - 1) / kBR;
     const int nblk = a.B * a.H * nqb;
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(256) void binattn_scores_kernel(FwdArgs a) {
     const int bh = lb / nqb, qb = lb % nqb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, n16 = lane & 15;
     const int q0 = qb * kBR;
-    v8i qop;
+    v4i qop;
     const int i = q0 + wave * 16 + n16;
     const float seed = load_q<W>(a.qbits + ((int64_t)bh * N + (i < N ? i : N - 1)) * W, i < N, d, g, qop);
     const v4f dseed = v4f{seed, seed, seed, seed};
@@ -209,11 +210,8 @@ __global__ __launch_bounds__(256) void binattn_scores_kernel(FwdArgs a) {
         v4f D[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const uint32_t* src = g < W ? &lds.k[((t * W + g) * 16 + n16) * 8] : zk + n16 * 8;
-            const v4i lo = *reinterpret_cast<const v4i*>(src);
-            const v4i hi = *reinterpret_cast<const v4i*>(src + 4);
-            const v8i kop = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            D[t] = mfma_f8(kop, qop, dseed);
+            const uint32_t* src = g < W ? &lds.k[((t * W + g) * 16 + n16) * 4] : zk + n16 * 4;
+            D[t] = mfma_f4(*reinterpret_cast<const v4i*>(src), qop, dseed);
         }
         if (i < N) {
             int32_t* row = a.scores + ((int64_t)bh * N + i) * N;
@@ -232,7 +230,7 @@ __global__ __launch_bounds__(256) void binattn_scores_kernel(FwdArgs a) {
 // QK-tile probe: D_ij for every (query, key) by one of two methods, reduced per query row to
 // max_j D_ij and sum_j D_ij (fp32, exact for these integer ranges), so that the cost of the
 // tile itself is measured rather than the N^2 score writes.
-//   METHOD 0: the forward's tile, fp8 MFMA on LDS-staged fp8 K operands;
+//   METHOD 0: the forward's tile, fp4 MFMA on LDS-staged fp4 K operands;
 //   METHOD 1: VALU XOR + v_bcnt on LDS-staged sign words, D = d - 2 popcount(q XOR k).
 // Both hand D to the softmax stage as fp32 in the same lane layout (query n, keys 16g..16g+15).
 template <int NT, int METHOD>
@@ -242,8 +240,8 @@ __global__ __launch_bounds__(256) void binattn_qk_stats_kernel(FwdArgs a, float*
     typedef TileLds<NT, 4> Lds;
     __shared__ Lds lds;
     __shared__ __attribute__((aligned(16))) uint32_t kraw[kBC * W];
-    __shared__ __attribute__((aligned(16))) uint32_t zk[16 * 8];
-    if (threadIdx.x < 16 * 8) zk[threadIdx.x] = 0u;
+    __shared__ __attribute__((aligned(16))) uint32_t zk[kZkWords];
+    if (threadIdx.x < kZkWords) zk[threadIdx.x] = 0u;
     const int N = a.N, d = a.d;
     const int nqb = (N + kBR - 1) / kBR;
     const int lb = xcd_logical_block(blockIdx.x, a.B * a.H * nqb);
@@ -252,7 +250,7 @@ __global__ __launch_bounds__(256) void binattn_qk_stats_kernel(FwdArgs a, float*
     const int i = qb * kBR + wave * 16 + n16;
     const bool live = i < N;
     const uint32_t* qrow = a.qbits + ((int64_t)bh * N + (live ? i : N - 1)) * W;
-    v8i qop;
+    v4i qop;
     v4f dseed = v4f{0.f, 0.f, 0.f, 0.f};
     uint32_t qw[W];
     if (METHOD == 0) {
@@ -284,10 +282,8 @@ __global__ __launch_bounds__(256) void binattn_qk_stats_kernel(FwdArgs a, float*
         if (METHOD == 0) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const uint32_t* src = g < W ? &lds.k[((t * W + g) * 16 + n16) * 8] : zk + n16 * 8;
-                const v4i lo = *reinterpret_cast<const v4i*>(src);
-                const v4i hi = *reinterpret_cast<const v4i*>(src + 4);
-                const v4f x = mfma_f8(v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, qop, dseed);
+                const uint32_t* src = g < W ? &lds.k[((t * W + g) * 16 + n16) * 4] : zk + n16 * 4;
+                const v4f x = mfma_f4(*reinterpret_cast<const v4i*>(src), qop, dseed);
 #pragma unroll
                 for (int r2 = 0; r2 < 4; ++r2) D[4 * t + r2] = x[r2];
             }

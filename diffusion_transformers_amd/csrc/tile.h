@@ -17,6 +17,7 @@ constexpr int kBC = 64;                     // keys per tile
 constexpr int kRelposWin = 1024;            // fp32 entries of a staged relative-position window
 constexpr int kKeepTiles = 4;               // rows of at most this many tiles: exact max, scores in registers
 constexpr int kDeferTiles = 16;             // streamed rows of at least this many tiles accumulate in int32
+constexpr int kZkWords = 16 * 4;            // K operand of lanes whose channel group is past d: zeros
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2_255 = 7.99435343685886f;
 
@@ -55,7 +56,7 @@ struct TileRegs {
 template <int NT, int TW>
 struct alignas(16) TileLds {
     static constexpr int W = (NT + 1) / 2;
-    uint32_t k[4 * W * 16 * 8];            // [t][group][row] x 32 B: A operand of QK MFMA t, lane (row, group)
+    uint32_t k[4 * W * 16 * 4];            // [t][group][row] x 16 B: fp4 A operand of QK MFMA t, lane (row, group)
     uint32_t v[NT * kWave * 4];            // [ct][lane] x 16 B: A operand of PV MFMA ct
     float mu[kBC];
     float tw[TW];
@@ -144,13 +145,11 @@ __device__ __forceinline__ void store_tile(const TileRegs<NT, TW>& r, TileLds<NT
             uint32_t word = r.kw[i];
             const int left = d - 32 * w;  // channels >= d contribute nothing
             if (left < 32) word &= (1u << left) - 1u;
-            uint32_t o[8];
-            unpack_bits32_f8(word, o);
+            uint32_t o[4];
+            unpack_bits32_f4(word, o);
             int t;
             const int m = key_slot(j, t);
-            uint32_t* dst = &s.k[((t * R::W + w) * 16 + m) * 8];
-            *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-            *reinterpret_cast<uint4*>(dst + 4) = make_uint4(o[4], o[5], o[6], o[7]);
+            *reinterpret_cast<uint4*>(&s.k[((t * R::W + w) * 16 + m) * 4]) = make_uint4(o[0], o[1], o[2], o[3]);
         }
     }
 #pragma unroll
@@ -170,15 +169,22 @@ __device__ __forceinline__ void store_tile(const TileRegs<NT, TW>& r, TileLds<NT
     }
 }
 
-// Q operand (B of the QK MFMA) for one lane: fp8 2*sign of channels 32g .. 32g+31 (0 past d);
-// returns -sum of the query's d signs (the accumulator seed), 0 for a query past N.
-template <int W>
-__device__ __forceinline__ float load_q(const uint32_t* __restrict__ qrow, bool live, int d, int g, v8i& q) {
-    uint32_t o[8];
-    const uint32_t word = (live && g < W) ? qrow[g] : 0u;
-    unpack_signs32_f8x2(word, o);
+// Q operand (B of the QK MFMA) for one lane from word g of its query's signs: fp4 2*sign of
+// channels 32g .. 32g+31, 0 past d (d is a multiple of 8, so whole dwords are dropped).
+__device__ __forceinline__ v4i q_operand(uint32_t word, bool live, int d, int g) {
+    uint32_t o[4];
+    unpack_signs32_f4x2(word, o);
+    v4i q;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) q[c] = (live && g < W && 32 * g + 4 * c < d) ? (int)o[c] : 0;
+    for (int i = 0; i < 4; ++i) q[i] = (live && 32 * g + 8 * i < d) ? (int)o[i] : 0;
+    return q;
+}
+
+// Q operand of one lane read from its packed row; returns -sum of the query's d signs (the
+// accumulator seed), 0 for a query past N.
+template <int W>
+__device__ __forceinline__ float load_q(const uint32_t* __restrict__ qrow, bool live, int d, int g, v4i& q) {
+    q = q_operand((live && g < W) ? qrow[g] : 0u, live && g < W, d, g);
     int pos = 0;
     if (live) {
 #pragma unroll
@@ -221,7 +227,7 @@ __device__ __forceinline__ float bias_at(const BiasRegs<BIAS>& b, int k) {
 
 // The lane's query: Q operand, accumulator seed and scale.
 struct LaneQ {
-    v8i qop;
+    v4i qop;
     v4f dseed;  // -sum of the query's signs
     float cq;   // mu_q / sqrt(d); 0 for a query past N
     int qi;     // query index (clamped to N-1)
@@ -264,7 +270,7 @@ __device__ __forceinline__ LaneQ lane_query(const FwdArgs& a, int bh, int qw0, i
 
 // Scores of one tile for one lane: S[k] for keys jg + k, k = 0..15, in natural units, keys >= N
 // (k >= nvalid on the tail tile) set to -inf, and the running lane max mloc over them.
-// sk/smu: the staged tile; zk: 16 rows x 32 zero bytes, the K operand of lanes whose channel
+// sk/smu: the staged tile; zk: 16 rows x 16 zero bytes, the K operand of lanes whose channel
 // group is past d.  win/idx0: relative-position window and the lane's index of key jg in it
 // (the run's bias is win[idx0 - k]).
 template <int NT, int BIAS>
@@ -277,11 +283,8 @@ __device__ __forceinline__ void tile_scores(const uint32_t* __restrict__ sk, con
     v4f D[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const uint32_t* src = g < W ? &sk[((t * W + g) * 16 + m16) * 8] : zk + m16 * 8;
-        const v4i lo = *reinterpret_cast<const v4i*>(src);
-        const v4i hi = *reinterpret_cast<const v4i*>(src + 4);
-        const v8i kop = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        D[t] = mfma_f8(kop, lq.qop, lq.dseed);
+        const uint32_t* src = g < W ? &sk[((t * W + g) * 16 + m16) * 4] : zk + m16 * 4;
+        D[t] = mfma_f4(*reinterpret_cast<const v4i*>(src), lq.qop, lq.dseed);
     }
     float muk[16];
 #pragma unroll
@@ -360,12 +363,12 @@ __device__ __forceinline__ void store_out(const FwdArgs& a, int bh, const LaneQ&
 // scales s_c = a_c / 127 (IEEE division, as the oracle), 0 for channel slots past d.
 __device__ __forceinline__ void stage_common(const FwdArgs& a, int bh, uint32_t* zk, float* sScale) {
     const int tid = threadIdx.x;
-    if (tid < 16 * 8) zk[tid] = 0u;
+    if (tid < kZkWords) zk[tid] = 0u;
     if (tid < 128) sScale[tid] = tid < a.d ? a.vamax[(int64_t)bh * a.d + tid] / 127.0f : 0.0f;
 }
 
 // Whole-attention staging of one (b, h) from fp16 Q, K, V, done by the short-row kernel itself:
-// K -> sign bits as fp8 operand rows and mu_k (one key per thread); V -> channel absmax,
+// K -> sign bits as fp4 operand rows and mu_k (one key per thread); V -> channel absmax,
 // dequantisation scales and int8 V^ written straight into the operand rows (V held in
 // registers in groups of 4 tokens, transposed with v_perm); the Q of the workgroup's query
 // blocks -> sign word g and mu_q per lane (sQw, sQmu).  The arithmetic is that of
@@ -384,7 +387,7 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
     // operand padding (keys >= N, channel slots >= d) stays zero
     for (int id = tid; id < NTL * NT * 64; id += 256)
         reinterpret_cast<uint4*>(lds[id / (NT * 64)].v)[id % (NT * 64)] = make_uint4(0, 0, 0, 0);
-    if (tid < 16 * 8) zk[tid] = 0u;
+    if (tid < kZkWords) zk[tid] = 0u;
 
     // ---- all K, V and Q loads of the head in flight together.  Buffer loads: rows past N read
     // as zero and no load sits under a lane-dependent branch (so no load is waited for early).
@@ -441,11 +444,9 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
         TileLds<NT, 4>& s = lds[j / kBC];
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-            uint32_t o[8];
-            unpack_bits32_f8(live ? words[w] : 0u, o);
-            uint32_t* dst = &s.k[((t * W + w) * 16 + m) * 8];
-            *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-            *reinterpret_cast<uint4*>(dst + 4) = make_uint4(o[4], o[5], o[6], o[7]);
+            uint32_t o[4];
+            unpack_bits32_f4(live ? words[w] : 0u, o);
+            *reinterpret_cast<uint4*>(&s.k[((t * W + w) * 16 + m) * 4]) = make_uint4(o[0], o[1], o[2], o[3]);
         }
         s.mu[jj] = live ? acc / (float)d : 0.0f;
     }
@@ -556,7 +557,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
     __shared__ Lds lds[NTL];
     __shared__ __attribute__((aligned(16))) float sWin[BIAS == BK_RELPOS ? kRelposWin : 4];
     __shared__ __attribute__((aligned(16))) float sScale[128];
-    __shared__ __attribute__((aligned(16))) uint32_t zk[16 * 8];
+    __shared__ __attribute__((aligned(16))) uint32_t zk[kZkWords];
     // whole-attention path only: the prepared Q of every query block, and staging scratch
     __shared__ __attribute__((aligned(16))) uint32_t sQw[FUSED ? kKeepTiles * kWaves * kWave : 1];
     __shared__ __attribute__((aligned(16))) float sQmu[FUSED ? kKeepTiles * kWaves * 16 : 1];
@@ -647,16 +648,13 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
         const bool more = qb + 1 < qb_hi;
         if (BIAS == BK_RELPOS && more) load_window<kRelposWin / 256>(wv, a, hp.table, window_lo(qb + 1) * (2 * a.gw - 1));
 
-        // the lane's query: Q operand (fp8 2*sign of channels 32g..32g+31, 0 past d) and seed
+        // the lane's query: Q operand (fp4 2*sign of channels 32g..32g+31, 0 past d) and seed
         LaneQ lq;
         {
             const int i = qw0 + n16;
             lq.live = i < N;
             lq.qi = lq.live ? i : N - 1;
-            uint32_t o[8];
-            unpack_signs32_f8x2(qword, o);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) lq.qop[c] = (lq.live && g < W && 32 * g + 4 * c < d) ? (int)o[c] : 0;
+            lq.qop = q_operand(qword, lq.live && g < W, d, g);
             const float pos = rows4_sum((float)__builtin_popcount(qword));  // sign bits set over the query
             const float seed = lq.live ? (float)d - 2.0f * pos : 0.0f;
             lq.dseed = v4f{seed, seed, seed, seed};

@@ -156,7 +156,7 @@ int binattn_scores_i32(const uint32_t* q_bits, const uint32_t* k_bits, int B, in
  * bullet runs it on binary tensor-core MMAs.  This entry computes every D_ij of a forward
  * launch's tiling with the chosen method and reduces each query row, so the two ways of
  * computing the tile on gfx950 can be timed against each other on identical work:
- *   method BINATTN_QK_MFMA     (0): fp8 MFMA on unpacked LDS operands (what binattn_forward uses);
+ *   method BINATTN_QK_MFMA     (0): fp4 MFMA on unpacked LDS operands (what binattn_forward uses);
  *   method BINATTN_QK_POPCOUNT (1): VALU XOR + v_bcnt on LDS-staged sign words.
  *
  *   q_bits, k_bits [B,H,N,W] uint32

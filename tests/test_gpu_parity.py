@@ -139,7 +139,7 @@ def test_scores_bit_exact(d, N):
 @pytest.mark.parametrize("d,N", [(64, 1), (64, 17), (8, 64), (72, 65), (128, 197), (64, 577), (72, 256)])
 def test_qk_tile_probe_both_methods(method, d, N):
     """The QK-tile probe reduces every D_ij of the forward's tiling; both ways of computing the
-    tile (fp8 MFMA, VALU XOR + popcount) give the oracle's row max and row sum exactly."""
+    tile (fp4 MFMA, VALU XOR + popcount) give the oracle's row max and row sum exactly."""
     _say(f"qk probe {method} d={d} N={N}")
     inp = W.custom(2, 3, N, d, "f16", "none", seed=5 * N + d)
     b = _b()
