@@ -9,19 +9,12 @@ namespace binattn {
 
 template <int NT, int BK>
 static hipError_t launch_fused_bk(const FwdArgs& a, hipStream_t s) {
-    const int ntiles = (a.N + kBC - 1) / kBC;
     const int nqb = (a.N + kBR - 1) / kBR;
     // one workgroup per head (each stages its head once) unless there are too few heads to
     // give every compute unit one
     const int64_t heads = (int64_t)a.B * a.H, cus = device_cus();
     const int nsplit = (int)std::min<int64_t>(nqb, std::max<int64_t>(1, (cus + heads - 1) / heads));
-    const dim3 grid((unsigned)(heads * nsplit));
-    switch (ntiles) {
-        case 1: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 1, true>), grid, dim3(256), 0, s, a, nsplit); break;
-        case 2: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 2, true>), grid, dim3(256), 0, s, a, nsplit); break;
-        case 3: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 3, true>), grid, dim3(256), 0, s, a, nsplit); break;
-        default: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 4, true>), grid, dim3(256), 0, s, a, nsplit); break;
-    }
+    launch_keep<NT, BK, true>(a, nsplit, s);
     return hipGetLastError();
 }
 

@@ -49,7 +49,6 @@ __global__ __launch_bounds__(256) void binattn_fwd_stream_kernel(FwdArgs a) {
     typedef TileLds<NT, TW> Lds;
     __shared__ Lds lds[2];
     __shared__ __attribute__((aligned(16))) float sScale[128];
-    __shared__ __attribute__((aligned(16))) uint32_t zk[kZkWords];
 
     const int N = a.N, d = a.d;
     int bh, q0;
@@ -69,7 +68,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_stream_kernel(FwdArgs a) {
         hp.table = a.bias_f32 ? (const void*)((const float*)a.bias + h * tsz)
                               : (const void*)((const _Float16*)a.bias + h * tsz);
     }
-    stage_common(a, bh, zk, sScale);
+    stage_common(a, bh, sScale);
 
     const int qw0 = q0 + wave * 16;
     const bool wave_live = qw0 < N;
@@ -119,7 +118,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_stream_kernel(FwdArgs a) {
         }
         if (!wave_live) return;
         const int j0 = tile * kBC, jg = j0 + 16 * g;
-        int idx0 = 0;
+        int idx0 = 15;
         if (BIAS == BK_RELPOS) {
             const RelposWin w = relpos_window(q0, j0, j0 + kBC, N, a.gh, a.gw);
             const int rj = jg / a.gw, cj = jg % a.gw;
@@ -127,8 +126,8 @@ __global__ __launch_bounds__(256) void binattn_fwd_stream_kernel(FwdArgs a) {
             if (jg >= N) idx0 = 15;
         }
         float S[16], mloc = -INFINITY;
-        tile_scores<NT, BIAS>(s.k, s.mu, zk, lq, bcur, s.tw, idx0, tile == ntiles - 1 && (N & (kBC - 1)) != 0, N - jg,
-                              S, mloc);
+        tile_scores<NT, BIAS>(s.k, s.mu, lq, bcur, s.tw + idx0 - 15, tile == ntiles - 1 && (N & (kBC - 1)) != 0,
+                              N - jg, S, mloc);
         const float mnew = fmaxf(mrun, rows4_max(mloc));
         if (__any(mnew > mrun)) {
             const float alpha = fast_exp2((mrun - mnew) * kLog2e);  // 0 on the first tile
@@ -181,8 +180,6 @@ __global__ __launch_bounds__(256) void binattn_scores_kernel(FwdArgs a) {
     typedef TileRegs<NT, 4> Regs;
     typedef TileLds<NT, 4> Lds;
     __shared__ Lds lds;
-    __shared__ __attribute__((aligned(16))) uint32_t zk[kZkWords];
-    if (threadIdx.x < kZkWords) zk[threadIdx.x] = 0u;
     const int N = a.N, d = a.d;
     const int nqb = (N + kBR - 1) / kBR;
     const int nblk = a.B * a.H * nqb;
@@ -210,7 +207,8 @@ __global__ __launch_bounds__(256) void binattn_scores_kernel(FwdArgs a) {
         v4f D[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const uint32_t* src = g < W ? &lds.k[((t * W + g) * 16 + n16) * 4] : zk + n16 * 4;
+            // lanes with g >= W read group 0: their Q operand is zero
+            const uint32_t* src = &lds.k[((t * W + (g < W ? g : 0)) * 16 + n16) * 4];
             D[t] = mfma_f4(*reinterpret_cast<const v4i*>(src), qop, dseed);
         }
         if (i < N) {
@@ -240,8 +238,6 @@ __global__ __launch_bounds__(256) void binattn_qk_stats_kernel(FwdArgs a, float*
     typedef TileLds<NT, 4> Lds;
     __shared__ Lds lds;
     __shared__ __attribute__((aligned(16))) uint32_t kraw[kBC * W];
-    __shared__ __attribute__((aligned(16))) uint32_t zk[kZkWords];
-    if (threadIdx.x < kZkWords) zk[threadIdx.x] = 0u;
     const int N = a.N, d = a.d;
     const int nqb = (N + kBR - 1) / kBR;
     const int lb = xcd_logical_block(blockIdx.x, a.B * a.H * nqb);
@@ -282,7 +278,7 @@ __global__ __launch_bounds__(256) void binattn_qk_stats_kernel(FwdArgs a, float*
         if (METHOD == 0) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const uint32_t* src = g < W ? &lds.k[((t * W + g) * 16 + n16) * 4] : zk + n16 * 4;
+                const uint32_t* src = &lds.k[((t * W + (g < W ? g : 0)) * 16 + n16) * 4];  // Q is 0 for g >= W
                 const v4f x = mfma_f4(*reinterpret_cast<const v4i*>(src), qop, dseed);
 #pragma unroll
                 for (int r2 = 0; r2 < 4; ++r2) D[4 * t + r2] = x[r2];
@@ -327,13 +323,7 @@ static void launch_fwd_bk(const FwdArgs& a, hipStream_t s) {
         const int64_t heads = (int64_t)a.B * a.H;
         const int64_t want = 3 * (int64_t)device_cus();
         const int nsplit = (int)std::min<int64_t>(nqb, std::max<int64_t>(1, (want + heads - 1) / heads));
-        const dim3 grid((unsigned)(heads * nsplit));
-        switch (ntiles) {
-            case 1: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 1, false>), grid, dim3(256), 0, s, a, nsplit); break;
-            case 2: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 2, false>), grid, dim3(256), 0, s, a, nsplit); break;
-            case 3: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 3, false>), grid, dim3(256), 0, s, a, nsplit); break;
-            default: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 4, false>), grid, dim3(256), 0, s, a, nsplit); break;
-        }
+        launch_keep<NT, BK, false>(a, nsplit, s);
         return;
     }
     const dim3 grid((unsigned)(a.B * a.H * nqb));

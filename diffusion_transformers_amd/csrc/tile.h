@@ -17,7 +17,6 @@ constexpr int kBC = 64;                     // keys per tile
 constexpr int kRelposWin = 1024;            // fp32 entries of a staged relative-position window
 constexpr int kKeepTiles = 4;               // rows of at most this many tiles: exact max, scores in registers
 constexpr int kDeferTiles = 16;             // streamed rows of at least this many tiles accumulate in int32
-constexpr int kZkWords = 16 * 4;            // K operand of lanes whose channel group is past d: zeros
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2_255 = 7.99435343685886f;
 
@@ -270,22 +269,26 @@ __device__ __forceinline__ LaneQ lane_query(const FwdArgs& a, int bh, int qw0, i
 
 // Scores of one tile for one lane: S[k] for keys jg + k, k = 0..15, in natural units, keys >= N
 // (k >= nvalid on the tail tile) set to -inf, and the running lane max mloc over them.
-// sk/smu: the staged tile; zk: 16 rows x 16 zero bytes, the K operand of lanes whose channel
-// group is past d.  win/idx0: relative-position window and the lane's index of key jg in it
-// (the run's bias is win[idx0 - k]).
+// sk/smu: the staged tile.  Lanes whose channel group g is past d read the operand rows of group
+// 0: their Q operand is zero, so those products vanish whatever the K codes are (every fp4 code
+// is finite).  wrun: relative-position window entry of key jg + 15 (the run's bias for key jg + k
+// is wrun[15 - k]: a grid row holds whole runs, and the column offset falls as the key rises).
 template <int NT, int BIAS>
 __device__ __forceinline__ void tile_scores(const uint32_t* __restrict__ sk, const float* __restrict__ smu,
-                                            const uint32_t* zk, const LaneQ& lq, const BiasRegs<BIAS>& bias,
-                                            const float* win, int idx0, bool tail, int nvalid, float (&S)[16],
-                                            float& mloc) {
+                                            const LaneQ& lq, const BiasRegs<BIAS>& bias, const float* wrun,
+                                            bool tail, int nvalid, float (&S)[16], float& mloc) {
     constexpr int W = (NT + 1) / 2;
     const int lane = threadIdx.x & 63, g = lane >> 4, m16 = lane & 15;
+    const int koff = ((g < W ? g : 0) * 16 + m16) * 4;  // lane-constant
     v4f D[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const uint32_t* src = g < W ? &sk[((t * W + g) * 16 + m16) * 4] : zk + m16 * 4;
-        D[t] = mfma_f4(*reinterpret_cast<const v4i*>(src), lq.qop, lq.dseed);
-    }
+    for (int t = 0; t < 4; ++t) D[t] = mfma_f4(*reinterpret_cast<const v4i*>(&sk[t * W * 64 + koff]), lq.qop, lq.dseed);
+    // the run's window entries through one base register and immediate offsets (the window's own
+    // LDS offset is beyond the reach of the read-pair offsets, and folded into it every pair
+    // would take an address add)
+    typedef const float __attribute__((address_space(3)))* lds_cfptr;
+    lds_cfptr wl = (lds_cfptr)wrun;
+    if (BIAS == BK_RELPOS) asm volatile("" : "+v"(wl));
     float muk[16];
 #pragma unroll
     for (int k = 0; k < 16; k += 4) {
@@ -296,7 +299,7 @@ __device__ __forceinline__ void tile_scores(const uint32_t* __restrict__ sk, con
     for (int k = 0; k < 16; ++k) {
         float b = 0.0f;
         if (BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32) b = bias_at<BIAS>(bias, k);
-        if (BIAS == BK_RELPOS) b = win[idx0 - k];
+        if (BIAS == BK_RELPOS) b = wl[15 - k];
         S[k] = __builtin_fmaf(D[k >> 2][k & 3] * muk[k], lq.cq, b);
     }
     // The max is taken separately on the two paths: on the common one every S is an fma
@@ -359,11 +362,10 @@ __device__ __forceinline__ void store_out(const FwdArgs& a, int bh, const LaneQ&
     }
 }
 
-// Per-workgroup set-up shared by both kernels: the K zero block and the dequantisation
-// scales s_c = a_c / 127 (IEEE division, as the oracle), 0 for channel slots past d.
-__device__ __forceinline__ void stage_common(const FwdArgs& a, int bh, uint32_t* zk, float* sScale) {
+// Per-workgroup set-up shared by both kernels: the dequantisation scales s_c = a_c / 127
+// (IEEE division, as the oracle), 0 for channel slots past d.
+__device__ __forceinline__ void stage_common(const FwdArgs& a, int bh, float* sScale) {
     const int tid = threadIdx.x;
-    if (tid < kZkWords) zk[tid] = 0u;
     if (tid < 128) sScale[tid] = tid < a.d ? a.vamax[(int64_t)bh * a.d + tid] / 127.0f : 0.0f;
 }
 
@@ -377,7 +379,7 @@ __device__ __forceinline__ void stage_common(const FwdArgs& a, int bh, uint32_t*
 // sRed: 2048 floats; sInv: 128 floats.
 template <int NT, int NTL>
 __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo, int nitems, TileLds<NT, 4>* lds,
-                                            float* sScale, uint32_t* zk, uint32_t* sQw, float* sQmu, float* sRed,
+                                            float* sScale, uint32_t* sQw, float* sQmu, float* sRed,
                                             float* sInv) {
     constexpr int W = (NT + 1) / 2;
     constexpr int MAXCK = 2 * NT;  // 8-channel chunks of one key (d <= 16 NT)
@@ -387,7 +389,6 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
     // operand padding (keys >= N, channel slots >= d) stays zero
     for (int id = tid; id < NTL * NT * 64; id += 256)
         reinterpret_cast<uint4*>(lds[id / (NT * 64)].v)[id % (NT * 64)] = make_uint4(0, 0, 0, 0);
-    if (tid < kZkWords) zk[tid] = 0u;
 
     // ---- all K, V and Q loads of the head in flight together.  Buffer loads: rows past N read
     // as zero and no load sits under a lane-dependent branch (so no load is waited for early).
@@ -548,7 +549,8 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
 // query blocks [qb_lo, qb_hi) of that head (nsplit workgroups per head).  The next block's query
 // words, dense-bias rows and relative-position window are loaded while the current block is
 // computed, into registers the current block no longer needs.
-template <int NT, int BIAS, int NTL, bool FUSED>
+// RAGGED: N is not a multiple of the tile (the last tile masks the keys >= N).
+template <int NT, int BIAS, int NTL, bool FUSED, bool RAGGED>
 __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int nsplit) {
     constexpr int W = (NT + 1) / 2;
     constexpr bool DENSE = BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32;
@@ -557,7 +559,6 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
     __shared__ Lds lds[NTL];
     __shared__ __attribute__((aligned(16))) float sWin[BIAS == BK_RELPOS ? kRelposWin : 4];
     __shared__ __attribute__((aligned(16))) float sScale[128];
-    __shared__ __attribute__((aligned(16))) uint32_t zk[kZkWords];
     // whole-attention path only: the prepared Q of every query block, and staging scratch
     __shared__ __attribute__((aligned(16))) uint32_t sQw[FUSED ? kKeepTiles * kWaves * kWave : 1];
     __shared__ __attribute__((aligned(16))) float sQmu[FUSED ? kKeepTiles * kWaves * 16 : 1];
@@ -612,13 +613,13 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
 
     // ---- stage the head once (all loads in flight together), then the first block's inputs
     if constexpr (FUSED) {
-        fused_stage<NT, NTL>(a, bh, qb_lo, qb_hi - qb_lo, lds, sScale, zk, sQw, sQmu, sRed, sInv);
+        fused_stage<NT, NTL>(a, bh, qb_lo, qb_hi - qb_lo, lds, sScale, sQw, sQmu, sRed, sInv);
         __syncthreads();  // the prepared query words are read by load_query below
     } else {
         Regs regs[NTL];
 #pragma unroll
         for (int t = 0; t < NTL; ++t) load_tile<NT, 4>(regs[t], a, hp, 0, t * kBC);
-        stage_common(a, bh, zk, sScale);
+        stage_common(a, bh, sScale);
 #pragma unroll
         for (int t = 0; t < NTL; ++t) store_tile<NT, 4>(regs[t], lds[t], d);
     }
@@ -677,14 +678,14 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
 #pragma unroll
             for (int t = 0; t < NTL; ++t) {
                 const int jg = t * kBC + 16 * g;
-                int idx0 = 0;
+                int idx0 = 15;
                 if (BIAS == BK_RELPOS) {
                     const int rj = jg / a.gw, cj = jg % a.gw;
                     idx0 = (ri - rj + a.gh - 1 - win_lo) * (2 * a.gw - 1) + (ci - cj + a.gw - 1);
                     if (jg >= N) idx0 = 15;  // the whole run is past N and masked; keep reads in the window
                 }
-                tile_scores<NT, BIAS>(L[t].k, L[t].mu, zk, lq, bias[t], sWin, idx0, t == NTL - 1, N - jg,
-                                      S[t], mloc);
+                tile_scores<NT, BIAS>(L[t].k, L[t].mu, lq, bias[t], sWin + idx0 - 15,
+                                      RAGGED && t == NTL - 1, N - jg, S[t], mloc);
 #pragma unroll
                 for (int ct = 0; ct < NT; ++ct) {
                     const v4i vop = *reinterpret_cast<const v4i*>(&L[t].v[(ct * kWave + lane) * 4]);
@@ -733,6 +734,28 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
             store_out<NT>(a, bh, lq, sScale, accf, rows4_sum(lsum));
         }
         if (BIAS == BK_RELPOS) __syncthreads();  // the next block's window is in place
+    }
+}
+
+// Launches the short-row kernel for rows of ceil(N / 64) <= kKeepTiles tiles, nsplit workgroups per head.
+template <int NT, int BK, bool FUSED>
+inline void launch_keep(const FwdArgs& a, int nsplit, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)a.B * a.H * nsplit)), block(256);
+    const int ntiles = (a.N + kBC - 1) / kBC;
+    if (a.N % kBC != 0) {
+        switch (ntiles) {
+            case 1: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 1, FUSED, true>), grid, block, 0, s, a, nsplit); break;
+            case 2: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 2, FUSED, true>), grid, block, 0, s, a, nsplit); break;
+            case 3: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 3, FUSED, true>), grid, block, 0, s, a, nsplit); break;
+            default: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 4, FUSED, true>), grid, block, 0, s, a, nsplit); break;
+        }
+    } else {
+        switch (ntiles) {
+            case 1: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 1, FUSED, false>), grid, block, 0, s, a, nsplit); break;
+            case 2: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 2, FUSED, false>), grid, block, 0, s, a, nsplit); break;
+            case 3: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 3, FUSED, false>), grid, block, 0, s, a, nsplit); break;
+            default: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 4, FUSED, false>), grid, block, 0, s, a, nsplit); break;
+        }
     }
 }
 
