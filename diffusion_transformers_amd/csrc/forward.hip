@@ -31,8 +31,9 @@
 //    the tiles through a two-stage LDS ring with the FlashAttention-2 running max.
 //  * p = 255 exp(S - m) = exp2(S log2e - m log2e + log2 255), P^ = rint(p) via
 //    v_cvt_pk_u8_f32; the row sum is taken over the unquantised p.
-//  * PV with signed int8 MFMA: sum P^ V^ = sum (P^-128) V^ + 2 * sum 64 V^; the two
-//    64-weighted column sums are two more MFMAs into the same accumulator.
+//  * PV with signed int8 MFMA: sum P^ V^ = sum (P^-128) V^ + 128 sum V^.  Short rows take
+//    the column sums once per head while staging and start the accumulator there; streamed
+//    rows add them per tile as two more MFMAs (B = 64) into the same accumulator.
 //  * Epilogue: O = acc * s_c / sum(p), s_c = a_c / 127 from the channel absmax a_c.
 #include "tile.h"
 

@@ -168,6 +168,34 @@ __device__ __forceinline__ void store_tile(const TileRegs<NT, TW>& r, TileLds<NT
     }
 }
 
+// Column sums of V^ for the u8 offset of P^: sum_j P^_j V^_jc = sum_j (P^_j - 128) V^_jc +
+// 128 sum_j V^_jc, and the second term does not depend on the query.  colsum_add adds the
+// sums of the 16-key chunks a thread stages (one channel slot per chunk); colsum_store
+// reduces the four chunks of a slot (four consecutive lanes) and writes 128 * sum per slot.
+template <int NT, int TW>
+__device__ __forceinline__ void colsum_add(const TileRegs<NT, TW>& r, int (&cs)[TileRegs<NT, TW>::VCH]) {
+#pragma unroll
+    for (int i = 0; i < TileRegs<NT, TW>::VCH; ++i) {
+        const uint4 x = r.v[i];
+        int sum = __builtin_amdgcn_sdot4((int)x.x, 0x01010101, 0, false);
+        sum = __builtin_amdgcn_sdot4((int)x.y, 0x01010101, sum, false);
+        sum = __builtin_amdgcn_sdot4((int)x.z, 0x01010101, sum, false);
+        cs[i] += __builtin_amdgcn_sdot4((int)x.w, 0x01010101, sum, false);
+    }
+}
+
+template <int NT, int VCH>
+__device__ __forceinline__ void colsum_store(const int (&cs)[VCH], int* sCol) {
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+        const int id = threadIdx.x + 256 * i;
+        int v = cs[i];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        if (id < NT * 64 && (id & 3) == 0) sCol[id >> 2] = 128 * v;
+    }
+}
+
 // Q operand (B of the QK MFMA) for one lane from word g of its query's signs: fp4 2*sign of
 // channels 32g .. 32g+31, 0 past d (d is a multiple of 8, so whole dwords are dropped).
 __device__ __forceinline__ v4i q_operand(uint32_t word, bool live, int d, int g) {
@@ -376,11 +404,11 @@ __device__ __forceinline__ void stage_common(const FwdArgs& a, int bh, float* sS
 // blocks -> sign word g and mu_q per lane (sQw, sQmu).  The arithmetic is that of
 // pack_block and quant_head_regs -- the same comparisons, the same fp32 summation order for
 // mu, the same IEEE 127/a and rint -- so the results equal the separate path bit for bit.
-// sRed: 2048 floats; sInv: 128 floats.
+// sRed: 2048 floats; sInv: 128 floats; sCol: 128 * sum_j V^_jc per channel slot (16 NT).
 template <int NT, int NTL>
 __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo, int nitems, TileLds<NT, 4>* lds,
                                             float* sScale, uint32_t* sQw, float* sQmu, float* sRed,
-                                            float* sInv) {
+                                            float* sInv, int* sCol) {
     constexpr int W = (NT + 1) / 2;
     constexpr int MAXCK = 2 * NT;  // 8-channel chunks of one key (d <= 16 NT)
     constexpr int MAXC = 16;       // V chunks per thread: 4 * ceil(64 / G) with G = 256 / (d/8) >= 16
@@ -471,6 +499,9 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
         sInv[tid] = av > 0.0f ? 127.0f / av : 0.0f;
     }
     __syncthreads();
+    float vsum[8];  // this thread's part of sum_j V^_jc for its 8 channels (exact integers)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vsum[e] = 0.0f;
     if (grp < G) {
         float inv[8];
 #pragma unroll
@@ -489,6 +520,7 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
                         for (int b = 0; b < 4; ++b) {
                             // |v| <= a keeps rint(v * fl32(127/a)) within +-127 (no clamp needed)
                             const float q = __builtin_rintf((float)vx[4 * u + r][4 * w + b] * inv[4 * w + b]);
+                            vsum[4 * w + b] += q;
                             word = __builtin_amdgcn_cvt_pk_u8_f32(q + 128.0f, b, word);  // exact: q is an integer
                         }
                         qb[r][w] = word ^ 0x80808080u;
@@ -509,6 +541,19 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
                 }
             }
         }
+    }
+
+    // column sums: partial sums through sRed (the absmax pass is done with it), then one thread per slot
+    if (grp < G) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sRed[grp * d + part * 8 + e] = vsum[e];
+    }
+    __syncthreads();
+    if (tid < NT * 16) {
+        float cs = 0.0f;
+        if (tid < d)
+            for (int gi = 0; gi < G; ++gi) cs += sRed[gi * d + tid];
+        sCol[tid] = 128 * (int)cs;
     }
 
     // ---- Q of every query block of this workgroup: word g of the signs and mu_q per lane
@@ -559,6 +604,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
     __shared__ Lds lds[NTL];
     __shared__ __attribute__((aligned(16))) float sWin[BIAS == BK_RELPOS ? kRelposWin : 4];
     __shared__ __attribute__((aligned(16))) float sScale[128];
+    __shared__ __attribute__((aligned(16))) int sCol[128];  // 128 * sum_j V^_jc per channel slot
     // whole-attention path only: the prepared Q of every query block, and staging scratch
     __shared__ __attribute__((aligned(16))) uint32_t sQw[FUSED ? kKeepTiles * kWaves * kWave : 1];
     __shared__ __attribute__((aligned(16))) float sQmu[FUSED ? kKeepTiles * kWaves * 16 : 1];
@@ -613,15 +659,22 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
 
     // ---- stage the head once (all loads in flight together), then the first block's inputs
     if constexpr (FUSED) {
-        fused_stage<NT, NTL>(a, bh, qb_lo, qb_hi - qb_lo, lds, sScale, sQw, sQmu, sRed, sInv);
+        fused_stage<NT, NTL>(a, bh, qb_lo, qb_hi - qb_lo, lds, sScale, sQw, sQmu, sRed, sInv, sCol);
         __syncthreads();  // the prepared query words are read by load_query below
     } else {
         Regs regs[NTL];
 #pragma unroll
         for (int t = 0; t < NTL; ++t) load_tile<NT, 4>(regs[t], a, hp, 0, t * kBC);
         stage_common(a, bh, sScale);
+        int cs[Regs::VCH];
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) store_tile<NT, 4>(regs[t], lds[t], d);
+        for (int i = 0; i < Regs::VCH; ++i) cs[i] = 0;
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+            store_tile<NT, 4>(regs[t], lds[t], d);
+            colsum_add(regs[t], cs);
+        }
+        colsum_store<NT>(cs, sCol);
     }
     float wv[kRelposWin / 256];
     if (BIAS == BK_RELPOS) {
@@ -668,12 +721,9 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
             win_lo = window_lo(qb);
         }
 
-        // ---- pass 1: scores, row max, and the V^ column-sum term (128 * sum V^ per channel)
+        // ---- pass 1: scores and row max
         float S[NTL][16];
         float mloc = -INFINITY;
-        v4i acc[NT];
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct) acc[ct] = v4i{0, 0, 0, 0};
         if (live) {
 #pragma unroll
             for (int t = 0; t < NTL; ++t) {
@@ -686,12 +736,6 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
                 }
                 tile_scores<NT, BIAS>(L[t].k, L[t].mu, lq, bias[t], sWin + idx0 - 15,
                                       RAGGED && t == NTL - 1, N - jg, S[t], mloc);
-#pragma unroll
-                for (int ct = 0; ct < NT; ++ct) {
-                    const v4i vop = *reinterpret_cast<const v4i*>(&L[t].v[(ct * kWave + lane) * 4]);
-                    acc[ct] = mfma_i8(vop, kC64, acc[ct]);
-                    acc[ct] = mfma_i8(vop, kC64, acc[ct]);
-                }
                 __builtin_amdgcn_sched_barrier(0);  // one tile's operands live at a time
             }
         }
@@ -716,6 +760,9 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
             const float m = rows4_max(mloc);
             const float negm = kLog2_255 - m * kLog2e;
             float lsum = 0.0f;
+            v4i acc[NT];  // starts at the column-sum term of the lane's channels
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) acc[ct] = *reinterpret_cast<const v4i*>(&sCol[4 * NT * g + 4 * ct]);
 #pragma unroll
             for (int t = 0; t < NTL; ++t) {
                 const v4i pw = tile_probs(S[t], negm, lsum);
