@@ -9,12 +9,7 @@ namespace binattn {
 
 template <int NT, int BK>
 static hipError_t launch_fused_bk(const FwdArgs& a, hipStream_t s) {
-    const int nqb = (a.N + kBR - 1) / kBR;
-    // one workgroup per head (each stages its head once) unless there are too few heads to
-    // give every compute unit one
-    const int64_t heads = (int64_t)a.B * a.H, cus = device_cus();
-    const int nsplit = (int)std::min<int64_t>(nqb, std::max<int64_t>(1, (cus + heads - 1) / heads));
-    launch_keep<NT, BK, true>(a, nsplit, s);
+    launch_keep<NT, BK, true>(a, s);
     return hipGetLastError();
 }
 

@@ -320,12 +320,14 @@ static void launch_fwd_bk(const FwdArgs& a, hipStream_t s) {
     const int ntiles = (a.N + kBC - 1) / kBC;
     const int nqb = (a.N + kBR - 1) / kBR;
     if (ntiles <= kKeepTiles && (BK != BK_RELPOS || keep_window_fits(a))) {
-        // enough workgroups for about three per compute unit, each looping over several query blocks
-        const int64_t heads = (int64_t)a.B * a.H;
-        const int64_t want = 3 * (int64_t)device_cus();
-        const int nsplit = (int)std::min<int64_t>(nqb, std::max<int64_t>(1, (want + heads - 1) / heads));
-        launch_keep<NT, BK, false>(a, nsplit, s);
+        launch_keep<NT, BK, false>(a, s);
         return;
+    }
+    if constexpr (NT <= 4 && BK != BK_RELPOS) {
+        if (ntiles <= kLongTiles) {
+            launch_keep_long<NT, BK>(a, s);
+            return;
+        }
     }
     const dim3 grid((unsigned)(a.B * a.H * nqb));
     if (ntiles >= kDeferTiles)

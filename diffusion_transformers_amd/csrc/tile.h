@@ -4,6 +4,9 @@
 #pragma once
 
 #include <algorithm>
+#include <functional>
+#include <mutex>
+#include <vector>
 
 #include "common.h"
 #include "internal.h"
@@ -16,11 +19,18 @@ constexpr int kBR = kWaves * 16;            // queries per workgroup (16 per wav
 constexpr int kBC = 64;                     // keys per tile
 constexpr int kRelposWin = 1024;            // fp32 entries of a staged relative-position window
 constexpr int kKeepTiles = 4;               // rows of at most this many tiles: exact max, scores in registers
+constexpr int kLongTiles = 10;              // d <= 64: rows of up to this many tiles take the same kernel
 constexpr int kDeferTiles = 16;             // streamed rows of at least this many tiles accumulate in int32
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2_255 = 7.99435343685886f;
 
 enum { BK_NONE = 0, BK_DENSE_F16 = 1, BK_DENSE_F32 = 2, BK_RELPOS = 3 };
+
+// How the short-row kernel splits the query blocks of a head over workgroups: `a` segments of f
+// blocks, then `b` segments of r blocks (the last segment of each kind clipped to the row).
+struct KeepPlan {
+    int a, f, b, r;
+};
 
 // Keys of one 64-key tile as A-operand rows: MFMA tile t, row m <-> key 16*(m/4) + 4t + (m%4).
 // After the MFMA, lane (n, g) register r of tile t holds key 16g + 4t + r.
@@ -595,10 +605,14 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
 // words, dense-bias rows and relative-position window are loaded while the current block is
 // computed, into registers the current block no longer needs.
 // RAGGED: N is not a multiple of the tile (the last tile masks the keys >= N).
+// NTL > kKeepTiles (long rows): NTL is the capacity and ceil(N / 64) <= NTL tiles are used; the
+// dense bias is then fetched one tile ahead instead of a whole query block ahead.
 template <int NT, int BIAS, int NTL, bool FUSED, bool RAGGED>
-__global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int nsplit) {
+__global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPlan plan) {
     constexpr int W = (NT + 1) / 2;
     constexpr bool DENSE = BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32;
+    constexpr bool LONG = NTL > kKeepTiles;
+    static_assert(!(LONG && FUSED), "the whole-attention staging covers short rows only");
     typedef TileRegs<NT, 4> Regs;
     typedef TileLds<NT, 4> Lds;
     __shared__ Lds lds[NTL];
@@ -613,12 +627,30 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
 
     const int N = a.N, d = a.d;
     const int nqb = (N + kBR - 1) / kBR;
-    const int lb = xcd_logical_block(blockIdx.x, a.B * a.H * nsplit);
-    const int bh = lb / nsplit, split = lb % nsplit;
-    const int qb_lo = split * nqb / nsplit, qb_hi = (split + 1) * nqb / nsplit;
-    const int h = bh % a.H;
+    const int nt = LONG ? (N + kBC - 1) / kBC : NTL;  // tiles in use
+    // This workgroup's segment of the query blocks of one head.  Workgroup b runs on XCD b % 8;
+    // each XCD owns a contiguous range of heads and lays its workgroups out by the plan (first
+    // the `a` segments of f blocks of each head, then the `b` segments of r blocks).
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int64_t nheads = (int64_t)a.B * a.H;
+    const int hx0 = (int)(nheads * xcd / 8), hx = (int)(nheads * (xcd + 1) / 8) - hx0;
+    int bh, qb_lo, qb_len;
+    if (slot < hx * plan.a) {
+        bh = hx0 + slot / plan.a;
+        qb_lo = (slot % plan.a) * plan.f;
+        qb_len = plan.f;
+    } else {
+        const int s2 = slot - hx * plan.a;
+        if (s2 >= hx * plan.b) return;  // this XCD has fewer heads than the grid allows for
+        bh = hx0 + s2 / plan.b;
+        qb_lo = plan.a * plan.f + (s2 % plan.b) * plan.r;
+        qb_len = plan.r;
+    }
+    const int qb_hi = min(nqb, qb_lo + qb_len);
+    if (qb_lo >= qb_hi) return;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: keeps row pointers scalar
+    const int h = bh % a.H;
 
     HeadPtrs hp;
     hp.kb = a.kbits + (int64_t)bh * N * W;
@@ -664,15 +696,18 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
     } else {
         Regs regs[NTL];
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) load_tile<NT, 4>(regs[t], a, hp, 0, t * kBC);
+        for (int t = 0; t < NTL; ++t)
+            if (!LONG || t < nt) load_tile<NT, 4>(regs[t], a, hp, 0, t * kBC);
         stage_common(a, bh, sScale);
         int cs[Regs::VCH];
 #pragma unroll
         for (int i = 0; i < Regs::VCH; ++i) cs[i] = 0;
 #pragma unroll
         for (int t = 0; t < NTL; ++t) {
-            store_tile<NT, 4>(regs[t], lds[t], d);
-            colsum_add(regs[t], cs);
+            if (!LONG || t < nt) {
+                store_tile<NT, 4>(regs[t], lds[t], d);
+                colsum_add(regs[t], cs);
+            }
         }
         colsum_store<NT>(cs, sCol);
     }
@@ -685,10 +720,12 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
     uint32_t qword;
     float qmu;
     load_query(qb_lo, qword, qmu);
-    BiasRegs<BIAS> bias[NTL];
+    // short rows: every tile's bias rows of the block, fetched a block ahead; long rows: two
+    // tile buffers, each tile fetched while the one before it is computed
+    BiasRegs<BIAS> bias[LONG ? 2 : NTL];
     if (DENSE) {
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) load_bias_tile(qb_lo, t, bias[t]);
+        for (int t = 0; t < (LONG ? 1 : NTL); ++t) load_bias_tile(qb_lo, t, bias[t]);
     }
     __syncthreads();
 
@@ -727,15 +764,18 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
         if (live) {
 #pragma unroll
             for (int t = 0; t < NTL; ++t) {
-                const int jg = t * kBC + 16 * g;
-                int idx0 = 15;
-                if (BIAS == BK_RELPOS) {
-                    const int rj = jg / a.gw, cj = jg % a.gw;
-                    idx0 = (ri - rj + a.gh - 1 - win_lo) * (2 * a.gw - 1) + (ci - cj + a.gw - 1);
-                    if (jg >= N) idx0 = 15;  // the whole run is past N and masked; keep reads in the window
+                if (!LONG || t < nt) {  // (a uniform skip, not a break: the loop must unroll to keep S in registers)
+                    if (LONG && DENSE && t + 1 < nt) load_bias_tile(qb, t + 1, bias[(t + 1) & 1]);
+                    const int jg = t * kBC + 16 * g;
+                    int idx0 = 15;
+                    if (BIAS == BK_RELPOS) {
+                        const int rj = jg / a.gw, cj = jg % a.gw;
+                        idx0 = (ri - rj + a.gh - 1 - win_lo) * (2 * a.gw - 1) + (ci - cj + a.gw - 1);
+                        if (jg >= N) idx0 = 15;  // the whole run is past N and masked; keep reads in the window
+                    }
+                    tile_scores<NT, BIAS>(L[t].k, L[t].mu, lq, bias[LONG ? (t & 1) : t], sWin + idx0 - 15,
+                                          RAGGED && t == nt - 1, N - jg, S[t], mloc);
                 }
-                tile_scores<NT, BIAS>(L[t].k, L[t].mu, lq, bias[t], sWin + idx0 - 15,
-                                      RAGGED && t == NTL - 1, N - jg, S[t], mloc);
                 __builtin_amdgcn_sched_barrier(0);  // one tile's operands live at a time
             }
         }
@@ -744,7 +784,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
             load_query(qb + 1, qword, qmu);
             if (DENSE) {
 #pragma unroll
-                for (int t = 0; t < NTL; ++t) load_bias_tile(qb + 1, t, bias[t]);
+                for (int t = 0; t < (LONG ? 1 : NTL); ++t) load_bias_tile(qb + 1, t, bias[t]);
             }
         }
         if (BIAS == BK_RELPOS) {
@@ -765,11 +805,13 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
             for (int ct = 0; ct < NT; ++ct) acc[ct] = *reinterpret_cast<const v4i*>(&sCol[4 * NT * g + 4 * ct]);
 #pragma unroll
             for (int t = 0; t < NTL; ++t) {
-                const v4i pw = tile_probs(S[t], negm, lsum);
+                if (!LONG || t < nt) {
+                    const v4i pw = tile_probs(S[t], negm, lsum);
 #pragma unroll
-                for (int ct = 0; ct < NT; ++ct) {
-                    const v4i vop = *reinterpret_cast<const v4i*>(&L[t].v[(ct * kWave + lane) * 4]);
-                    acc[ct] = mfma_i8(vop, pw, acc[ct]);
+                    for (int ct = 0; ct < NT; ++ct) {
+                        const v4i vop = *reinterpret_cast<const v4i*>(&L[t].v[(ct * kWave + lane) * 4]);
+                        acc[ct] = mfma_i8(vop, pw, acc[ct]);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -781,28 +823,6 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, int ns
             store_out<NT>(a, bh, lq, sScale, accf, rows4_sum(lsum));
         }
         if (BIAS == BK_RELPOS) __syncthreads();  // the next block's window is in place
-    }
-}
-
-// Launches the short-row kernel for rows of ceil(N / 64) <= kKeepTiles tiles, nsplit workgroups per head.
-template <int NT, int BK, bool FUSED>
-inline void launch_keep(const FwdArgs& a, int nsplit, hipStream_t s) {
-    const dim3 grid((unsigned)((int64_t)a.B * a.H * nsplit)), block(256);
-    const int ntiles = (a.N + kBC - 1) / kBC;
-    if (a.N % kBC != 0) {
-        switch (ntiles) {
-            case 1: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 1, FUSED, true>), grid, block, 0, s, a, nsplit); break;
-            case 2: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 2, FUSED, true>), grid, block, 0, s, a, nsplit); break;
-            case 3: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 3, FUSED, true>), grid, block, 0, s, a, nsplit); break;
-            default: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 4, FUSED, true>), grid, block, 0, s, a, nsplit); break;
-        }
-    } else {
-        switch (ntiles) {
-            case 1: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 1, FUSED, false>), grid, block, 0, s, a, nsplit); break;
-            case 2: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 2, FUSED, false>), grid, block, 0, s, a, nsplit); break;
-            case 3: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 3, FUSED, false>), grid, block, 0, s, a, nsplit); break;
-            default: hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, 4, FUSED, false>), grid, block, 0, s, a, nsplit); break;
-        }
     }
 }
 
@@ -828,6 +848,112 @@ inline int device_cus() {
         cache[dev] = n;
     }
     return cache[dev];
+}
+
+// Resident 256-thread workgroups of `kernel` per compute unit (registers and LDS permitting).
+template <typename K>
+inline int resident_per_cu(K kernel) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, 256, 0) != hipSuccess || nb < 1) nb = 1;
+    return nb;
+}
+
+// Makespan, in units of one query block's work, of one XCD's workgroups under `plan`, dispatched
+// in order onto `slots` resident slots as they free up (each workgroup also stages its head,
+// `stage` units).
+inline double keep_plan_makespan(int heads, int nqb, int slots, double stage, KeepPlan p) {
+    std::vector<double> free_at((size_t)std::max(slots, 1), 0.0);
+    std::make_heap(free_at.begin(), free_at.end(), std::greater<double>());
+    double end = 0.0;
+    auto run = [&](int len) {
+        std::pop_heap(free_at.begin(), free_at.end(), std::greater<double>());
+        const double t = free_at.back() + stage + len;
+        free_at.back() = t;
+        std::push_heap(free_at.begin(), free_at.end(), std::greater<double>());
+        end = std::max(end, t);
+    };
+    for (int h = 0; h < heads; ++h)
+        for (int k = 0; k < p.a; ++k) run(std::max(0, std::min(p.f, nqb - k * p.f)));
+    for (int h = 0; h < heads; ++h)
+        for (int k = 0; k < p.b; ++k) run(std::max(0, std::min(p.r, nqb - p.a * p.f - k * p.r)));
+    return end;
+}
+
+// The plan with the shortest modelled makespan for B*H heads of nqb query blocks on a device
+// with `slots` resident workgroups (all XCDs); remembered per shape.
+inline KeepPlan keep_plan(int64_t nheads, int nqb, int slots, double stage) {
+    struct Entry {
+        int64_t nheads;
+        int nqb, slots, stage_milli;
+        KeepPlan plan;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    const int stage_milli = (int)(stage * 1000.0);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (const Entry& e : cache)
+            if (e.nheads == nheads && e.nqb == nqb && e.slots == slots && e.stage_milli == stage_milli) return e.plan;
+    }
+    const int heads = (int)((nheads + 7) / 8), xslots = std::max(1, slots / 8);  // the busiest XCD
+    KeepPlan best{1, nqb, 0, 1};
+    double best_t = keep_plan_makespan(heads, nqb, xslots, stage, best);
+    for (int f = 1; f <= nqb; ++f)
+        for (int na = 1; na * f <= nqb + f - 1; ++na) {
+            const int rest = nqb - na * f;
+            for (int r = 1; r <= (rest > 0 ? f : 1); ++r) {
+                const KeepPlan p{na, f, rest > 0 ? (rest + r - 1) / r : 0, r};
+                const double t = keep_plan_makespan(heads, nqb, xslots, stage, p);
+                if (t < best_t - 1e-9) best_t = t, best = p;
+            }
+        }
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache.size() > 64) cache.clear();
+    cache.push_back(Entry{nheads, nqb, slots, stage_milli, best});
+    return best;
+}
+
+// Staging a head costs about half a query block's work (plain), three (whole attention).
+template <int NT, int BK, int NTL, bool FUSED, bool RAGGED>
+inline void launch_keep_inst(const FwdArgs& a, hipStream_t s) {
+    static const int per_cu = resident_per_cu(binattn_fwd_keep_kernel<NT, BK, NTL, FUSED, RAGGED>);
+    const int64_t nheads = (int64_t)a.B * a.H;
+    const int nqb = (a.N + kBR - 1) / kBR;
+    const KeepPlan p = keep_plan(nheads, nqb, per_cu * device_cus(), FUSED ? 3.0 : 0.5);
+    const int64_t grid = 8 * ((nheads + 7) / 8) * (p.a + p.b);
+    hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, NTL, FUSED, RAGGED>), dim3((unsigned)grid), dim3(256), 0, s,
+                       a, p);
+}
+
+// The head-resident kernel for rows of kKeepTiles < ceil(N / 64) <= kLongTiles tiles (d <= 64).
+template <int NT, int BK>
+inline void launch_keep_long(const FwdArgs& a, hipStream_t s) {
+    static_assert(NT <= 4, "long rows are staged whole for d <= 64 only");
+    if (a.N % kBC != 0)
+        launch_keep_inst<NT, BK, kLongTiles, false, true>(a, s);
+    else
+        launch_keep_inst<NT, BK, kLongTiles, false, false>(a, s);
+}
+
+// The short-row kernel for rows of ceil(N / 64) <= kKeepTiles tiles.
+template <int NT, int BK, bool FUSED>
+inline void launch_keep(const FwdArgs& a, hipStream_t s) {
+    const int ntiles = (a.N + kBC - 1) / kBC;
+    if (a.N % kBC != 0) {
+        switch (ntiles) {
+            case 1: launch_keep_inst<NT, BK, 1, FUSED, true>(a, s); break;
+            case 2: launch_keep_inst<NT, BK, 2, FUSED, true>(a, s); break;
+            case 3: launch_keep_inst<NT, BK, 3, FUSED, true>(a, s); break;
+            default: launch_keep_inst<NT, BK, 4, FUSED, true>(a, s); break;
+        }
+    } else {
+        switch (ntiles) {
+            case 1: launch_keep_inst<NT, BK, 1, FUSED, false>(a, s); break;
+            case 2: launch_keep_inst<NT, BK, 2, FUSED, false>(a, s); break;
+            case 3: launch_keep_inst<NT, BK, 3, FUSED, false>(a, s); break;
+            default: launch_keep_inst<NT, BK, 4, FUSED, false>(a, s); break;
+        }
+    }
 }
 
 }  // namespace binattn

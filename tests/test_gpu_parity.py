@@ -228,6 +228,13 @@ SMALL = [
     (1, 2, 197, 64, "f32", "dense", ()),
     (2, 2, 256, 72, "f16", "relpos", (16, 16)),
     (1, 2, 384, 64, "f16", "relpos", (12, 32)),
+    # 5..10 tiles, d <= 64: the head-resident kernel for long rows (ragged and whole last tiles)
+    (1, 2, 300, 64, "f16", "dense", ()),
+    (2, 1, 320, 64, "f32", "none", ()),
+    (1, 1, 577, 64, "f16", "none", ()),
+    (1, 1, 600, 48, "f32", "dense", ()),
+    (1, 2, 640, 32, "f16", "dense", ()),
+    (1, 1, 641, 64, "f16", "dense", ()),
     (1, 1, 577, 128, "f16", "dense", ()),
     (1, 2, 1024, 96, "f32", "relpos", (8, 128)),
     (1, 1, 2400, 64, "f16", "relpos", (15, 160)),
