@@ -5,12 +5,9 @@
 // keeps the magnitude.  mu is taken as mean |x| over the d channels.
 //
 // HBM-bound: a token is read once (2d or 4d bytes) and 4*ceil(d/32) + 4 bytes are
-// written.  A workgroup owns T = floor(256 / (d/8)) consecutive tokens -- a
-// contiguous span of memory -- and each thread loads one 8-channel chunk of it, so
-// every load instruction is contiguous and the launch has enough waves to hide
-// memory latency.  Per chunk a thread forms one byte of sign bits and a partial
-// |x| sum; the bytes and partial sums meet in LDS, where thread t assembles token
-// t's words and mu in channel order.
+// written.  One thread per token: its 16-byte chunks are loaded together (the 64 lanes of a
+// wave cover 64 consecutive tokens, so the loads of one wave cover one contiguous span), the
+// sign words and mu are formed in registers and stored directly -- no LDS, no barrier.
 #include "common.h"
 #include "internal.h"
 #include "prep.h"
@@ -20,15 +17,13 @@ namespace binattn {
 template <typename T>
 __global__ __launch_bounds__(256) void pack_qk_kernel(const T* __restrict__ x, int64_t ntok, int d, int W,
                                                       uint32_t* __restrict__ bits, float* __restrict__ mu) {
-    __shared__ __attribute__((aligned(16))) uint8_t sBits[256 * 16];  // 16 sign bytes per token
-    __shared__ float sSum[256];                                        // partial |x| sum per chunk
-    pack_block<T>(x, ntok, d, W, bits, mu, blockIdx.x, sBits, sSum);
+    pack_wave<T>(x, ntok, d, W, bits, mu, (int64_t)blockIdx.x);
 }
 
 hipError_t launch_pack_qk(const void* x, int f32, int64_t ntok, int d, uint32_t* bits, float* mu,
                           hipStream_t s) {
     const int W = (d + 31) / 32;
-    const dim3 block(256), grid((unsigned)pack_blocks<float>(ntok, d));
+    const dim3 block(256), grid((unsigned)pack_blocks(ntok));
     if (f32)
         hipLaunchKernelGGL(pack_qk_kernel<float>, grid, block, 0, s, (const float*)x, ntok, d, W, bits, mu);
     else

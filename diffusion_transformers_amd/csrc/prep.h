@@ -8,6 +8,8 @@
 //                 channel's absmax over the tokens of one (batch, head).
 #pragma once
 
+#include <algorithm>
+
 #include "common.h"
 
 namespace binattn {
@@ -44,81 +46,73 @@ __device__ __forceinline__ void chunk_sign_abs(const h8& x, uint32_t& byte, floa
     sum = acc;
 }
 
-// Sign words and mu of the tokens of workgroup `blk`: kPackSub contiguous spans of
-// floor(256 / (d/8)) tokens, one 8-channel chunk (16 or 32 bytes) per thread and span.  All of
-// a thread's chunk loads are issued first (enough bytes in flight per compute unit to stream
-// at HBM rate); then per span each chunk yields one sign byte and a partial |x| sum, which meet
-// in LDS, where thread t assembles token t's words and mu in channel order.
-// sBits: 256*16 bytes, sSum: 256 floats.
-constexpr int kPackSub = 16;
-
+// Sign words and mu of one token per thread: token 256 blk + 64 wave + lane (tokens >= ntok read
+// as zero and are not written).  All of the token's 16-byte chunks are
+// loaded first; each 8-channel chunk then gives one sign byte and a partial |x| sum
+// (chunk_sign_abs for fp16; channel order for fp32), and the partial sums add up in channel
+// order.  No LDS and no barrier: a workgroup is four independent waves.
 template <typename T>
-__host__ __device__ inline int64_t pack_blocks(int64_t ntok, int d) {
-    const int ntw = 256 / (d / 8);
-    return (ntok + (int64_t)ntw * kPackSub - 1) / ((int64_t)ntw * kPackSub);
-}
-
-template <typename T>
-__device__ __forceinline__ void pack_block(const T* __restrict__ x, int64_t ntok, int d, int W,
-                                           uint32_t* __restrict__ bits, float* __restrict__ mu, int64_t blk,
-                                           uint8_t* sBits, float* sSum) {
-    typedef T vec8 __attribute__((ext_vector_type(8)));  // one chunk: 8 channels
-    const int tid = threadIdx.x;
-    const int cpt = d >> 3;                               // chunks per token
-    const int ntw = 256 / cpt;                            // tokens per span
-    const int t = tid / cpt, part = tid - t * cpt;
-    vec8 v[kPackSub];
+__device__ __forceinline__ void pack_wave(const T* __restrict__ x, int64_t ntok, int d, int W,
+                                          uint32_t* __restrict__ bits, float* __restrict__ mu, int64_t blk) {
+    constexpr int ES = sizeof(T);
+    constexpr int LPC = 8 * ES / 16;  // 16-byte loads per 8-channel chunk
+    constexpr int MAXC = 16;          // chunks of d <= 128
+    const int lane = threadIdx.x & 63;
+    const int64_t tok0 = blk * 256 + 64 * __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int cpt = d >> 3;
+    const int64_t left = ntok - tok0;
+    const int ntw = left < 64 ? (int)left : 64;
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x + tok0 * d, ntw * d * ES);
+    const int off = lane * d * ES;
+    uint4 v[MAXC * LPC];
 #pragma unroll
-    for (int u = 0; u < kPackSub; ++u) {
-        const int64_t tok = (blk * kPackSub + u) * ntw + t;
-        if (t < ntw && tok < ntok) {
-            v[u] = *reinterpret_cast<const vec8*>(x + tok * d + 8 * part);
-        } else {
+    for (int c = 0; c < MAXC; ++c)
+        if (c < cpt) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[u][e] = (T)0;
+            for (int l = 0; l < LPC; ++l)
+                v[c * LPC + l] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16 * (c * LPC + l), 0, 0));
         }
-    }
+    uint32_t words[4] = {0u, 0u, 0u, 0u};
+    float acc = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kPackSub; ++u) {
-        const int64_t t0 = (blk * kPackSub + u) * ntw;
-        uint32_t byte = 0;
-        float sum = 0.0f;
-        if constexpr (sizeof(T) == 2) {
-            chunk_sign_abs(v[u], byte, sum);
-        } else {
+    for (int c = 0; c < MAXC; ++c) {
+        if (c < cpt) {
+            uint32_t byte = 0;
+            float sum = 0.0f;
+            if constexpr (ES == 2) {
+                chunk_sign_abs(__builtin_bit_cast(h8, v[c]), byte, sum);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float f = (float)v[u][e];
-                byte |= (f >= 0.0f ? 1u : 0u) << e;  // -0.0 >= 0 holds: zero counts as +1
-                sum += fabsf(f);
+                for (int e = 0; e < 8; ++e) {
+                    const uint4 q = v[c * LPC + e / 4];
+                    const float f = __uint_as_float(e % 4 == 0 ? q.x : e % 4 == 1 ? q.y : e % 4 == 2 ? q.z : q.w);
+                    byte |= (f >= 0.0f ? 1u : 0u) << e;  // -0.0 >= 0 holds: zero counts as +1
+                    sum += fabsf(f);
+                }
             }
+            words[c >> 2] |= byte << (8 * (c & 3));
+            acc += sum;
         }
-        // bytes past the token's d channels read as zero
-        reinterpret_cast<uint4*>(sBits)[tid] = make_uint4(0, 0, 0, 0);
-        __syncthreads();
-        if (t < ntw) {
-            sBits[t * 16 + part] = (uint8_t)byte;
-            sSum[tid] = sum;  // tid == t * cpt + part
+    }
+    if (lane < ntw) {
+        const int64_t tok = tok0 + lane;
+        uint32_t* out = bits + tok * W;
+        switch (W) {
+            case 1: out[0] = words[0]; break;
+            case 2: *reinterpret_cast<uint2*>(out) = make_uint2(words[0], words[1]); break;
+            case 3: out[0] = words[0]; out[1] = words[1]; out[2] = words[2]; break;
+            default: *reinterpret_cast<uint4*>(out) = make_uint4(words[0], words[1], words[2], words[3]); break;
         }
-        __syncthreads();
-        if (tid < ntw && t0 + tid < ntok) {
-            const int64_t o = t0 + tid;
-            const uint4 w = reinterpret_cast<const uint4*>(sBits)[tid];
-            uint32_t* out = bits + o * W;
-            out[0] = w.x;
-            if (W > 1) out[1] = w.y;
-            if (W > 2) out[2] = w.z;
-            if (W > 3) out[3] = w.w;
-            float acc = 0.0f;
-            for (int p = 0; p < cpt; ++p) acc += sSum[tid * cpt + p];
-            mu[o] = acc / (float)d;
-        }
-        __syncthreads();  // the LDS is reused by the next span
+        mu[tok] = acc / (float)d;
     }
 }
 
-constexpr int kQuantTS = 64 + 4;  // LDS row stride (bytes) of the 64-token transpose tile: 17 dwords, so
-                                  // rows of consecutive channels fall in different banks
+// Workgroups of 256 tokens (four waves of 64) over ntok tokens.
+__host__ __device__ inline int64_t pack_blocks(int64_t ntok) { return (ntok + 255) / 256; }
+
+constexpr int kQuantTB = 128;     // tokens per block of the transpose tile
+constexpr int kQuantTS = 128 + 4;  // LDS row stride (bytes) of that tile: 33 dwords, so rows of
+                                   // consecutive channels fall in different banks
 
 template <typename T>
 struct QuantVec {
@@ -148,12 +142,12 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&in)[4], uint32_t (
 }
 
 // Channel-wise int8 quantisation of one head with its V held in registers (MAXC chunks per
-// thread, in groups of 4 consecutive tokens): absmax per channel (registers, then LDS across
-// thread groups), IEEE 127 / a, rint, clamp to +-127 -- every chunk quantised in registers --
-// then per 64-token block each 4-token group is transposed in registers (v_perm) into one
-// dword per channel, written to an LDS tile of channel rows, and stored as 16-byte rows of
-// ldv keys; tokens >= N are written as 0.  sRed: 256*VE floats, sAmax: 128 floats,
-// sT: 128 * kQuantTS bytes (16-byte aligned).
+// thread, in groups of 4 consecutive tokens): absmax per channel (registers; then the 256
+// threads reduce the per-thread maxima, 256/d threads per channel, meeting in an LDS max),
+// IEEE 127 / a, rint -- every chunk quantised in registers -- then per 128-token block each
+// 4-token group is transposed in registers (v_perm) into one dword per channel, written to an
+// LDS tile of channel rows, and stored as rows of ldv keys; tokens >= N are written as 0.
+// sRed: 256*VE floats, sAmax: 128 words, sT: 128 * kQuantTS bytes (16-byte aligned).
 template <typename T, int MAXC>
 __device__ __forceinline__ void quant_head_regs(const T* __restrict__ v, int N, int d, int64_t ldv, int64_t bh,
                                                 int8_t* __restrict__ vq, float* __restrict__ vamax, float* sRed,
@@ -166,6 +160,8 @@ __device__ __forceinline__ void quant_head_regs(const T* __restrict__ v, int N, 
     const int P = d / VE, G = 256 / P;
     const int part = tid % P, grp = tid / P;
     const T* vh = v + bh * (int64_t)N * d;
+    uint32_t* sAmaxU = reinterpret_cast<uint32_t*>(sAmax);
+    if (tid < 128) sAmaxU[tid] = 0u;  // the max of non-negative floats, compared as their bit patterns
     vecT x[MAXC];
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
@@ -188,17 +184,21 @@ __device__ __forceinline__ void quant_head_regs(const T* __restrict__ v, int N, 
         for (int e = 0; e < VE; ++e) sRed[grp * d + part * VE + e] = (float)mv[e];
     }
     __syncthreads();
-    if (tid < d) {
-        float a = 0.0f;
-        for (int g = 0; g < G; ++g) a = fmaxf(a, sRed[g * d + tid]);
-        vamax[bh * d + tid] = a;
-        sAmax[tid] = a;
+    {
+        const int K = 256 / d;  // threads per channel
+        if (tid < K * d) {
+            const int c = tid % d, s0 = tid / d;
+            float a = 0.0f;
+            for (int g = s0; g < G; g += K) a = fmaxf(a, sRed[g * d + c]);
+            atomicMax(&sAmaxU[c], __float_as_uint(a));
+        }
     }
     __syncthreads();
+    if (tid < d) vamax[bh * d + tid] = __uint_as_float(sAmaxU[tid]);
     float inv[VE];
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
-        const float a = grp < G ? sAmax[part * VE + e] : 0.0f;
+        const float a = grp < G ? __uint_as_float(sAmaxU[part * VE + e]) : 0.0f;
         inv[e] = a > 0.0f ? 127.0f / a : 0.0f;
     }
     // quantise every chunk and transpose each 4-token group: qt[u][e] = channel part*VE+e,
@@ -230,10 +230,10 @@ __device__ __forceinline__ void quant_head_regs(const T* __restrict__ v, int N, 
         }
     }
     int8_t* vqh = vq + bh * d * ldv;
-    const int nblk = (int)(ldv / 64);
-    for (int jb = 0; jb < nblk; ++jb) {
-        const int j0 = jb * 64;
-        if (j0 + 64 > N) {  // ragged last block: positions past N stay 0
+    for (int j0 = 0; j0 < ldv; j0 += kQuantTB) {
+        const int nb = (int)std::min<int64_t>(kQuantTB, ldv - j0);  // 64 or 128 keys
+        if (j0 > 0) __syncthreads();  // the previous block's tile has been stored
+        if (j0 + nb > N) {  // ragged last block: positions past N stay 0
             for (int id = tid; id < 128 * kQuantTS / 16; id += 256) reinterpret_cast<uint4*>(sT)[id] = make_uint4(0, 0, 0, 0);
             __syncthreads();
         }
@@ -241,7 +241,7 @@ __device__ __forceinline__ void quant_head_regs(const T* __restrict__ v, int N, 
 #pragma unroll
             for (int u = 0; u < MAXU; ++u) {
                 const int n0 = 4 * (grp + G * u);  // first token of the group (tokens past N hold 0)
-                if (n0 >= j0 && n0 < j0 + 64 && n0 < N) {
+                if (n0 >= j0 && n0 < j0 + nb && n0 < N) {
 #pragma unroll
                     for (int e = 0; e < VE; ++e)
                         *reinterpret_cast<uint32_t*>(sT + (part * VE + e) * kQuantTS + (n0 - j0)) = qt[u][e];
@@ -249,12 +249,12 @@ __device__ __forceinline__ void quant_head_regs(const T* __restrict__ v, int N, 
             }
         }
         __syncthreads();
-        for (int id = tid; id < d * 16; id += 256) {  // one dword per thread: c = id / 16, keys 4*(id%16)..
-            const int c = id >> 4, q = id & 15;
+        const int dw = nb / 4;  // dwords per row
+        for (int id = tid; id < d * dw; id += 256) {
+            const int c = id / dw, q = id - c * dw;
             *reinterpret_cast<uint32_t*>(vqh + (int64_t)c * ldv + j0 + 4 * q) =
                 *reinterpret_cast<const uint32_t*>(sT + c * kQuantTS + 4 * q);
         }
-        __syncthreads();
     }
 }
 

@@ -20,8 +20,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
                                                    float* __restrict__ qmu, uint32_t* __restrict__ kbits,
                                                    float* __restrict__ kmu, int8_t* __restrict__ vq,
                                                    float* __restrict__ vamax) {
-    // LDS shared by the two roles: quantise uses sRed (8 KB) + sAmax + the transpose tile,
-    // pack uses the sign bytes and partial sums.
+    // LDS of the quantise role: sRed (8 KB) + sAmax + the transpose tile (packing uses none).
     __shared__ __attribute__((aligned(16))) uint8_t smem[2048 * 4 + 128 * 4 + 128 * kQuantTS];
     const int64_t b = blockIdx.x;
     const int64_t span = (int64_t)R * BH;  // blocks [0, span): head b / R where b % R == 0
@@ -31,13 +30,11 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
         return;
     }
     const int64_t ntok = (int64_t)BH * N;
-    uint8_t* sBits = smem;
-    float* sSum = reinterpret_cast<float*>(smem + 256 * 16);
     const int64_t pb = b < span ? b - (b + R - 1) / R : b - BH;  // minus the heads placed before b
     if (pb < npack)
-        pack_block<T>(q, ntok, d, W, qbits, qmu, pb, sBits, sSum);
+        pack_wave<T>(q, ntok, d, W, qbits, qmu, pb);
     else
-        pack_block<T>(k, ntok, d, W, kbits, kmu, pb - npack, sBits, sSum);
+        pack_wave<T>(k, ntok, d, W, kbits, kmu, pb - npack);
 }
 
 template <typename T>
@@ -46,7 +43,7 @@ static hipError_t launch_prepare_t(const T* q, const T* k, const T* v, int BH, i
                                    float* vamax, hipStream_t s) {
     const int W = (d + 31) / 32;
     const int64_t ntok = (int64_t)BH * N;
-    const int64_t npack = pack_blocks<T>(ntok, d);
+    const int64_t npack = pack_blocks(ntok);
     const int nc = quant_chunks_per_thread<T>(N, d);
     const int64_t nblocks = BH + 2 * npack;
     if (nblocks <= 0x7fffffff && nc <= 20) {

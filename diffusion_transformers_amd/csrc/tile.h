@@ -412,7 +412,7 @@ __device__ __forceinline__ void stage_common(const FwdArgs& a, int bh, float* sS
 // dequantisation scales and int8 V^ written straight into the operand rows (V held in
 // registers in groups of 4 tokens, transposed with v_perm); the Q of the workgroup's query
 // blocks -> sign word g and mu_q per lane (sQw, sQmu).  The arithmetic is that of
-// pack_block and quant_head_regs -- the same comparisons, the same fp32 summation order for
+// pack_wave and quant_head_regs -- the same comparisons, the same fp32 summation order for
 // mu, the same IEEE 127/a and rint -- so the results equal the separate path bit for bit.
 // sRed: 2048 floats; sInv: 128 floats; sCol: 128 * sum_j V^_jc per channel slot (16 NT).
 template <int NT, int NTL>
@@ -461,7 +461,7 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
     }
     __syncthreads();  // the zero fill is complete before any operand row is written
 
-    // ---- K: sign bytes and partial |x| sums per chunk, words, mu_k (pack_block's order)
+    // ---- K: sign bytes and partial |x| sums per chunk, words, mu_k (pack_wave's order)
     if (j < NTL * kBC) {
         uint32_t words[W];
 #pragma unroll
