@@ -1,20 +1,21 @@
 """Benchmark of the BinaryAttention forward hot path on one MI355X.
 
-A step is one pass of the whole hot path over one batch: sign-pack Q, sign-pack
-K, quantise V (one preparation launch), fused forward -- binattn_attention through
-the C ABI.  The default
-workload is DeiT-S 224^2 (B=64, H=6, N=197, d=64, fp16, dense per-head bias);
-``--workload`` selects another named shape.  Inputs are seeded synthetic
-activations (diffusion_transformers_amd/workloads.py) already resident in HBM;
-``--rotate`` input sets are cycled so the 256 MB last-level cache does not hold
-the step's working set.
+A step is one pass of the whole hot path over one batch: sign-pack Q and K, quantise V,
+the forward -- binattn_attention through the C ABI, which runs either as one kernel
+straight from fp16 Q, K, V (rows of at most 256 keys) or as the preparation launch
+followed by the forward from packed inputs.  The default workload is DeiT-S 224^2
+(B=64, H=6, N=197, d=64, fp16, dense per-head bias); ``--workload`` selects another named
+shape.  Inputs are seeded synthetic activations (diffusion_transformers_amd/workloads.py)
+already resident in HBM; ``--rotate`` input sets are cycled so the 256 MB last-level cache
+does not hold the step's working set.
 
-Prints ONE JSON line.  value = effective TOPS of the step, counting
-2*B*H*N^2*d for QK^T plus the same for PV.  The roofline object is for the
-dominant kernel (the fused forward): algorithmic bytes per launch over its
-average launch time measured with HIP events on the launch stream, against the
-binding roofline of the two the method names (int8 MFMA 5.0 POPS, HBM 8 TB/s).
-cpu_baseline times the CPU oracle (whole hot path) on the host cores.
+Prints ONE JSON line.  value = effective TOPS of the step, counting 2*B*H*N^2*d for QK^T
+plus the same for PV.  The roofline object is for the step's dominant kernel (the one
+kernel, or the forward from packed inputs): algorithmic bytes per launch over its average
+launch time measured with HIP events on the launch stream, against the binding roofline of
+the two the method names (int8 MFMA 5.0 POPS, HBM 8 TB/s).  fwd_ms_per_call times the
+forward from packed inputs alone.  cpu_baseline times the CPU oracle (whole hot path) on
+the host cores.
 """
 from __future__ import annotations
 
@@ -31,7 +32,18 @@ sys.path.insert(0, ROOT)
 METRIC = "binary-attention fwd ms/call & effective TOPS; % of int8 MFMA peak (1 GPU)"
 HBM_PEAK_GBS = 8000.0
 I8_PEAK_TOPS = 5000.0
-FWD_SOURCE = os.path.join(ROOT, "diffusion_transformers_amd", "csrc", "forward.hip")
+CSRC = os.path.join(ROOT, "diffusion_transformers_amd", "csrc")
+
+
+def bias_bytes(w) -> float:
+    """Bias bytes read once per launch: the dense [H,N,N] bias (shared over the batch) or the tables."""
+    esz = 2 if w.dtype == "f16" else 4
+    if w.bias == "dense":
+        return float(w.H * w.N * w.N * esz)
+    if w.bias == "relpos":
+        gh, gw = w.grid
+        return float(w.H * (2 * gh - 1) * (2 * gw - 1) * esz)
+    return 0.0
 
 
 def fwd_bytes(w) -> float:
@@ -43,15 +55,14 @@ def fwd_bytes(w) -> float:
     vq = B * H * N * d                      # int8 V^
     vs = B * H * d * 4                      # V scales
     esz = 2 if w.dtype == "f16" else 4
-    if w.bias == "dense":
-        bias = H * N * N * esz              # shared over the batch
-    elif w.bias == "relpos":
-        gh, gw = w.grid
-        bias = H * (2 * gh - 1) * (2 * gw - 1) * esz
-    else:
-        bias = 0
     out = B * H * N * d * esz
-    return float(bits + mu + vq + vs + bias + out)
+    return float(bits + mu + vq + vs + out) + bias_bytes(w)
+
+
+def one_kernel_bytes(w) -> float:
+    """Algorithmic HBM bytes of the one-kernel step: Q, K, V read once, the bias once, O written once."""
+    esz = 2 if w.dtype == "f16" else 4
+    return float(4 * w.B * w.H * w.N * w.d * esz) + bias_bytes(w)
 
 
 def step_bytes(w) -> float:
@@ -64,10 +75,20 @@ def step_bytes(w) -> float:
     return float(pack + quant + fwd_bytes(w))
 
 
-def stored_traffic(workload: str):
-    """HBM traffic per forward launch from the committed rocprofv3 PMC summary, or None when
-    that summary was taken on a different forward kernel source."""
-    path = os.path.join(ROOT, "profiles", f"forward_{workload}_hbm_traffic.txt")
+def sources_sha() -> str:
+    """sha256 (first 16 hex digits) over the kernel sources, in name order."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, kernel_tag: str):
+    """HBM traffic per launch of the dominant kernel from the committed rocprofv3 PMC summary,
+    or None when that summary was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -75,8 +96,7 @@ def stored_traffic(workload: str):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(FWD_SOURCE, "rb").read()).hexdigest()[:16]
-    if kv.get("forward_source_sha256_16") != sha or "traffic_bytes_per_launch" not in kv:
+    if kv.get("sources_sha256_16") != sources_sha() or "traffic_bytes_per_launch" not in kv:
         return None
     return float(kv["traffic_bytes_per_launch"])
 
@@ -246,23 +266,31 @@ def main():
     eager_ms = timed(lambda: [step(st) for st in sets], reps) / steps
 
     ops = w.ops()
-    fb = fwd_bytes(w)
+    one = b.attention_one_kernel(w.B, w.H, w.N, w.d, sets[0]["q"].dtype, sets[0]["kind"],
+                                 None if sets[0]["bias"] is None else sets[0]["bias"].dtype, sets[0]["grid"])
+    if one:  # the step is one launch of the whole-attention kernel
+        kernel, tag, kb, ks = ("binattn_fwd_keep_kernel (whole attention from fp16 Q, K, V)", "attention",
+                               one_kernel_bytes(w), step_ms * 1e-3)
+    else:    # the forward from packed inputs dominates the step
+        kernel, tag, kb, ks = ("binattn_fwd_keep_kernel (forward from packed inputs)", "forward", fwd_bytes(w),
+                               fwd_ms * 1e-3)
     t_mfma = ops / (I8_PEAK_TOPS * 1e12)
-    t_hbm = fb / (HBM_PEAK_GBS * 1e9)
-    fwd_s = fwd_ms * 1e-3
+    t_hbm = kb / (HBM_PEAK_GBS * 1e9)
     if t_hbm >= t_mfma:
-        achieved = fb / fwd_s / 1e9
+        achieved = kb / ks / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
     else:
-        achieved = ops / fwd_s / 1e12
+        achieved = ops / ks / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": I8_PEAK_TOPS, "unit": "TOPS",
                 "frac": achieved / I8_PEAK_TOPS}
-    roof["traffic"] = stored_traffic(w.name)
-    roof["kernel"] = "binattn_fwd_kernel"
-    roof["algorithmic_bytes_per_launch"] = fb
-    roof["mfma_frac"] = ops / fwd_s / 1e12 / I8_PEAK_TOPS
-    roof["hbm_frac"] = fb / fwd_s / 1e9 / HBM_PEAK_GBS
+    roof["traffic"] = stored_traffic(w.name, tag)
+    roof["kernel"] = kernel
+    roof["algorithmic_bytes_per_launch"] = kb
+    roof["launch_us"] = ks * 1e6
+    roof["mfma_frac"] = ops / ks / 1e12 / I8_PEAK_TOPS
+    roof["hbm_frac"] = kb / ks / 1e9 / HBM_PEAK_GBS
+    fwd_s = fwd_ms * 1e-3
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -283,6 +311,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "input_dtype": w.dtype,
                    "bias": w.bias, "rotated_input_sets": len(sets)},
+        "path": "one kernel" if one else "prepare + forward",
         "fwd_ms_per_call": fwd_ms,
         "eager_ms_per_step": eager_ms,
         "timing": "HIP events around graph replays; one graph = one step per rotated input set",

@@ -56,13 +56,15 @@ def _load():
     lib.binattn_attention.argtypes = [vp, vp, vp, i32, i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, vp, i32, vp,
                                       i64, vp]
     lib.binattn_attention.restype = i32
+    lib.binattn_attention_one_kernel.argtypes = [i32] * 9
+    lib.binattn_attention_one_kernel.restype = i32
     return lib
 
 
 _lib = _load()
 EXPORTS = ["binattn_abi_version", "binattn_strerror", "binattn_words", "binattn_vq_ld", "binattn_pack_qk",
            "binattn_quant_v", "binattn_forward", "binattn_scores_i32", "binattn_qk_rowstats",
-           "binattn_prepare", "binattn_attention_workspace", "binattn_attention"]
+           "binattn_prepare", "binattn_attention_workspace", "binattn_attention", "binattn_attention_one_kernel"]
 QK_MFMA, QK_POPCOUNT = 0, 1
 
 
@@ -201,6 +203,17 @@ def attention_workspace(B, H, N, d, device):
     if n < 0:
         raise BinAttnError("binattn_attention_workspace", -2)
     return torch.empty((n,), dtype=torch.uint8, device=device)
+
+
+def attention_one_kernel(B, H, N, d, dtype, bias_kind=BIAS_NONE, bias_dtype=None, grid=None):
+    """Whether attention() on these shapes runs as one kernel (True) or as prepare + forward."""
+    gh, gw = grid if grid else (0, 0)
+    bdt = F16 if bias_dtype is None else (F32 if bias_dtype == torch.float32 else F16)
+    dt = F32 if dtype == torch.float32 else F16
+    rc = _lib.binattn_attention_one_kernel(dt, bias_kind, bdt, gh, gw, B, H, N, d)
+    if rc < 0:
+        raise BinAttnError("binattn_attention_one_kernel", rc)
+    return rc == 1
 
 
 def attention(q, k, v, bias=None, bias_kind=BIAS_NONE, grid=None, out_dtype=None, out=None, workspace=None):

@@ -203,6 +203,24 @@ int64_t binattn_attention_workspace(int B, int H, int N, int d) {
     return workspace_layout(B, H, N, d).total;
 }
 
+int binattn_attention_one_kernel(int dtype, int bias_kind, int bias_dtype, int grid_h, int grid_w, int B, int H, int N,
+                                 int d) {
+    int rc = check_dims(B, H, N, d);
+    if (rc) return rc;
+    if (!dtype_ok(dtype)) return BINATTN_EUNSUPPORTED;
+    if (bias_kind < BINATTN_BIAS_NONE || bias_kind > BINATTN_BIAS_RELPOS) return BINATTN_EUNSUPPORTED;
+    if (bias_kind != BINATTN_BIAS_NONE && !dtype_ok(bias_dtype)) return BINATTN_EUNSUPPORTED;
+    if (bias_kind == BINATTN_BIAS_RELPOS) {  // as check_bias
+        if (grid_h <= 0 || grid_w <= 0 || (int64_t)grid_h * grid_w != N) return BINATTN_EINVAL;
+        if (grid_w % 16 != 0 || !relpos_window_fits(grid_w)) return BINATTN_EUNSUPPORTED;
+    }
+    if (dtype != BINATTN_F16) return 0;
+    FwdArgs f = {};
+    f.B = B; f.H = H; f.N = N; f.d = d; f.gh = grid_h; f.gw = grid_w;
+    f.bias_f32 = bias_dtype == BINATTN_F32;
+    return attention_fused_applies(f, bias_kind) ? 1 : 0;
+}
+
 int binattn_attention(const void* q, const void* k, const void* v, int dtype, int bias_kind, int bias_dtype,
                       const void* bias, int64_t bias_ld, int grid_h, int grid_w, int B, int H, int N, int d,
                       void* out, int out_dtype, void* workspace, int64_t workspace_bytes, void* stream) {

@@ -23,9 +23,15 @@ static hipError_t launch_fused_nt(const FwdArgs& a, int bk, hipStream_t s) {
     }
 }
 
-hipError_t launch_attention_fused(const FwdArgs& a, int bias_kind, hipStream_t s) {
+bool attention_fused_applies(const FwdArgs& a, int bias_kind) {
     const int ntiles = (a.N + kBC - 1) / kBC;
-    if (ntiles > kKeepTiles || (bias_kind == 2 && !keep_window_fits(a))) return hipErrorNotSupported;
+    if (ntiles > kKeepTiles || (bias_kind == 2 && !keep_window_fits(a))) return false;
+    const int nt = (a.d + 15) / 16;
+    return nt == 4 || nt == 5 || nt == 8;
+}
+
+hipError_t launch_attention_fused(const FwdArgs& a, int bias_kind, hipStream_t s) {
+    if (!attention_fused_applies(a, bias_kind)) return hipErrorNotSupported;
     int bk = BK_NONE;
     if (bias_kind == 1) bk = a.bias_f32 ? BK_DENSE_F32 : BK_DENSE_F16;
     if (bias_kind == 2) bk = BK_RELPOS;

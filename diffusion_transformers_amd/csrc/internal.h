@@ -39,6 +39,7 @@ hipError_t launch_forward(const FwdArgs& a, int bias_kind, hipStream_t s);
 // Whole attention from fp16 Q, K, V in one kernel where the shape allows it (short rows);
 // returns hipErrorNotSupported, launching nothing, where it does not.
 hipError_t launch_attention_fused(const FwdArgs& a, int bias_kind, hipStream_t s);
+bool attention_fused_applies(const FwdArgs& a, int bias_kind);
 hipError_t launch_scores(const FwdArgs& a, hipStream_t s);
 hipError_t launch_qk_stats(const FwdArgs& a, int method, float* rowmax, float* rowsum, hipStream_t s);
 bool relpos_window_fits(int gw);

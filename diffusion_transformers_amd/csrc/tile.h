@@ -414,11 +414,13 @@ __device__ __forceinline__ void stage_common(const FwdArgs& a, int bh, float* sS
 // blocks -> sign word g and mu_q per lane (sQw, sQmu).  The arithmetic is that of
 // pack_wave and quant_head_regs -- the same comparisons, the same fp32 summation order for
 // mu, the same IEEE 127/a and rint -- so the results equal the separate path bit for bit.
-// sRed: 2048 floats; sInv: 128 floats; sCol: 128 * sum_j V^_jc per channel slot (16 NT).
+// sRed: 2048 floats; sInv, sAmx: 128 words; sCol: 128 * sum_j V^_jc per channel slot (16 NT).
+// The per-channel reductions (absmax, column sum) take 256/d threads per channel, which meet in
+// an LDS max / add.
 template <int NT, int NTL>
 __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo, int nitems, TileLds<NT, 4>* lds,
                                             float* sScale, uint32_t* sQw, float* sQmu, float* sRed,
-                                            float* sInv, int* sCol) {
+                                            float* sInv, uint32_t* sAmx, int* sCol) {
     constexpr int W = (NT + 1) / 2;
     constexpr int MAXCK = 2 * NT;  // 8-channel chunks of one key (d <= 16 NT)
     constexpr int MAXC = 16;       // V chunks per thread: 4 * ceil(64 / G) with G = 256 / (d/8) >= 16
@@ -427,6 +429,10 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
     // operand padding (keys >= N, channel slots >= d) stays zero
     for (int id = tid; id < NTL * NT * 64; id += 256)
         reinterpret_cast<uint4*>(lds[id / (NT * 64)].v)[id % (NT * 64)] = make_uint4(0, 0, 0, 0);
+    if (tid < 128) {
+        sAmx[tid] = 0u;  // max of non-negative floats, compared as bit patterns
+        sCol[tid] = 0;
+    }
 
     // ---- all K, V and Q loads of the head in flight together.  Buffer loads: rows past N read
     // as zero and no load sits under a lane-dependent branch (so no load is waited for early).
@@ -501,10 +507,16 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
         for (int e = 0; e < 8; ++e) sRed[grp * d + part * 8 + e] = (float)mv[e];
     }
     __syncthreads();
-    if (tid < 128) {
+    const int K = 256 / d;  // threads per channel in the reductions
+    if (tid < K * d) {
+        const int c = tid % d;
         float av = 0.0f;
-        if (tid < d)
-            for (int gi = 0; gi < G; ++gi) av = fmaxf(av, sRed[gi * d + tid]);
+        for (int gi = tid / d; gi < G; gi += K) av = fmaxf(av, sRed[gi * d + c]);
+        atomicMax(&sAmx[c], __float_as_uint(av));
+    }
+    __syncthreads();
+    if (tid < 128) {
+        const float av = __uint_as_float(sAmx[tid]);
         sScale[tid] = tid < d ? av / 127.0f : 0.0f;  // dequantisation scale, as fp32 a/127
         sInv[tid] = av > 0.0f ? 127.0f / av : 0.0f;
     }
@@ -553,17 +565,18 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
         }
     }
 
-    // column sums: partial sums through sRed (the absmax pass is done with it), then one thread per slot
+    // column sums: partial sums through sRed (the absmax pass is done with it); integers, so the
+    // order of the additions does not matter
     if (grp < G) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) sRed[grp * d + part * 8 + e] = vsum[e];
     }
     __syncthreads();
-    if (tid < NT * 16) {
-        float cs = 0.0f;
-        if (tid < d)
-            for (int gi = 0; gi < G; ++gi) cs += sRed[gi * d + tid];
-        sCol[tid] = 128 * (int)cs;
+    if (tid < K * d) {
+        const int c = tid % d;
+        int cs = 0;
+        for (int gi = tid / d; gi < G; gi += K) cs += (int)sRed[gi * d + c];
+        atomicAdd(&sCol[c], 128 * cs);
     }
 
     // ---- Q of every query block of this workgroup: word g of the signs and mu_q per lane
@@ -624,6 +637,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
     __shared__ __attribute__((aligned(16))) float sQmu[FUSED ? kKeepTiles * kWaves * 16 : 1];
     __shared__ __attribute__((aligned(16))) float sRed[FUSED ? 2048 : 1];
     __shared__ __attribute__((aligned(16))) float sInv[FUSED ? 128 : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t sAmx[FUSED ? 128 : 1];
 
     const int N = a.N, d = a.d;
     const int nqb = (N + kBR - 1) / kBR;
@@ -691,7 +705,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
 
     // ---- stage the head once (all loads in flight together), then the first block's inputs
     if constexpr (FUSED) {
-        fused_stage<NT, NTL>(a, bh, qb_lo, qb_hi - qb_lo, lds, sScale, sQw, sQmu, sRed, sInv, sCol);
+        fused_stage<NT, NTL>(a, bh, qb_lo, qb_hi - qb_lo, lds, sScale, sQw, sQmu, sRed, sInv, sAmx, sCol);
         __syncthreads();  // the prepared query words are read by load_query below
     } else {
         Regs regs[NTL];

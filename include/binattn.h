@@ -173,9 +173,13 @@ int binattn_prepare(const void* q, const void* k, const void* v, int dtype, int 
                     void* stream);
 
 /*
- * binattn_attention -- the whole forward from fp16/fp32 Q, K, V: binattn_prepare into
- * the caller's workspace, then binattn_forward.  The pages present the method as a
- * drop-in replacement of attention; this is that call.
+ * binattn_attention -- the whole forward from fp16/fp32 Q, K, V, with results identical bit
+ * for bit to binattn_prepare into the caller's workspace followed by binattn_forward.  The
+ * pages present the method as a drop-in replacement of attention; this is that call.  For
+ * fp16 inputs with rows of at most 256 keys, d of 56, 64, 72, 80, 120 or 128 (and, for the
+ * relative-position bias, a table window that fits the kernel's staging) it runs as one
+ * kernel that packs K, quantises V and packs its queries itself (the workspace is then not
+ * written); otherwise as those two calls.  binattn_attention_one_kernel tells which.
  *
  *   q, k, v    [B,H,N,d] of dtype (contiguous)
  *   bias...    as binattn_forward
@@ -189,6 +193,13 @@ int binattn_prepare(const void* q, const void* k, const void* v, int dtype, int 
  * one BINATTN_EALIGN.
  */
 int64_t binattn_attention_workspace(int B, int H, int N, int d);
+/*
+ * binattn_attention_one_kernel -- 1 when binattn_attention with these arguments runs as one
+ * kernel from Q, K, V, 0 when it runs as binattn_prepare + binattn_forward; the dimension,
+ * dtype and relative-position grid checks of binattn_attention give the same error codes.
+ */
+int binattn_attention_one_kernel(int dtype, int bias_kind, int bias_dtype, int grid_h, int grid_w, int B, int H, int N,
+                                 int d);
 int binattn_attention(const void* q, const void* k, const void* v, int dtype, int bias_kind, int bias_dtype,
                       const void* bias, int64_t bias_ld, int grid_h, int grid_w, int B, int H, int N, int d,
                       void* out, int out_dtype, void* workspace, int64_t workspace_bytes, void* stream);

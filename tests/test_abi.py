@@ -125,6 +125,24 @@ def test_prepare_and_attention_validation(lib):
     assert lib.binattn_attention(*bad) == -1
 
 
+def test_attention_one_kernel_query(lib):
+    """Which way binattn_attention runs is a pure function of the shapes (no device needed):
+    one kernel for fp16 rows of <= 256 keys at d of 56..80 or 120..128, else prepare + forward."""
+    q = lib.binattn_attention_one_kernel
+    F32, F16, NONE, DENSE, REL = 0, 1, 0, 1, 2
+    assert q(F16, DENSE, F16, 0, 0, 64, 6, 197, 64) == 1      # DeiT-S
+    assert q(F16, REL, F16, 16, 16, 64, 16, 256, 72) == 1     # DiT-XL/2
+    assert q(F16, NONE, F16, 0, 0, 1, 1, 1, 128) == 1
+    assert q(F16, DENSE, F16, 0, 0, 32, 12, 577, 64) == 0     # DeiT-B/384: rows of 577 keys
+    assert q(F32, DENSE, F32, 0, 0, 1, 3, 197, 64) == 0       # fp32 inputs
+    assert q(F16, NONE, F16, 0, 0, 2, 2, 100, 32) == 0        # d = 32
+    assert q(F16, NONE, F16, 0, 0, 2, 2, 257, 64) == 0
+    assert q(F16, NONE, F16, 0, 0, 2, 2, 100, 60) == -2       # d not a multiple of 8
+    assert q(F16, REL, F16, 32, 8, 2, 2, 256, 64) == -2       # grid width not a multiple of 16
+    assert q(F16, REL, F16, 16, 16, 2, 2, 255, 64) == -1      # grid does not cover N
+    assert q(7, NONE, F16, 0, 0, 2, 2, 100, 64) == -2
+
+
 def test_valid_arguments_without_a_device_report_enodevice(lib):
     import torch
     if torch.cuda.is_available():
