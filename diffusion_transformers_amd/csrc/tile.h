@@ -662,6 +662,10 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
     }
     const int qb_hi = min(nqb, qb_lo + qb_len);
     if (qb_lo >= qb_hi) return;
+    if (DENSE) {  // heads in (h, b) order: the batch items of one head share its bias rows in the XCD's L2
+        const int hh = bh / a.B, bb = bh - hh * a.B;
+        bh = bb * a.H + hh;
+    }
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: keeps row pointers scalar
     const int h = bh % a.H;
