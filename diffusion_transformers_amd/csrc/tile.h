@@ -142,22 +142,25 @@ __device__ __forceinline__ void load_tile(TileRegs<NT, TW>& r, const FwdArgs& a,
     }
 }
 
-template <int NT, int TW>
+// NARROW: the tile holds at most 16 valid keys (the last tile of a row) and is staged for the
+// narrow score tile: key j is K operand row j of MFMA 0, and the V^ dword of keys 4q..4q+3 is the
+// first dword of operand lane (slot, q) -- those lanes' other bytes meet zero P^ bytes.
+template <int NT, int TW, bool NARROW = false>
 __device__ __forceinline__ void store_tile(const TileRegs<NT, TW>& r, TileLds<NT, TW>& s, int d) {
     typedef TileRegs<NT, TW> R;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < R::KT; ++i) {
         const int id = tid + 256 * i;
-        if (id < kBC * R::W) {
+        if (id < (NARROW ? 16 : kBC) * R::W) {
             const int j = id / R::W, w = id % R::W;
             uint32_t word = r.kw[i];
             const int left = d - 32 * w;  // channels >= d contribute nothing
             if (left < 32) word &= (1u << left) - 1u;
             uint32_t o[4];
             unpack_bits32_f4(word, o);
-            int t;
-            const int m = key_slot(j, t);
+            int t = 0, m = j;
+            if (!NARROW) m = key_slot(j, t);
             *reinterpret_cast<uint4*>(&s.k[((t * R::W + w) * 16 + m) * 4]) = make_uint4(o[0], o[1], o[2], o[3]);
         }
     }
@@ -168,7 +171,15 @@ __device__ __forceinline__ void store_tile(const TileRegs<NT, TW>& r, TileLds<NT
             const int c = id >> 2, gg = id & 3;
             int ct;
             const int m = chan_slot<NT>(c, ct);
-            *reinterpret_cast<uint4*>(&s.v[(ct * kWave + m + 16 * gg) * 4]) = r.v[i];
+            if (!NARROW) {
+                *reinterpret_cast<uint4*>(&s.v[(ct * kWave + m + 16 * gg) * 4]) = r.v[i];
+            } else if (gg == 0) {
+                const uint4 x = r.v[i];
+                s.v[(ct * kWave + m) * 4] = x.x;
+                s.v[(ct * kWave + m + 16) * 4] = x.y;
+                s.v[(ct * kWave + m + 32) * 4] = x.z;
+                s.v[(ct * kWave + m + 48) * 4] = x.w;
+            }
         }
     }
     if (tid < kBC) s.mu[tid] = r.mu;
@@ -372,6 +383,45 @@ __device__ __forceinline__ v4i tile_probs(const float (&S)[16], float negm, floa
     return pw;
 }
 
+// The narrow last tile (at most 16 valid keys, staged by store_tile<..., true>): one MFMA, lane
+// (query n, group g) holds keys jg + r, jg = j0 + 4g, r = 0..3; keys >= N (r >= nvalid) get -inf.
+// bias: loaded at key column jg (bias_at r < 4); wrun: window entry of key jg + 3.
+template <int NT, int BIAS>
+__device__ __forceinline__ void tile_scores4(const uint32_t* __restrict__ sk, const float* __restrict__ smu,
+                                             const LaneQ& lq, const BiasRegs<BIAS>& bias, const float* wrun,
+                                             int nvalid, float (&S)[4], float& mloc) {
+    constexpr int W = (NT + 1) / 2;
+    const int lane = threadIdx.x & 63, g = lane >> 4, m16 = lane & 15;
+    const int koff = ((g < W ? g : 0) * 16 + m16) * 4;
+    const v4f D = mfma_f4(*reinterpret_cast<const v4i*>(&sk[koff]), lq.qop, lq.dseed);
+    typedef const float __attribute__((address_space(3)))* lds_cfptr;
+    lds_cfptr wl = (lds_cfptr)wrun;
+    if (BIAS == BK_RELPOS) asm volatile("" : "+v"(wl));
+    const float4 m4 = *reinterpret_cast<const float4*>(&smu[4 * g]);
+    const float muk[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float b = 0.0f;
+        if (BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32) b = bias_at<BIAS>(bias, r);
+        if (BIAS == BK_RELPOS) b = wl[3 - r];
+        S[r] = r < nvalid ? __builtin_fmaf(D[r] * muk[r], lq.cq, b) : -INFINITY;
+    }
+    mloc = fmaxf(fmaxf(mloc, S[0]), S[1]);
+    mloc = fmaxf(fmaxf(mloc, S[2]), S[3]);
+}
+
+// P^ - 128 of the narrow tile in the first dword of the lane's PV operand, zeros after it.
+__device__ __forceinline__ v4i tile_probs4(const float (&S)[4], float negm, float& lsum) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(S[r], kLog2e, negm));
+        lsum += p;
+        word = __builtin_amdgcn_cvt_pk_u8_f32(p, r, word);
+    }
+    return v4i{(int)(word ^ 0x80808080u), 0, 0, 0};
+}
+
 constexpr v4i kC64 = v4i{0x40404040, 0x40404040, 0x40404040, 0x40404040};
 
 // Dequantise, normalise and store the lane's 4*NT channels of its query.
@@ -417,7 +467,7 @@ __device__ __forceinline__ void stage_common(const FwdArgs& a, int bh, float* sS
 // sRed: 2048 floats; sInv, sAmx: 128 words; sCol: 128 * sum_j V^_jc per channel slot (16 NT).
 // The per-channel reductions (absmax, column sum) take 256/d threads per channel, which meet in
 // an LDS max / add.
-template <int NT, int NTL>
+template <int NT, int NTL, bool NARROW>
 __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo, int nitems, TileLds<NT, 4>* lds,
                                             float* sScale, uint32_t* sQw, float* sQmu, float* sRed,
                                             float* sInv, uint32_t* sAmx, int* sCol) {
@@ -484,14 +534,18 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
             }
         }
         const bool live = j < N;
-        int t;
-        const int jj = j & (kBC - 1), m = key_slot(jj, t);
+        const int jj = j & (kBC - 1);
+        const bool narrow = NARROW && j / kBC == NTL - 1;  // the last tile, staged narrow
+        int t = 0, m = jj;
+        if (!narrow) m = key_slot(jj, t);
         TileLds<NT, 4>& s = lds[j / kBC];
+        if (!narrow || jj < 16) {
 #pragma unroll
-        for (int w = 0; w < W; ++w) {
-            uint32_t o[4];
-            unpack_bits32_f4(live ? words[w] : 0u, o);
-            *reinterpret_cast<uint4*>(&s.k[((t * W + w) * 16 + m) * 4]) = make_uint4(o[0], o[1], o[2], o[3]);
+            for (int w = 0; w < W; ++w) {
+                uint32_t o[4];
+                unpack_bits32_f4(live ? words[w] : 0u, o);
+                *reinterpret_cast<uint4*>(&s.k[((t * W + w) * 16 + m) * 4]) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
         }
         s.mu[jj] = live ? acc / (float)d : 0.0f;
     }
@@ -547,7 +601,9 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
                         }
                         qb[r][w] = word ^ 0x80808080u;
                     }
-                const int t = n0 >> 6, jj = n0 & (kBC - 1), gg = jj >> 4, ii = jj & 15;
+                const int t = n0 >> 6, jj = n0 & (kBC - 1);
+                const bool narrow = NARROW && t == NTL - 1;  // keys 4q..4q+3 -> first dword of lane q
+                const int gg = narrow ? jj >> 2 : jj >> 4, ii = narrow ? 0 : jj & 15;
                 char* vbase = reinterpret_cast<char*>(lds[t].v);
 #pragma unroll
                 for (int w = 0; w < 2; ++w) {
@@ -617,14 +673,16 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
 // query blocks [qb_lo, qb_hi) of that head (nsplit workgroups per head).  The next block's query
 // words, dense-bias rows and relative-position window are loaded while the current block is
 // computed, into registers the current block no longer needs.
-// RAGGED: N is not a multiple of the tile (the last tile masks the keys >= N).
+// TAIL: 0 when N is a multiple of the tile; 1 when the last tile masks the keys >= N; 2 when the
+// last tile (tile NTL - 1) holds at most 16 keys and is computed as the narrow tile.
 // NTL > kKeepTiles (long rows): NTL is the capacity and ceil(N / 64) <= NTL tiles are used; the
 // dense bias is then fetched one tile ahead instead of a whole query block ahead.
-template <int NT, int BIAS, int NTL, bool FUSED, bool RAGGED>
+template <int NT, int BIAS, int NTL, bool FUSED, int TAIL>
 __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPlan plan) {
     constexpr int W = (NT + 1) / 2;
     constexpr bool DENSE = BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32;
     constexpr bool LONG = NTL > kKeepTiles;
+    constexpr bool RAGGED = TAIL != 0, NARROW = TAIL == 2;
     static_assert(!(LONG && FUSED), "the whole-attention staging covers short rows only");
     typedef TileRegs<NT, 4> Regs;
     typedef TileLds<NT, 4> Lds;
@@ -696,20 +754,22 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
             qmu = live ? a.qmu[(int64_t)bh * N + i] : 0.0f;
         }
     };
-    // Dense bias rows of this wave's 16 queries of block qb, key tile t (rows >= N read 0).
+    // Dense bias rows of this wave's 16 queries of block qb, key tile t (rows >= N read 0); the
+    // narrow last tile reads its lane's four keys.
     auto load_bias_tile = [&](int qb, int t, BiasRegs<BIAS>& bias_t) {
         const int r0 = min(qb * kBR + wave * 16, N);
         const char* brow = (const char*)a.bias + ((int64_t)h * N + r0) * a.bias_ld * esz;
         const int brow_bytes = min(N - r0, 16) * (int)a.bias_ld * esz;  // at most 16 rows: far below 2^31
         const int j0 = t * kBC;
-        load_bias<BIAS>(bias_t, buffer_rsrc(brow + j0 * esz, brow_bytes - j0 * esz), bvoff);
+        const int voff = NARROW && t == NTL - 1 ? (n16 * (int)a.bias_ld + 4 * g) * esz : bvoff;
+        load_bias<BIAS>(bias_t, buffer_rsrc(brow + j0 * esz, brow_bytes - j0 * esz), voff);
     };
     // First table row of the relative-position window of block qb (every key touched).
     auto window_lo = [&](int qb) { return relpos_window(qb * kBR, 0, N, N, a.gh, a.gw).dr_lo; };
 
     // ---- stage the head once (all loads in flight together), then the first block's inputs
     if constexpr (FUSED) {
-        fused_stage<NT, NTL>(a, bh, qb_lo, qb_hi - qb_lo, lds, sScale, sQw, sQmu, sRed, sInv, sAmx, sCol);
+        fused_stage<NT, NTL, NARROW>(a, bh, qb_lo, qb_hi - qb_lo, lds, sScale, sQw, sQmu, sRed, sInv, sAmx, sCol);
         __syncthreads();  // the prepared query words are read by load_query below
     } else {
         Regs regs[NTL];
@@ -723,7 +783,10 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
 #pragma unroll
         for (int t = 0; t < NTL; ++t) {
             if (!LONG || t < nt) {
-                store_tile<NT, 4>(regs[t], lds[t], d);
+                if (NARROW && t == NTL - 1)
+                    store_tile<NT, 4, true>(regs[t], lds[t], d);
+                else
+                    store_tile<NT, 4>(regs[t], lds[t], d);
                 colsum_add(regs[t], cs);
             }
         }
@@ -778,21 +841,28 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
 
         // ---- pass 1: scores and row max
         float S[NTL][16];
+        float S4[4];  // the narrow last tile
         float mloc = -INFINITY;
         if (live) {
 #pragma unroll
             for (int t = 0; t < NTL; ++t) {
                 if (!LONG || t < nt) {  // (a uniform skip, not a break: the loop must unroll to keep S in registers)
                     if (LONG && DENSE && t + 1 < nt) load_bias_tile(qb, t + 1, bias[(t + 1) & 1]);
-                    const int jg = t * kBC + 16 * g;
-                    int idx0 = 15;
+                    const bool nar = NARROW && t == NTL - 1;
+                    const int run = nar ? 4 : 16;  // keys per lane
+                    const int jg = t * kBC + run * g;
+                    int idx0 = run - 1;
                     if (BIAS == BK_RELPOS) {
                         const int rj = jg / a.gw, cj = jg % a.gw;
                         idx0 = (ri - rj + a.gh - 1 - win_lo) * (2 * a.gw - 1) + (ci - cj + a.gw - 1);
-                        if (jg >= N) idx0 = 15;  // the whole run is past N and masked; keep reads in the window
+                        if (jg >= N) idx0 = run - 1;  // the whole run is past N and masked; keep reads in the window
                     }
-                    tile_scores<NT, BIAS>(L[t].k, L[t].mu, lq, bias[LONG ? (t & 1) : t], sWin + idx0 - 15,
-                                          RAGGED && t == nt - 1, N - jg, S[t], mloc);
+                    if (nar)
+                        tile_scores4<NT, BIAS>(L[t].k, L[t].mu, lq, bias[LONG ? (t & 1) : t], sWin + idx0 - 3, N - jg,
+                                               S4, mloc);
+                    else
+                        tile_scores<NT, BIAS>(L[t].k, L[t].mu, lq, bias[LONG ? (t & 1) : t], sWin + idx0 - 15,
+                                              RAGGED && t == nt - 1, N - jg, S[t], mloc);
                 }
                 __builtin_amdgcn_sched_barrier(0);  // one tile's operands live at a time
             }
@@ -824,7 +894,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
 #pragma unroll
             for (int t = 0; t < NTL; ++t) {
                 if (!LONG || t < nt) {
-                    const v4i pw = tile_probs(S[t], negm, lsum);
+                    const v4i pw = NARROW && t == NTL - 1 ? tile_probs4(S4, negm, lsum) : tile_probs(S[t], negm, lsum);
 #pragma unroll
                     for (int ct = 0; ct < NT; ++ct) {
                         const v4i vop = *reinterpret_cast<const v4i*>(&L[t].v[(ct * kWave + lane) * 4]);
@@ -932,46 +1002,63 @@ inline KeepPlan keep_plan(int64_t nheads, int nqb, int slots, double stage) {
 }
 
 // Staging a head costs about half a query block's work (plain), three (whole attention).
-template <int NT, int BK, int NTL, bool FUSED, bool RAGGED>
+template <int NT, int BK, int NTL, bool FUSED, int TAIL>
 inline void launch_keep_inst(const FwdArgs& a, hipStream_t s) {
-    static const int per_cu = resident_per_cu(binattn_fwd_keep_kernel<NT, BK, NTL, FUSED, RAGGED>);
+    static const int per_cu = resident_per_cu(binattn_fwd_keep_kernel<NT, BK, NTL, FUSED, TAIL>);
     const int64_t nheads = (int64_t)a.B * a.H;
     const int nqb = (a.N + kBR - 1) / kBR;
     const KeepPlan p = keep_plan(nheads, nqb, per_cu * device_cus(), FUSED ? 3.0 : 0.5);
     const int64_t grid = 8 * ((nheads + 7) / 8) * (p.a + p.b);
-    hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, NTL, FUSED, RAGGED>), dim3((unsigned)grid), dim3(256), 0, s,
+    hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, NTL, FUSED, TAIL>), dim3((unsigned)grid), dim3(256), 0, s,
                        a, p);
 }
 
-// The head-resident kernel for rows of kKeepTiles < ceil(N / 64) <= kLongTiles tiles (d <= 64).
+// Kind of the last tile: 0 whole, 2 at most 16 keys (narrow), 1 otherwise.
+inline int keep_tail(int N) {
+    const int r = N % kBC;
+    return r == 0 ? 0 : (r <= 16 ? 2 : 1);
+}
+
+// The head-resident kernel for rows of kKeepTiles < ceil(N / 64) <= kLongTiles tiles (d <= 64);
+// the narrow last tile only where it is tile kLongTiles - 1.
 template <int NT, int BK>
 inline void launch_keep_long(const FwdArgs& a, hipStream_t s) {
     static_assert(NT <= 4, "long rows are staged whole for d <= 64 only");
-    if (a.N % kBC != 0)
-        launch_keep_inst<NT, BK, kLongTiles, false, true>(a, s);
+    const int ntiles = (a.N + kBC - 1) / kBC, tail = keep_tail(a.N);
+    if (tail == 0)
+        launch_keep_inst<NT, BK, kLongTiles, false, 0>(a, s);
+    else if (tail == 2 && ntiles == kLongTiles)
+        launch_keep_inst<NT, BK, kLongTiles, false, 2>(a, s);
     else
-        launch_keep_inst<NT, BK, kLongTiles, false, false>(a, s);
+        launch_keep_inst<NT, BK, kLongTiles, false, 1>(a, s);
+}
+
+template <int NT, int BK, bool FUSED, int TAIL>
+inline void launch_keep_tail(const FwdArgs& a, int ntiles, hipStream_t s) {
+    switch (ntiles) {
+        case 1: launch_keep_inst<NT, BK, 1, FUSED, TAIL>(a, s); break;
+        case 2: launch_keep_inst<NT, BK, 2, FUSED, TAIL>(a, s); break;
+        case 3: launch_keep_inst<NT, BK, 3, FUSED, TAIL>(a, s); break;
+        default: launch_keep_inst<NT, BK, 4, FUSED, TAIL>(a, s); break;
+    }
 }
 
 // The short-row kernel for rows of ceil(N / 64) <= kKeepTiles tiles.
 template <int NT, int BK, bool FUSED>
 inline void launch_keep(const FwdArgs& a, hipStream_t s) {
     const int ntiles = (a.N + kBC - 1) / kBC;
-    if (a.N % kBC != 0) {
-        switch (ntiles) {
-            case 1: launch_keep_inst<NT, BK, 1, FUSED, true>(a, s); break;
-            case 2: launch_keep_inst<NT, BK, 2, FUSED, true>(a, s); break;
-            case 3: launch_keep_inst<NT, BK, 3, FUSED, true>(a, s); break;
-            default: launch_keep_inst<NT, BK, 4, FUSED, true>(a, s); break;
-        }
-    } else {
-        switch (ntiles) {
-            case 1: launch_keep_inst<NT, BK, 1, FUSED, false>(a, s); break;
-            case 2: launch_keep_inst<NT, BK, 2, FUSED, false>(a, s); break;
-            case 3: launch_keep_inst<NT, BK, 3, FUSED, false>(a, s); break;
-            default: launch_keep_inst<NT, BK, 4, FUSED, false>(a, s); break;
+    const int tail = keep_tail(a.N);
+    if (tail == 0) {
+        launch_keep_tail<NT, BK, FUSED, 0>(a, ntiles, s);
+        return;
+    }
+    if constexpr (BK != BK_RELPOS) {  // relative-position grids give a narrow tail only for N = 64k + 16
+        if (tail == 2) {
+            launch_keep_tail<NT, BK, FUSED, 2>(a, ntiles, s);
+            return;
         }
     }
+    launch_keep_tail<NT, BK, FUSED, 1>(a, ntiles, s);
 }
 
 }  // namespace binattn

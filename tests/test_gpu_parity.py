@@ -197,7 +197,10 @@ def test_attention_equals_pipeline(name):
 @pytest.mark.parametrize("B,H,N,d,bias,grid", [(1, 1, 1, 64, "dense", ()), (2, 3, 17, 64, "none", ()),
                                                 (1, 2, 65, 72, "dense", ()), (2, 2, 130, 128, "none", ()),
                                                 (2, 3, 197, 64, "dense", ()), (1, 4, 256, 72, "relpos", (16, 16)),
-                                                (1, 2, 192, 64, "relpos", (12, 16)), (3, 1, 256, 128, "relpos", (8, 32))])
+                                                (1, 2, 192, 64, "relpos", (12, 16)), (3, 1, 256, 128, "relpos", (8, 32)),
+                                                # last tile of <= 16 keys (the narrow tile): 80 = 64 + 16, 208 = 192 + 16
+                                                (1, 2, 80, 72, "none", ()), (2, 2, 208, 64, "dense", ()),
+                                                (1, 2, 144, 128, "dense", ())])
 def test_attention_short_rows_one_kernel(B, H, N, d, bias, grid):
     """Short rows from fp16 inputs run as one kernel that stages K, V and Q itself; its output
     equals the four-call pipeline bit for bit (same comparisons, summation orders, divisions)."""
@@ -235,6 +238,11 @@ SMALL = [
     (1, 1, 600, 48, "f32", "dense", ()),
     (1, 2, 640, 32, "f16", "dense", ()),
     (1, 1, 641, 64, "f16", "dense", ()),
+    # last tile of <= 16 keys (the narrow tile), short and 10-tile rows
+    (1, 2, 80, 64, "f16", "dense", ()),
+    (2, 1, 208, 72, "f16", "none", ()),
+    (1, 1, 592, 64, "f16", "dense", ()),
+    (1, 1, 590, 32, "f32", "none", ()),
     (1, 1, 577, 128, "f16", "dense", ()),
     (1, 2, 1024, 96, "f32", "relpos", (8, 128)),
     (1, 1, 2400, 64, "f16", "relpos", (15, 160)),
