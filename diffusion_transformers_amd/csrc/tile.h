@@ -484,7 +484,7 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
         sCol[tid] = 0;
     }
 
-    // ---- all K, V and Q loads of the head in flight together.  Buffer loads: rows past N read
+    // ---- the K and V loads of the head in flight together.  Buffer loads: rows past N read
     // as zero and no load sits under a lane-dependent branch (so no load is waited for early).
     const int hbytes = N * d * 2;  // at most 256 * 128 * 2
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(a.k_raw + (int64_t)bh * N * d, hbytes);
@@ -507,14 +507,6 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
         vx[i] = load16(vr, grp < G ? n * d * 2 + part * 16 : hbytes);  // past N (or idle thread): 0
     }
     const int lane = tid & 63, g = lane >> 4, n16 = lane & 15, wave = tid >> 6;
-    h8 qx[kKeepTiles][4];
-#pragma unroll
-    for (int it = 0; it < kKeepTiles; ++it) {
-        const int i = (qb_lo + it) * kBR + wave * 16 + n16;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)  // chunks past d belong to the next query: masked where used
-            if (it < nitems) qx[it][c] = load16(qr, min(i, N) * d * 2 + 64 * g + 16 * c);
-    }
     __syncthreads();  // the zero fill is complete before any operand row is written
 
     // ---- K: sign bytes and partial |x| sums per chunk, words, mu_k (pack_wave's order)
@@ -635,7 +627,16 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
         atomicAdd(&sCol[c], 128 * cs);
     }
 
-    // ---- Q of every query block of this workgroup: word g of the signs and mu_q per lane
+    // ---- Q of every query block of this workgroup: word g of the signs and mu_q per lane.  Its
+    // loads are issued only now, after K and V have released their registers.
+    h8 qx[kKeepTiles][4];
+#pragma unroll
+    for (int it = 0; it < kKeepTiles; ++it) {
+        const int i = (qb_lo + it) * kBR + wave * 16 + n16;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)  // chunks past d belong to the next query: masked where used
+            if (it < nitems) qx[it][c] = load16(qr, min(i, N) * d * 2 + 64 * g + 16 * c);
+    }
 #pragma unroll
     for (int it = 0; it < kKeepTiles; ++it) {
         if (it >= nitems) break;
