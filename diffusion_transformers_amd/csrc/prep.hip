@@ -2,11 +2,10 @@
 // ([notes] key design 1) and the channel-wise int8 V ([notes] key design 3), where
 // [notes] is the "BinaryAttention" paper notes page (CVPR 2026), Method details.
 //
-// One grid, two kinds of workgroup: B*H quantise one head each with its V held in registers,
-// the rest pack contiguous spans of Q tokens and then of K tokens.  The two kinds are
-// interleaved in launch order (one head every R blocks), so the compute units always hold a
-// mix: packing streams HBM while the quantisers compute.  Heads whose V does not fit the register budget take the general path:
-// the pack kernel, then the absmax and quantise kernels.
+// One grid, two kinds of workgroup: the first B*H quantise one head each with its V held in
+// registers (the long ones, dispatched first so that none starts late), the rest pack spans of
+// 256 Q tokens and then of K tokens.  Heads whose V does not fit the register budget take the
+// general path: the pack kernel, then the absmax and quantise kernels.
 #include "common.h"
 #include "internal.h"
 #include "prep.h"
@@ -16,21 +15,20 @@ namespace binattn {
 template <typename T, int MAXC>
 __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, int BH, int N, int d, int W,
-                                                   int64_t ldv, int64_t npack, int R, uint32_t* __restrict__ qbits,
+                                                   int64_t ldv, int64_t npack, uint32_t* __restrict__ qbits,
                                                    float* __restrict__ qmu, uint32_t* __restrict__ kbits,
                                                    float* __restrict__ kmu, int8_t* __restrict__ vq,
                                                    float* __restrict__ vamax) {
     // LDS of the quantise role: sRed (8 KB) + sAmax + the transpose tile (packing uses none).
     __shared__ __attribute__((aligned(16))) uint8_t smem[2048 * 4 + 128 * 4 + 128 * kQuantTS];
     const int64_t b = blockIdx.x;
-    const int64_t span = (int64_t)R * BH;  // blocks [0, span): head b / R where b % R == 0
-    if (b < span && b % R == 0) {
-        quant_head_regs<T, MAXC>(v, N, d, ldv, b / R, vq, vamax, reinterpret_cast<float*>(smem),
+    if (b < BH) {
+        quant_head_regs<T, MAXC>(v, N, d, ldv, b, vq, vamax, reinterpret_cast<float*>(smem),
                                  reinterpret_cast<float*>(smem + 2048 * 4), smem + 2048 * 4 + 128 * 4);
         return;
     }
     const int64_t ntok = (int64_t)BH * N;
-    const int64_t pb = b < span ? b - (b + R - 1) / R : b - BH;  // minus the heads placed before b
+    const int64_t pb = b - BH;
     if (pb < npack)
         pack_wave<T>(q, ntok, d, W, qbits, qmu, pb);
     else
@@ -48,12 +46,11 @@ static hipError_t launch_prepare_t(const T* q, const T* k, const T* v, int BH, i
     const int64_t nblocks = BH + 2 * npack;
     if (nblocks <= 0x7fffffff && nc <= 20) {
         const dim3 grid((unsigned)nblocks), block(256);
-        const int R = (int)(nblocks / BH);
         if (nc <= 8)
-            hipLaunchKernelGGL((prep_kernel<T, 8>), grid, block, 0, s, q, k, v, BH, N, d, W, ldv, npack, R, qbits, qmu,
+            hipLaunchKernelGGL((prep_kernel<T, 8>), grid, block, 0, s, q, k, v, BH, N, d, W, ldv, npack, qbits, qmu,
                                kbits, kmu, vq, vamax);
         else
-            hipLaunchKernelGGL((prep_kernel<T, 20>), grid, block, 0, s, q, k, v, BH, N, d, W, ldv, npack, R, qbits,
+            hipLaunchKernelGGL((prep_kernel<T, 20>), grid, block, 0, s, q, k, v, BH, N, d, W, ldv, npack, qbits,
                                qmu, kbits, kmu, vq, vamax);
         return hipGetLastError();
     }
