@@ -542,6 +542,16 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
         s.mu[jj] = live ? acc / (float)d : 0.0f;
     }
 
+    // the Q loads, issued once K has released its registers, arrive while V is processed
+    h8 qx[kKeepTiles][4];
+#pragma unroll
+    for (int it = 0; it < kKeepTiles; ++it) {
+        const int i = (qb_lo + it) * kBR + wave * 16 + n16;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)  // chunks past d belong to the next query: masked where used
+            if (it < nitems) qx[it][c] = load16(qr, min(i, N) * d * 2 + 64 * g + 16 * c);
+    }
+
     // ---- V: channel absmax (input precision), scales, quantise, transpose, scatter
     h8 mv;
 #pragma unroll
@@ -627,16 +637,7 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
         atomicAdd(&sCol[c], 128 * cs);
     }
 
-    // ---- Q of every query block of this workgroup: word g of the signs and mu_q per lane.  Its
-    // loads are issued only now, after K and V have released their registers.
-    h8 qx[kKeepTiles][4];
-#pragma unroll
-    for (int it = 0; it < kKeepTiles; ++it) {
-        const int i = (qb_lo + it) * kBR + wave * 16 + n16;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)  // chunks past d belong to the next query: masked where used
-            if (it < nitems) qx[it][c] = load16(qr, min(i, N) * d * 2 + 64 * g + 16 * c);
-    }
+    // ---- Q of every query block of this workgroup: word g of the signs and mu_q per lane
 #pragma unroll
     for (int it = 0; it < kKeepTiles; ++it) {
         if (it >= nitems) break;
