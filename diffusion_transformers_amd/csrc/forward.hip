@@ -25,10 +25,12 @@
 //    V^ (channel-major in HBM) is staged the same way.  All global reads go through
 //    buffer resources rebased per tile on the scalar unit, so addresses cost no vector
 //    ALU and reads past a head's end return zero.
-//  * Rows of at most four tiles (N <= 256) take the exact row max: every tile is staged in
-//    LDS at once, pass 1 computes the scores into registers and the max, pass 2 quantises
-//    exp(S - max) and accumulates P^ V^ in int32 with no rescaling.  Longer rows stream
-//    the tiles through a two-stage LDS ring with the FlashAttention-2 running max.
+//  * Rows that a workgroup can hold (at most four tiles, N <= 256; or at most ten tiles at
+//    d <= 64 without the relative-position bias) take the exact row max in the head-resident
+//    kernel of tile.h: every tile is staged in LDS at once, pass 1 computes the scores into
+//    registers and the max, pass 2 quantises exp(S - max) and accumulates P^ V^ in int32 with
+//    no rescaling.  Longer rows stream the tiles through a two-stage LDS ring with the
+//    FlashAttention-2 running max (this file).
 //  * p = 255 exp(S - m) = exp2(S log2e - m log2e + log2 255), P^ = rint(p) via
 //    v_cvt_pk_u8_f32; the row sum is taken over the unquantised p.
 //  * PV with signed int8 MFMA: sum P^ V^ = sum (P^-128) V^ + 128 sum V^.  Short rows take

@@ -1,6 +1,6 @@
 // tile.h -- device building blocks of the BinaryAttention forward kernels (tile staging,
-// Q operand, bias, score tile, quantised probabilities, epilogue) and the short-row kernel,
-// shared by the forward from packed inputs and the whole-attention path.
+// Q operand, bias, score tile, quantised probabilities, epilogue), the head-resident kernel and
+// its launch plan, shared by the forward from packed inputs and the whole-attention path.
 #pragma once
 
 #include <algorithm>
@@ -670,11 +670,12 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
 }
 
 // ---------------------------------------------------------------------------------------------
-// Rows of NTL <= kKeepTiles tiles (N <= 256): exact row max in two passes over register-resident
-// scores.  A workgroup stages the K bits, mu_k and V^ of one (b, h) once and then loops over the
-// query blocks [qb_lo, qb_hi) of that head (nsplit workgroups per head).  The next block's query
-// words, dense-bias rows and relative-position window are loaded while the current block is
-// computed, into registers the current block no longer needs.
+// Head-resident kernel: exact row max in two passes over register-resident scores.  A workgroup
+// stages the K operand rows, mu_k, V^ and the V^ column sums of one (b, h) once and then loops
+// over its segment [qb_lo, qb_hi) of that head's query blocks (segments per the KeepPlan).  The
+// next block's query words, dense-bias rows and relative-position window are loaded while the
+// current block is computed, into registers the current block no longer needs.  FUSED: the
+// staging reads fp16 Q, K, V and packs / quantises them itself (fused_stage).
 // TAIL: 0 when N is a multiple of the tile; 1 when the last tile masks the keys >= N; 2 when the
 // last tile (tile NTL - 1) holds at most 16 keys and is computed as the narrow tile.
 // NTL > kKeepTiles (long rows): NTL is the capacity and ceil(N / 64) <= NTL tiles are used; the
