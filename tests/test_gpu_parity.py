@@ -200,7 +200,10 @@ def test_attention_equals_pipeline(name):
                                                 (1, 2, 192, 64, "relpos", (12, 16)), (3, 1, 256, 128, "relpos", (8, 32)),
                                                 # last tile of <= 16 keys (the narrow tile): 80 = 64 + 16, 208 = 192 + 16
                                                 (1, 2, 80, 72, "none", ()), (2, 2, 208, 64, "dense", ()),
-                                                (1, 2, 144, 128, "dense", ())])
+                                                (1, 2, 144, 128, "dense", ()),
+                                                # head dims with a partial channel group or tile
+                                                (2, 2, 100, 56, "dense", ()), (1, 3, 256, 80, "relpos", (16, 16)),
+                                                (1, 2, 197, 120, "none", ())])
 def test_attention_short_rows_one_kernel(B, H, N, d, bias, grid):
     """Short rows from fp16 inputs run as one kernel that stages K, V and Q itself; its output
     equals the four-call pipeline bit for bit (same comparisons, summation orders, divisions)."""
