@@ -26,6 +26,7 @@ struct FwdArgs {
     const _Float16* q_raw;  // whole-attention path: fp16 Q, K, V [B,H,N,d] (packed inputs above unused)
     const _Float16* k_raw;
     const _Float16* v_raw;
+    int wrs;              // head-resident kernel: LDS row stride of its relative-position window
 };
 
 hipError_t launch_pack_qk(const void* x, int f32, int64_t ntok, int d, uint32_t* bits, float* mu,

@@ -94,25 +94,35 @@ struct HeadPtrs {
     const void* table;  // relative-position table of head h
 };
 
-// Loads PER window entries per thread (entry tid + 256 i) of a head's relative-position table,
-// starting at element off, as fp32.  Entries past the table read as 0.
+// Loads entries off + eo[i] (i < PER) of a head's relative-position table as fp32; entries past
+// the table read as 0.
 template <int PER>
-__device__ __forceinline__ void load_window(float (&dst)[PER], const FwdArgs& a, const void* table, int off) {
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void load_window_at(float (&dst)[PER], const FwdArgs& a, const void* table, int off,
+                                               const int (&eo)[PER]) {
     const int tsz = (2 * a.gh - 1) * (2 * a.gw - 1);
     if (a.bias_f32) {
         const __amdgpu_buffer_rsrc_t tr = buffer_rsrc((const float*)table + off, (tsz - off) * 4);
 #pragma unroll
         for (int i = 0; i < PER; ++i)
-            dst[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(tr, (tid + 256 * i) * 4, 0, 0));
+            dst[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(tr, eo[i] * 4, 0, 0));
     } else {
         const __amdgpu_buffer_rsrc_t tr = buffer_rsrc((const _Float16*)table + off, (tsz - off) * 2);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const uint16_t hbits = __builtin_amdgcn_raw_buffer_load_b16(tr, (tid + 256 * i) * 2, 0, 0);
+            const uint16_t hbits = __builtin_amdgcn_raw_buffer_load_b16(tr, eo[i] * 2, 0, 0);
             dst[i] = (float)__builtin_bit_cast(_Float16, hbits);
         }
     }
+}
+
+// Loads PER window entries per thread (entry tid + 256 i) of a head's relative-position table,
+// starting at element off, as fp32.  Entries past the table read as 0.
+template <int PER>
+__device__ __forceinline__ void load_window(float (&dst)[PER], const FwdArgs& a, const void* table, int off) {
+    int eo[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) eo[i] = threadIdx.x + 256 * i;
+    load_window_at<PER>(dst, a, table, off, eo);
 }
 
 template <int NT, int TW>
@@ -795,9 +805,17 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
         }
         colsum_store<NT>(cs, sCol);
     }
+    // window slot tid + 256 i holds table row r, column c of the window (row stride a.wrs; the
+    // slots past a row's 2 gw - 1 entries are padding, loaded but never read)
     float wv[kRelposWin / 256];
+    int weo[kRelposWin / 256];
     if (BIAS == BK_RELPOS) {
-        load_window<kRelposWin / 256>(wv, a, hp.table, window_lo(qb_lo) * (2 * a.gw - 1));
+#pragma unroll
+        for (int i = 0; i < kRelposWin / 256; ++i) {
+            const int slot = tid + 256 * i, r = slot / a.wrs;
+            weo[i] = r * (2 * a.gw - 1) + (slot - r * a.wrs);
+        }
+        load_window_at<kRelposWin / 256>(wv, a, hp.table, window_lo(qb_lo) * (2 * a.gw - 1), weo);
 #pragma unroll
         for (int i = 0; i < kRelposWin / 256; ++i) sWin[tid + 256 * i] = wv[i];
     }
@@ -821,7 +839,8 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
         const int q0 = qb * kBR, qw0 = q0 + wave * 16;
         const bool live = qw0 < N;  // some query of this wave is < N (wave-uniform)
         const bool more = qb + 1 < qb_hi;
-        if (BIAS == BK_RELPOS && more) load_window<kRelposWin / 256>(wv, a, hp.table, window_lo(qb + 1) * (2 * a.gw - 1));
+        if (BIAS == BK_RELPOS && more)
+            load_window_at<kRelposWin / 256>(wv, a, hp.table, window_lo(qb + 1) * (2 * a.gw - 1), weo);
 
         // the lane's query: Q operand (fp4 2*sign of channels 32g..32g+31, 0 past d) and seed
         LaneQ lq;
@@ -857,7 +876,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
                     int idx0 = run - 1;
                     if (BIAS == BK_RELPOS) {
                         const int rj = jg / a.gw, cj = jg % a.gw;
-                        idx0 = (ri - rj + a.gh - 1 - win_lo) * (2 * a.gw - 1) + (ci - cj + a.gw - 1);
+                        idx0 = (ri - rj + a.gh - 1 - win_lo) * a.wrs + (ci - cj + a.gw - 1);
                         if (jg >= N) idx0 = run - 1;  // the whole run is past N and masked; keep reads in the window
                     }
                     if (nar)
@@ -917,16 +936,42 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
     }
 }
 
-// Whether the relative-position window of a whole short row (queries of one block, every key)
-// fits the staged window; false sends the launch to the streaming kernel.
-inline bool keep_window_fits(const FwdArgs& a) {
-    const int N = a.N, gw = a.gw, gh = a.gh;
+// LDS row stride (fp32 entries) of the relative-position window the head-resident kernel stages
+// for a whole short row (the queries of one block, every key), or 0 when it does not fit (the
+// launch then goes to the streaming kernel).  A wave's 16 queries share a grid row, and so do the
+// 16 keys of lane group g (the grid width is a multiple of 16), so group g reads 16 consecutive
+// window entries from an offset that moves by -(rj stride + cj) with its first key (rj, cj).  The
+// smallest stride >= the table row 2 gw - 1 that puts the four groups' runs on disjoint banks
+// (their starts 16 apart modulo 32 within each half-wave and at least 16 apart modulo 64 across
+// the wave) makes every window read free of bank conflicts; 2 gw - 1 itself when none fits.
+inline int keep_window_stride(const FwdArgs& a) {
+    const int N = a.N, gw = a.gw, gh = a.gh, row = 2 * gw - 1;
+    int rows = 0;  // table rows of the largest window
     for (int q0 = 0; q0 < N; q0 += kBR) {
         const int ri_min = q0 / gw, ri_max = (min(q0 + kBR, N) - 1) / gw;
-        if ((ri_max - ri_min + gh) * (2 * gw - 1) > kRelposWin) return false;
+        rows = max(rows, ri_max - ri_min + gh);
     }
-    return true;
+    auto conflict_free = [&](int rs) {
+        for (int j0 = 0; j0 < N; j0 += kBC) {
+            int st[4];
+            for (int g = 0; g < 4; ++g) {
+                const int j = j0 + 16 * g;
+                st[g] = (((-(j / gw) * rs - j % gw) % 64) + 64) % 64;
+            }
+            for (int g = 0; g < 4; ++g)
+                for (int h = g + 1; h < 4 && j0 + 16 * h < N; ++h) {  // groups past N are masked
+                    const int dist = (st[h] - st[g] + 64) % 64;
+                    if (dist < 16 || dist > 48) return false;
+                    if (h == g + 1 && (g & 1) == 0 && dist % 32 != 16) return false;
+                }
+        }
+        return true;
+    };
+    for (int rs = row; rs < row + 64; ++rs)
+        if (rows * rs <= kRelposWin && conflict_free(rs)) return rs;
+    return rows * row <= kRelposWin ? row : 0;
 }
+inline bool keep_window_fits(const FwdArgs& a) { return keep_window_stride(a) > 0; }
 
 // Compute units of the current device (cached per device; 256 on MI355X).
 inline int device_cus() {
@@ -1012,8 +1057,10 @@ inline void launch_keep_inst(const FwdArgs& a, hipStream_t s) {
     const int nqb = (a.N + kBR - 1) / kBR;
     const KeepPlan p = keep_plan(nheads, nqb, per_cu * device_cus(), FUSED ? 3.0 : 0.5);
     const int64_t grid = 8 * ((nheads + 7) / 8) * (p.a + p.b);
+    FwdArgs ka = a;
+    if (BK == BK_RELPOS) ka.wrs = keep_window_stride(a);
     hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, NTL, FUSED, TAIL>), dim3((unsigned)grid), dim3(256), 0, s,
-                       a, p);
+                       ka, p);
 }
 
 // Kind of the last tile: 0 whole, 2 at most 16 keys (narrow), 1 otherwise.

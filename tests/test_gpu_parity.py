@@ -203,7 +203,7 @@ def test_attention_equals_pipeline(name):
                                                 (1, 2, 144, 128, "dense", ()),
                                                 # head dims with a partial channel group or tile
                                                 (2, 2, 100, 56, "dense", ()), (1, 3, 256, 80, "relpos", (16, 16)),
-                                                (1, 2, 197, 120, "none", ())])
+                                                (1, 2, 197, 120, "none", ()), (2, 2, 240, 64, "relpos", (5, 48))])
 def test_attention_short_rows_one_kernel(B, H, N, d, bias, grid):
     """Short rows from fp16 inputs run as one kernel that stages K, V and Q itself; its output
     equals the four-call pipeline bit for bit (same comparisons, summation orders, divisions)."""
@@ -234,6 +234,11 @@ SMALL = [
     (1, 2, 197, 64, "f32", "dense", ()),
     (2, 2, 256, 72, "f16", "relpos", (16, 16)),
     (1, 2, 384, 64, "f16", "relpos", (12, 32)),
+    # relative-position grids whose staged window rows are padded to other strides (48 and 112
+    # entries for widths 16 and 48; none at width 64), a ragged last tile at 240 = 5 x 48
+    (2, 1, 64, 64, "f32", "relpos", (4, 16)),
+    (1, 2, 240, 64, "f16", "relpos", (5, 48)),
+    (1, 2, 256, 72, "f16", "relpos", (4, 64)),
     # 5..10 tiles, d <= 64: the head-resident kernel for long rows (ragged and whole last tiles)
     (1, 2, 300, 64, "f16", "dense", ()),
     (2, 1, 320, 64, "f32", "none", ()),
