@@ -364,9 +364,13 @@ __device__ __forceinline__ void tile_scores(const uint32_t* __restrict__ sk, con
     // The max is taken separately on the two paths: on the common one every S is an fma
     // result and needs no NaN canonicalisation before v_max3.
     if (tail) {  // ragged end: keys >= N take no weight
+        // (the empty asm keeps this a branch of its own: without it the compiler turns the
+        // masking of every tile into selects on lane masks it hoists out of the block loop)
+        int nv = nvalid;
+        asm volatile("" : "+v"(nv));
 #pragma unroll
         for (int k = 0; k < 16; ++k)
-            if (k >= nvalid) S[k] = -INFINITY;
+            if (k >= nv) S[k] = -INFINITY;
 #pragma unroll
         for (int k = 15; k > 0; k -= 2) mloc = fmaxf(fmaxf(mloc, S[k]), S[k - 1]);
     } else {
@@ -884,7 +888,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
                                                S4, mloc);
                     else
                         tile_scores<NT, BIAS>(L[t].k, L[t].mu, lq, bias[LONG ? (t & 1) : t], sWin + idx0 - 15,
-                                              RAGGED && t == nt - 1, N - jg, S[t], mloc);
+                                              TAIL == 1 && t == nt - 1, N - jg, S[t], mloc);
                 }
                 __builtin_amdgcn_sched_barrier(0);  // one tile's operands live at a time
             }
