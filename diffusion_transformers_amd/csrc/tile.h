@@ -1047,6 +1047,9 @@ inline KeepPlan keep_plan(int64_t nheads, int nqb, int slots, double stage) {
                 if (t < best_t - 1e-9) best_t = t, best = p;
             }
         }
+    // equal segments all go first: the workgroups of one head are then launched next to each
+    // other (same XCD, consecutive slots) and the later ones find its inputs in L2
+    if (best.b > 0 && best.r == best.f) best.a += best.b, best.b = 0;
     std::lock_guard<std::mutex> lock(mu);
     if (cache.size() > 64) cache.clear();
     cache.push_back(Entry{nheads, nqb, slots, stage_milli, best});
