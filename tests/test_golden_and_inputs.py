@@ -65,3 +65,22 @@ def test_outlier_channels_count():
     ratio = np.abs(x["q"]) / np.maximum(np.abs(base), 1e-30)
     scaled = np.isclose(ratio, 8.0).all(axis=(0, 2))
     assert int(scaled.sum()) == round(0.01 * 12 * 64) == 8
+
+
+def test_bench_roofline_helpers():
+    """bench.py's roofline bookkeeping (host arithmetic only): the forward kernel named per
+    shape, the MFMA time of the effective ops at the fp4 and int8 peaks, and the algorithmic
+    bytes of the DeiT-B/384 forward from packed inputs."""
+    import bench
+    names = {w.name: bench.forward_kernel(w) for w in W.WORKLOADS}
+    assert names["deit_s_224"] == names["deit_b_384"] == names["dit_xl2_256"] == "binattn_fwd_keep_kernel"
+    assert names["highres_16k"] == "binattn_fwd_stream_kernel"
+    # 4 B H N^2 d effective ops: half at 10.1, half at 5.0 dense POPS -> 6.69 POPS overall
+    ops = 4.0e15
+    assert abs(bench.mfma_seconds(ops) - (2.0e15 / 10.1e15 + 2.0e15 / 5.0e15)) < 1e-15
+    assert abs(ops / bench.mfma_seconds(ops) / 1e12 - 6688.7) < 0.1
+    w = next(x for x in W.WORKLOADS if x.name == "deit_b_384")
+    # sign words + mu of Q and K, V^ bytes, channel absmax, dense fp16 bias once, fp16 O
+    B, H, N, d = w.B, w.H, w.N, w.d
+    expect = 2 * B * H * N * 2 * 4 + 2 * B * H * N * 4 + B * H * N * d + 4 * B * H * d + H * N * N * 2 + B * H * N * d * 2
+    assert abs(bench.fwd_bytes(w) - expect) <= 0.02 * expect
