@@ -591,9 +591,18 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
         sInv[tid] = av > 0.0f ? 127.0f / av : 0.0f;
     }
     __syncthreads();
-    float vsum[8];  // this thread's part of sum_j V^_jc for its 8 channels (exact integers)
+    // V^ = rint(v * fl32(127/a)), |v| <= a keeping it within +-127 (no clamp needed).  d <= 64:
+    // through t + 1.5 * 2^23, which for |t| < 2^22 rounds t to the nearest integer (ties to even,
+    // as rint) and holds it in the low mantissa bits, so its low byte is V^ as int8 and its bit
+    // pattern minus that of 1.5 * 2^23 is V^ -- a channel's four token bytes go straight into one
+    // dword (byte t = token t) with three v_perm.  Wider heads keep rint, v_cvt_pk_u8 and a 4x4
+    // transpose, which hold fewer registers at once (the three-waves-per-SIMD budget).
+    constexpr float kRound = 12582912.0f;
+    uint32_t vsum[8];  // d <= 64: sum of those bit patterns per channel (wraps; minus cnt times kRound's)
+    float vsumf[8];    // wider: sum of V^ per channel (exact integers)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vsum[e] = 0.0f;
+    for (int e = 0; e < 8; ++e) vsum[e] = 0u, vsumf[e] = 0.0f;
+    uint32_t cnt = 0;
     if (grp < G) {
         float inv[8];
 #pragma unroll
@@ -602,35 +611,55 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
         for (int u = 0; u < MAXC / 4; ++u) {
             const int n0 = 4 * (grp + G * u);
             if (n0 < N) {
-                uint32_t qb[4][2];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int w = 0; w < 2; ++w) {
-                        uint32_t word = 0;
-#pragma unroll
-                        for (int b = 0; b < 4; ++b) {
-                            // |v| <= a keeps rint(v * fl32(127/a)) within +-127 (no clamp needed)
-                            const float q = __builtin_rintf((float)vx[4 * u + r][4 * w + b] * inv[4 * w + b]);
-                            vsum[4 * w + b] += q;
-                            word = __builtin_amdgcn_cvt_pk_u8_f32(q + 128.0f, b, word);  // exact: q is an integer
-                        }
-                        qb[r][w] = word ^ 0x80808080u;
-                    }
+                cnt += 4;
                 const int t = n0 >> 6, jj = n0 & (kBC - 1);
                 const bool narrow = NARROW && t == NTL - 1;  // keys 4q..4q+3 -> first dword of lane q
                 const int gg = narrow ? jj >> 2 : jj >> 4, ii = narrow ? 0 : jj & 15;
                 char* vbase = reinterpret_cast<char*>(lds[t].v);
+                if constexpr (NT <= 4) {
 #pragma unroll
-                for (int w = 0; w < 2; ++w) {
-                    const uint32_t in[4] = {qb[0][w], qb[1][w], qb[2][w], qb[3][w]};
-                    uint32_t out[4];
-                    transpose4x4(in, out);
+                    for (int e = 0; e < 8; ++e) {  // channel part * 8 + e of the four tokens
+                        uint32_t ub[4];
 #pragma unroll
-                    for (int cc = 0; cc < 4; ++cc) {
+                        for (int r = 0; r < 4; ++r) {
+#pragma clang fp contract(off)
+                            const float x = (float)vx[4 * u + r][e] * inv[e];  // product and sum round separately
+                            ub[r] = __float_as_uint(x + kRound);
+                            vsum[e] += ub[r];
+                        }
+                        const uint32_t lo = __builtin_amdgcn_perm(ub[1], ub[0], 0x0c0c0400u);  // t0 t1 0 0
+                        const uint32_t hi = __builtin_amdgcn_perm(ub[3], ub[2], 0x0c0c0400u);  // t2 t3 0 0
                         int ct;
-                        const int m = chan_slot<NT>(part * 8 + 4 * w + cc, ct);
-                        *reinterpret_cast<uint32_t*>(vbase + ((ct * kWave + m + 16 * gg) * 16 + ii)) = out[cc];
+                        const int m = chan_slot<NT>(part * 8 + e, ct);
+                        *reinterpret_cast<uint32_t*>(vbase + ((ct * kWave + m + 16 * gg) * 16 + ii)) =
+                            __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                    }
+                } else {
+                    uint32_t qb[4][2];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int w = 0; w < 2; ++w) {
+                            uint32_t word = 0;
+#pragma unroll
+                            for (int b = 0; b < 4; ++b) {
+                                const float q = __builtin_rintf((float)vx[4 * u + r][4 * w + b] * inv[4 * w + b]);
+                                vsumf[4 * w + b] += q;
+                                word = __builtin_amdgcn_cvt_pk_u8_f32(q + 128.0f, b, word);  // exact: q is an integer
+                            }
+                            qb[r][w] = word ^ 0x80808080u;
+                        }
+#pragma unroll
+                    for (int w = 0; w < 2; ++w) {
+                        const uint32_t in[4] = {qb[0][w], qb[1][w], qb[2][w], qb[3][w]};
+                        uint32_t out[4];
+                        transpose4x4(in, out);
+#pragma unroll
+                        for (int cc = 0; cc < 4; ++cc) {
+                            int ct;
+                            const int m = chan_slot<NT>(part * 8 + 4 * w + cc, ct);
+                            *reinterpret_cast<uint32_t*>(vbase + ((ct * kWave + m + 16 * gg) * 16 + ii)) = out[cc];
+                        }
                     }
                 }
             }
@@ -639,15 +668,17 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int bh, int qb_lo,
 
     // column sums: partial sums through sRed (the absmax pass is done with it); integers, so the
     // order of the additions does not matter
+    int* sRedI = reinterpret_cast<int*>(sRed);
     if (grp < G) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sRed[grp * d + part * 8 + e] = vsum[e];
+        for (int e = 0; e < 8; ++e)
+            sRedI[grp * d + part * 8 + e] = NT <= 4 ? (int)(vsum[e] - cnt * __float_as_uint(kRound)) : (int)vsumf[e];
     }
     __syncthreads();
     if (tid < K * d) {
         const int c = tid % d;
         int cs = 0;
-        for (int gi = tid / d; gi < G; gi += K) cs += (int)sRed[gi * d + c];
+        for (int gi = tid / d; gi < G; gi += K) cs += sRedI[gi * d + c];
         atomicAdd(&sCol[c], 128 * cs);
     }
 
