@@ -304,6 +304,7 @@ def main():
     roof["algorithmic_bytes_per_launch"] = kb
     roof["launch_us"] = ks * 1e6
     roof["mfma_frac"] = t_mfma / ks
+    roof["ops_frac_of_int8_peak"] = ops / ks / 1e12 / I8_PEAK_TOPS  # the metric's own yardstick (5 POPS for all ops)
     roof["hbm_frac"] = kb / ks / 1e9 / HBM_PEAK_GBS
     fwd_s = fwd_ms * 1e-3
 
