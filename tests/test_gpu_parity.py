@@ -362,3 +362,25 @@ def test_workload_full_size(name):
         got = D.view(-1, w.N)[torch.from_numpy(rows).to(DEV)].cpu().numpy()
         np.testing.assert_array_equal(got, oracle.scores_rows(oq, ok_, w.d, rows))
     del D
+
+
+@pytest.mark.parametrize("N", [65536, 65535])
+def test_forward_at_the_largest_row_length(N):
+    """Rows of the largest length the ABI accepts (65536 keys, and one less for a ragged last
+    tile) through the streaming kernel: sampled rows against the oracle, V^ and the sign words
+    exactly as the oracle computes them, and an all-zero V channel giving exact zeros."""
+    _say(f"forward at N={N}")
+    inp = W.custom(1, 1, N, 64, "f16", "none", seed=N)
+    inp["v"][0, 0, :, 5] = 0  # a_c = 0: V^ and the output channel are 0
+    g = gpu_pipeline(inp)
+    o = g["o"].cpu().numpy()
+    vmax = float(np.abs(inp["v"].astype(np.float64)).max())
+    rows = _sample_rows(1, 1, N, 48, seed=3)
+    ref = oracle.forward_rows(inp["q"], inp["k"], inp["v"], rows, None, oracle.BIAS_NONE)
+    assert_o(o.reshape(-1, 64)[rows], ref, vmax, f"N={N} (sampled rows)")
+    assert not np.any(o[0, 0, :, 5])
+    oq, _ = oracle.pack_qk(inp["q"].astype(np.float64))
+    np.testing.assert_array_equal(_u32(g["qb"]), oq)
+    ovq, _, oamax = oracle.quant_v(inp["v"].astype(np.float64), with_amax=True)
+    np.testing.assert_array_equal(g["vs"].cpu().numpy(), oamax)
+    np.testing.assert_array_equal(np.swapaxes(g["vq"].cpu().numpy()[..., :N], 2, 3), ovq)
