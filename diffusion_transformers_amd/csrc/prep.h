@@ -146,7 +146,8 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&in)[4], uint32_t (
 // threads reduce the per-thread maxima, 256/d threads per channel, meeting in an LDS max),
 // IEEE 127 / a, rint -- every chunk quantised in registers -- then per 128-token block each
 // 4-token group is transposed in registers (v_perm) into one dword per channel, written to an
-// LDS tile of channel rows, and stored as rows of ldv keys; tokens >= N are written as 0.
+// LDS tile of channel rows, and stored as rows of ldv keys (16-byte stores); tokens >= N are
+// written as 0.
 // sRed: 256*VE floats, sAmax: 128 words, sT: 128 * kQuantTS bytes (16-byte aligned).
 template <typename T, int MAXC>
 __device__ __forceinline__ void quant_head_regs(const T* __restrict__ v, int N, int d, int64_t ldv, int64_t bh,
@@ -249,11 +250,11 @@ __device__ __forceinline__ void quant_head_regs(const T* __restrict__ v, int N, 
             }
         }
         __syncthreads();
-        const int dw = nb / 4;  // dwords per row
-        for (int id = tid; id < d * dw; id += 256) {
-            const int c = id / dw, q = id - c * dw;
-            *reinterpret_cast<uint32_t*>(vqh + (int64_t)c * ldv + j0 + 4 * q) =
-                *reinterpret_cast<const uint32_t*>(sT + c * kQuantTS + 4 * q);
+        const int qw = nb / 16;  // 16-byte pieces per row: one global store each
+        for (int id = tid; id < d * qw; id += 256) {
+            const int c = id / qw, q = id - c * qw;
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(sT + c * kQuantTS + 16 * q);
+            *reinterpret_cast<uint4*>(vqh + (int64_t)c * ldv + j0 + 16 * q) = make_uint4(src[0], src[1], src[2], src[3]);
         }
     }
 }
