@@ -16,33 +16,24 @@ namespace binattn {
 
 // One 8-channel fp16 chunk: the sign byte (bit e = x_e >= 0, so -0.0 counts as +1) and the
 // fp32 sum of |x_e| (a fixed chain of v_dot2_f32_f16 against 1.0, so every caller gets the same
-// rounding).  Packed: +0.0 is added to both halves (turning -0.0 into +0.0), the four sign-carrying
-// high bytes of each half are gathered with v_perm and compressed with one multiply.
+// rounding).  The sign test reads the bit patterns of a channel pair: a half is negative when
+// its sign bit is set and its magnitude is not 0, and magnitude + 0x7FFF carries into the sign
+// position exactly when the magnitude is not 0 (no carry crosses into the other half).
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t sign_nibble(uint32_t hw0, uint32_t hw1) {
-    // bytes 1 and 3 of each word hold the signs of its two halves (bit 7 of each byte)
-    const uint32_t z = __builtin_amdgcn_perm(hw1, hw0, 0x07050301u);
-    const uint32_t pos = (~z >> 7) & 0x01010101u;  // 1 where the sign bit is clear
-    return (pos * 0x01020408u) >> 24;              // byte k -> bit 24 + k
-}
-
 __device__ __forceinline__ void chunk_sign_abs(const h8& x, uint32_t& byte, float& sum) {
-    uint32_t w[4];
-    const h2 zero = h2{(_Float16)0, (_Float16)0};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const h2 pair = h2{x[2 * i], x[2 * i + 1]} + zero;  // -0.0 + 0.0 = +0.0
-        w[i] = __builtin_bit_cast(uint32_t, pair);
-    }
-    byte = sign_nibble(w[0], w[1]) | (sign_nibble(w[2], w[3]) << 4);
     const h2 one = h2{(_Float16)1, (_Float16)1};
+    uint32_t y = 0;  // channel 2i >= 0 at bit 2i, channel 2i+1 >= 0 at bit 16 + 2i
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const h2 a = __builtin_bit_cast(h2, __builtin_bit_cast(uint32_t, h2{x[2 * i], x[2 * i + 1]}) & 0x7FFF7FFFu);
-        acc = __builtin_amdgcn_fdot2(a, one, acc, false);
+        const uint32_t w = __builtin_bit_cast(uint32_t, h2{x[2 * i], x[2 * i + 1]});
+        const uint32_t mag = w & 0x7FFF7FFFu;
+        const uint32_t nonneg = ~(w & (mag + 0x7FFF7FFFu)) & 0x80008000u;
+        y |= nonneg >> (15 - 2 * i);
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, mag), one, acc, false);
     }
+    byte = (y & 0x55u) | ((y >> 15) & 0xAAu);
     sum = acc;
 }
 
