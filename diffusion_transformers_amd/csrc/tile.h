@@ -866,6 +866,17 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
     }
     __syncthreads();
 
+    // relative position: the key part of each tile's window offset for this lane's key run
+    // (keys 64 t + 16 g ..), so a block adds only its query's part
+    int krel[BIAS == BK_RELPOS ? NTL : 1];
+    if (BIAS == BK_RELPOS) {
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+            const int jg = t * kBC + 16 * g, rj = jg / a.gw, cj = jg % a.gw;
+            krel[t] = (a.gh - 1 - rj) * a.wrs + (a.gw - 1 - cj);
+        }
+    }
+
     for (int qb = qb_lo; qb < qb_hi; ++qb) {
         // The staged tiles do not change across query blocks; reading them through an offset the
         // compiler cannot see is zero keeps it from hoisting every tile's operands out of this
@@ -889,11 +900,10 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
             lq.dseed = v4f{seed, seed, seed, seed};
             lq.cq = qmu * a.qk_scale;
         }
-        int ri = 0, ci = 0, win_lo = 0;
+        int qrel = 0;  // relative position: the query's part of the window offsets
         if (BIAS == BK_RELPOS) {
-            ri = lq.qi / a.gw;
-            ci = lq.qi % a.gw;
-            win_lo = window_lo(qb);
+            const int ri = lq.qi / a.gw, ci = lq.qi % a.gw;
+            qrel = (ri - window_lo(qb)) * a.wrs + ci;
         }
 
         // ---- pass 1: scores and row max
@@ -909,11 +919,8 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
                     const int run = nar ? 4 : 16;  // keys per lane
                     const int jg = t * kBC + run * g;
                     int idx0 = run - 1;
-                    if (BIAS == BK_RELPOS) {
-                        const int rj = jg / a.gw, cj = jg % a.gw;
-                        idx0 = (ri - rj + a.gh - 1 - win_lo) * a.wrs + (ci - cj + a.gw - 1);
-                        if (jg >= N) idx0 = run - 1;  // the whole run is past N and masked; keep reads in the window
-                    }
+                    if (BIAS == BK_RELPOS)  // (a run wholly past N is masked; its reads stay in the window)
+                        idx0 = jg >= N ? run - 1 : qrel + krel[t];
                     if (nar)
                         tile_scores4<NT, BIAS>(L[t].k, L[t].mu, lq, bias[LONG ? (t & 1) : t], sWin + idx0 - 3, N - jg,
                                                S4, mloc);
