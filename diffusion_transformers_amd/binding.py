@@ -101,6 +101,12 @@ def vq_ld(N: int) -> int:
     return _lib.binattn_vq_ld(N)
 
 
+def vq_token_major(vq: torch.Tensor, N: int) -> torch.Tensor:
+    """The canonical [B,H,N,d] view of a quantised V in the library's channel-major layout
+    [B,H,d,ldv] (keys past N dropped): a strided view, no copy and no arithmetic."""
+    return vq[..., :N].transpose(2, 3)
+
+
 def pack_qk(x: torch.Tensor, bits=None, mu=None):
     """x [B,H,N,d] (fp16/fp32, cuda, contiguous) -> (bits uint32-as-int32 [B,H,N,W], mu fp32 [B,H,N])."""
     B, H, N, d = x.shape

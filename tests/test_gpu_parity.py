@@ -350,7 +350,7 @@ def test_workload_full_size(name):
     np.testing.assert_allclose(g["qm"].cpu().numpy(), oqm, rtol=w.d * 2.0**-24)
     ovq, _, oamax = oracle.quant_v(inp["v"].astype(np.float64), with_amax=True)
     np.testing.assert_array_equal(g["vs"].cpu().numpy(), oamax)
-    np.testing.assert_array_equal(np.swapaxes(g["vq"].cpu().numpy()[..., :w.N], 2, 3), ovq)
+    np.testing.assert_array_equal(_b().vq_token_major(g["vq"], w.N).cpu().numpy(), ovq)
     # integer scores: whole matrix when it fits, sampled rows otherwise
     ok_, _ = oracle.pack_qk(inp["k"].astype(np.float64))
     D = _b().scores_i32(g["qb"], g["kb"], w.d)
