@@ -384,3 +384,42 @@ def test_forward_at_the_largest_row_length(N):
     ovq, _, oamax = oracle.quant_v(inp["v"].astype(np.float64), with_amax=True)
     np.testing.assert_array_equal(g["vs"].cpu().numpy(), oamax)
     np.testing.assert_array_equal(np.swapaxes(g["vq"].cpu().numpy()[..., :N], 2, 3), ovq)
+
+
+def _random_cases(n, seed):
+    """Seeded shapes across the launch choices: short, long and streamed rows, whole, ragged and
+    narrow last tiles, every head-dimension class, both dtypes, the three bias kinds."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        d = int(rng.choice([8, 16, 24, 32, 40, 48, 56, 64, 64, 64, 72, 80, 96, 104, 120, 128]))
+        dt = "f16" if rng.random() < 0.75 else "f32"
+        bias = str(rng.choice(["none", "dense", "relpos"]))
+        if bias == "relpos":
+            gw = int(rng.choice([16, 32, 48]))
+            gh = int(rng.integers(1, max(2, 1200 // gw)))
+            N, grid = gh * gw, (gh, gw)
+        else:
+            N, grid = int(rng.integers(1, 1200)), ()
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        cases.append((B, H, N, d, dt, bias, grid))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(40, seed=2026), ids=lambda c: "x".join(map(str, c[:4])) + f"-{c[4]}-{c[5]}")
+def test_attention_random_shapes(case):
+    """binattn_attention (whichever way the shape runs: one kernel, prepare + head-resident
+    forward, or prepare + streaming forward) against the oracle on seeded random shapes."""
+    B, H, N, d, dt, bias, grid = case
+    _say(f"attention random {case}")
+    inp = W.custom(B, H, N, d, dt, bias, grid, seed=7 * N + d)
+    b = _b()
+    bt, kind = None, b.BIAS_NONE
+    if bias == "dense":
+        bt, kind = b.aligned_dense_bias(_t(inp["bias"])), b.BIAS_DENSE
+    elif bias == "relpos":
+        bt, kind = _t(inp["bias"]), b.BIAS_RELPOS
+    o = b.attention(_t(inp["q"]), _t(inp["k"]), _t(inp["v"]), bt, kind, grid or None)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["bias"], oracle_kind(inp["workload"]), grid=grid or None)
+    assert_o(o.cpu().numpy(), ref, float(np.abs(inp["v"].astype(np.float64)).max()), str(case))
