@@ -58,13 +58,16 @@ def _load():
     lib.binattn_attention.restype = i32
     lib.binattn_attention_one_kernel.argtypes = [i32] * 9
     lib.binattn_attention_one_kernel.restype = i32
+    lib.binattn_keep_plan.argtypes = [i64, i32, i32, i32, ctypes.POINTER(ctypes.c_int)]
+    lib.binattn_keep_plan.restype = i32
     return lib
 
 
 _lib = _load()
 EXPORTS = ["binattn_abi_version", "binattn_strerror", "binattn_words", "binattn_vq_ld", "binattn_pack_qk",
            "binattn_quant_v", "binattn_forward", "binattn_scores_i32", "binattn_qk_rowstats",
-           "binattn_prepare", "binattn_attention_workspace", "binattn_attention", "binattn_attention_one_kernel"]
+           "binattn_prepare", "binattn_attention_workspace", "binattn_attention", "binattn_attention_one_kernel",
+           "binattn_keep_plan"]
 QK_MFMA, QK_POPCOUNT = 0, 1
 
 
@@ -209,6 +212,13 @@ def attention_workspace(B, H, N, d, device):
     if n < 0:
         raise BinAttnError("binattn_attention_workspace", -2)
     return torch.empty((n,), dtype=torch.uint8, device=device)
+
+
+def keep_plan(nheads, nqb, slots, fused=False):
+    """The head-resident forward's workgroup plan (a, f, b, r) (binattn_keep_plan; host only)."""
+    out = (ctypes.c_int * 4)()
+    _check("binattn_keep_plan", _lib.binattn_keep_plan(int(nheads), int(nqb), int(slots), int(bool(fused)), out))
+    return tuple(out)
 
 
 def attention_one_kernel(B, H, N, d, dtype, bias_kind=BIAS_NONE, bias_dtype=None, grid=None):

@@ -221,6 +221,13 @@ int binattn_attention_one_kernel(int dtype, int bias_kind, int bias_dtype, int g
     return attention_fused_applies(f, bias_kind) ? 1 : 0;
 }
 
+int binattn_keep_plan(int64_t nheads, int nqb, int slots, int fused, int* plan) {
+    if (!plan || nheads <= 0 || nqb <= 0 || slots <= 0) return BINATTN_EINVAL;
+    if (nheads > (int64_t)1 << 24 || nqb > keep_plan_max_blocks()) return BINATTN_EUNSUPPORTED;
+    keep_plan_host(nheads, nqb, slots, fused != 0, plan);
+    return BINATTN_OK;
+}
+
 int binattn_attention(const void* q, const void* k, const void* v, int dtype, int bias_kind, int bias_dtype,
                       const void* bias, int64_t bias_ld, int grid_h, int grid_w, int B, int H, int N, int d,
                       void* out, int out_dtype, void* workspace, int64_t workspace_bytes, void* stream) {

@@ -404,4 +404,14 @@ bool relpos_window_fits(int gw) {
     return rows * (2 * gw - 1) <= kRelposWin;
 }
 
+int keep_plan_max_blocks() { return kLongTiles; }
+
+void keep_plan_host(int64_t nheads, int nqb, int slots, bool fused, int plan[4]) {
+    const KeepPlan p = keep_plan(nheads, nqb, slots, fused ? 3.0 : 0.5);
+    plan[0] = p.a;
+    plan[1] = p.f;
+    plan[2] = p.b;
+    plan[3] = p.r;
+}
+
 }  // namespace binattn

@@ -44,5 +44,10 @@ bool attention_fused_applies(const FwdArgs& a, int bias_kind);
 hipError_t launch_scores(const FwdArgs& a, hipStream_t s);
 hipError_t launch_qk_stats(const FwdArgs& a, int method, float* rowmax, float* rowsum, hipStream_t s);
 bool relpos_window_fits(int gw);
+// The head-resident kernel's workgroup plan {a, f, b, r} for nheads heads of nqb query blocks
+// (nqb <= keep_plan_max_blocks()) on `slots` resident workgroups: per head, a segments of f
+// blocks then b segments of r blocks; fused: the whole-attention variant (costlier staging).
+int keep_plan_max_blocks();
+void keep_plan_host(int64_t nheads, int nqb, int slots, bool fused, int plan[4]);
 
 }  // namespace binattn

@@ -204,6 +204,22 @@ int binattn_attention(const void* q, const void* k, const void* v, int dtype, in
                       const void* bias, int64_t bias_ld, int grid_h, int grid_w, int B, int H, int N, int d,
                       void* out, int out_dtype, void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * binattn_keep_plan -- inspection export (host only, no device call): how the head-resident
+ * forward splits the query blocks of every (b, h) over workgroups.  nheads = B*H heads of
+ * nqb = ceil(N / 64) query blocks (1 <= nqb <= 10, the rows that kernel takes), `slots` resident
+ * workgroups on the device (the library itself uses the occupancy the runtime reports times the
+ * compute units), fused != 0 for the whole-attention variant of binattn_attention.
+ *   plan[4] (caller-owned) receives {a, f, b, r}: each head is covered by a segments of f query
+ *   blocks (blocks [k f, k f + f), k < a, cut at nqb) followed by b segments of r blocks
+ *   (from block a f on); a launch is 8 * ceil(nheads / 8) * (a + b) workgroups, workgroup w on
+ *   XCD w % 8, each XCD taking a contiguous eighth of the heads.
+ * The plan minimises a list-scheduling model of one XCD's makespan (a head's staging counts as
+ * half a query block's work, three for the whole-attention variant).  BINATTN_EINVAL for a NULL
+ * plan or non-positive sizes, BINATTN_EUNSUPPORTED for nqb > 10 or nheads > 2^24.
+ */
+int binattn_keep_plan(int64_t nheads, int nqb, int slots, int fused, int* plan);
+
 #define BINATTN_QK_MFMA 0
 #define BINATTN_QK_POPCOUNT 1
 int binattn_qk_rowstats(const uint32_t* q_bits, const uint32_t* k_bits, int B, int H, int N, int d, int method,

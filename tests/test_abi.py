@@ -152,3 +152,59 @@ def test_valid_arguments_without_a_device_report_enodevice(lib):
     assert _fwd(lib, kind=2, bias=_a(4096), gh=16, gw=16) == -4
     assert lib.binattn_prepare(_a(256), _a(512), _a(768), 1, 2, 3, 197, 64, _a(1024), _a(1280), _a(1536),
                                _a(1792), _a(2048), _a(2304), None) == -4
+
+
+def _plan_cover(nheads, nqb, plan):
+    """(head, query block) -> how many workgroups of the launch compute it: the launch's
+    workgroup-to-work mapping (XCD = workgroup % 8, a contiguous eighth of the heads per XCD,
+    first the `a` segments of f blocks of each head, then the `b` segments of r blocks)."""
+    a, f, b, r = plan
+    grid = 8 * (-(-nheads // 8)) * (a + b)
+    cover = {}
+    for w in range(grid):
+        xcd, slot = w % 8, w // 8
+        hx0 = nheads * xcd // 8
+        hx = nheads * (xcd + 1) // 8 - hx0
+        if slot < hx * a:
+            bh, lo, ln = hx0 + slot // a, (slot % a) * f, f
+        else:
+            s2 = slot - hx * a
+            if s2 >= hx * b:
+                continue
+            bh, lo, ln = hx0 + s2 // b, a * f + (s2 % b) * r, r
+        for qb in range(lo, min(nqb, lo + ln)):
+            cover[(bh, qb)] = cover.get((bh, qb), 0) + 1
+    return cover
+
+
+@pytest.mark.parametrize("fused", [0, 1])
+def test_keep_plan_covers_every_block_once(lib, fused):
+    """The head-resident forward's workgroup plan (host logic, no device): for head counts
+    below, at and above the XCD count and the model shapes (DeiT-S 384, DiT-XL/2 1024 heads),
+    rows of 1..10 query blocks and 2..4 resident workgroups per CU, every (head, block) is
+    computed by exactly one workgroup."""
+    from diffusion_transformers_amd import binding
+    for nheads in (1, 3, 8, 13, 100, 384, 1024):
+        for nqb in range(1, 11):
+            for slots in (512, 768, 1024):
+                plan = binding.keep_plan(nheads, nqb, slots, fused)
+                a, f, b, r = plan
+                assert a >= 1 and f >= 1 and b >= 0 and r >= 1, plan
+                assert a * f + b * r >= nqb, plan
+                cover = _plan_cover(nheads, nqb, plan)
+                assert len(cover) == nheads * nqb and set(cover.values()) == {1}, (nheads, nqb, slots, plan)
+
+
+def test_keep_plan_shapes_and_validation(lib):
+    """Whole heads where they fill the device; split heads where whole ones would leave most
+    resident slots idle; argument checks."""
+    from diffusion_transformers_amd import binding
+    assert binding.keep_plan(1024, 4, 768, True) == (1, 4, 0, 1)   # DiT-XL/2 one kernel: whole heads
+    a, f, b, r = binding.keep_plan(8, 10, 512, False)              # 8 heads of 10 blocks on 512 slots
+    assert a + b > 1                                                # split, not one workgroup per head
+    out = (ctypes.c_int * 4)()
+    assert lib.binattn_keep_plan(0, 4, 512, 0, out) == -1
+    assert lib.binattn_keep_plan(8, 0, 512, 0, out) == -1
+    assert lib.binattn_keep_plan(8, 4, 0, 0, out) == -1
+    assert lib.binattn_keep_plan(8, 4, 512, 0, None) == -1
+    assert lib.binattn_keep_plan(8, 11, 512, 0, out) == -2
