@@ -1,0 +1,50 @@
+"""bench.py's output contract: one JSON line with the metric, the step time, the roofline of
+the dominant kernel and the oracle baseline; more than one GPU is refused."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BENCH = os.path.join(ROOT, "bench.py")
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The build runs on one GPU: --gpus above 1 exits with status 2 and says so (before any
+    device is touched)."""
+    r = subprocess.run([sys.executable, BENCH, "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+@pytest.mark.gpu
+def test_bench_prints_one_json_line():
+    """A short default-workload run: exactly one JSON line on stdout, with the fields the
+    metric needs and a roofline whose fraction is achieved / peak."""
+    print("bench.py --steps 8 (subprocess)", flush=True)
+    r = subprocess.run([sys.executable, "-u", BENCH, "--steps", "8", "--warmup", "4", "--rotate", "2",
+                        "--cpu-seconds", "1"], capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout[-2000:]
+    res = json.loads(lines[0])
+    sys.path.insert(0, ROOT)
+    import bench
+    assert res["metric"] == bench.METRIC
+    assert res["n_gpus"] == 1 and res["steps"] == 8 and res["higher_is_better"] is True
+    assert res["unit"] == "TOPS" and res["value"] > 0 and res["ms_per_step"] > 0
+    assert res["vs_baseline"] is None and res["data"] == "synthetic"
+    assert res["config"]["workload"] == "deit_s_224"
+    ops = 4.0 * 64 * 6 * 197 * 197 * 64
+    assert abs(res["value"] - ops / (res["ms_per_step"] * 1e-3) / 1e12) <= 1e-6 * res["value"]
+    roof = res["roofline"]
+    assert roof["bound"] in ("hbm", "mfma")
+    assert roof["unit"] == ("GB/s" if roof["bound"] == "hbm" else "TOPS")
+    assert 0 < roof["achieved"] and 0 < roof["frac"] < 1
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) <= 1e-9
+    assert roof["traffic"] is None or roof["traffic"] > 0
+    cpu = res["cpu_baseline"]
+    assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
