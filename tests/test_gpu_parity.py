@@ -423,3 +423,33 @@ def test_attention_random_shapes(case):
     torch.cuda.synchronize()
     ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["bias"], oracle_kind(inp["workload"]), grid=grid or None)
     assert_o(o.cpu().numpy(), ref, float(np.abs(inp["v"].astype(np.float64)).max()), str(case))
+
+
+@pytest.mark.parametrize("B,H,N,d,bias,grid,bias_f32", [(2, 2, 197, 64, "dense", (), False),
+                                                        (2, 2, 197, 64, "dense", (), True),
+                                                        (1, 2, 256, 72, "relpos", (16, 16), False),
+                                                        (1, 2, 256, 72, "relpos", (16, 16), True),
+                                                        (1, 2, 300, 64, "dense", (), False),
+                                                        (1, 1, 1500, 64, "none", (), False)])
+def test_attention_fp32_output_and_bias(B, H, N, d, bias, grid, bias_f32):
+    """binattn_attention from fp16 Q, K, V into an fp32 O, with the bias in fp16 or fp32, on
+    one-kernel and two-launch shapes: equal to the four-call pipeline with the same bias
+    bit for bit, and to the oracle within the tolerance."""
+    _say(f"attention fp32 out {B}x{H}x{N}x{d} {bias} bias_f32={bias_f32}")
+    inp = W.custom(B, H, N, d, "f16", bias, grid, seed=5 * N + d)
+    b = _b()
+    bt, kind = None, b.BIAS_NONE
+    if bias != "none":
+        src = _t(inp["bias"].astype(np.float32 if bias_f32 else np.float16))  # the same values either way
+        if bias == "dense":
+            bt, kind = b.aligned_dense_bias(src), b.BIAS_DENSE
+        else:
+            bt, kind = src.contiguous(), b.BIAS_RELPOS
+    q, k, v = _t(inp["q"]), _t(inp["k"]), _t(inp["v"])
+    o = b.attention(q, k, v, bt, kind, grid or None, out_dtype=torch.float32)
+    qb, qm, kb, km, vq, vs = b.prepare(q, k, v)
+    o2 = b.forward(qb, qm, kb, km, vq, vs, d, bt, kind, grid or None, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float32 and torch.equal(o, o2)
+    ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["bias"], oracle_kind(inp["workload"]), grid=grid or None)
+    assert_o(o.cpu().numpy(), ref, float(np.abs(inp["v"].astype(np.float64)).max()), f"{B}x{H}x{N}x{d}-{bias}")
