@@ -35,23 +35,25 @@ __device__ __forceinline__ v4f mfma_f4(v4i a, v4i b, v4f c) {
                                                            0, 0, 0);
 }
 
-// Eight bits -> bit 0 of eight nibbles: bit k (k < 4) to nibble 2k, bit 4 + k to nibble 2k + 1.
-// The channel order inside a dword is immaterial as long as both MFMA operands use the same one.
-__device__ __forceinline__ uint32_t spread8_nib(uint32_t x) {
-    return ((x & 0xFu) * 0x00204081u & 0x01010101u) | (((x >> 4) & 0xFu) * 0x00204081u & 0x01010101u) << 4;
-}
-
 // E2M1 codes used as exact small integers: 1.0 = 0x2, 2.0 = 0x4, -2.0 = 0xC.
-// 32 sign bits -> 32 fp4 values {0, 1.0} (bit set: 1.0), four dwords (dword i: bits 8i .. 8i+7).
+// A lane's 32 channels are laid out with channel 4j + i of its 32-bit sign word in dword i,
+// nibble j.  The order inside the operand is immaterial to the dot product as long as both MFMA
+// operands use the same one, and this one moves every bit with one shift and one mask: bit
+// 4j + i sits at bit i of nibble j already.
+// 32 sign bits -> 32 fp4 values {0, 1.0} (bit set: 1.0): code bit 1 of each nibble.
 __device__ __forceinline__ void unpack_bits32_f4(uint32_t w, uint32_t out[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = spread8_nib((w >> (8 * i)) & 0xFFu) << 1;
+    out[0] = (w << 1) & 0x22222222u;
+    out[1] = w & 0x22222222u;
+    out[2] = (w >> 1) & 0x22222222u;
+    out[3] = (w >> 2) & 0x22222222u;
 }
 
-// 32 sign bits -> 32 fp4 values {+2.0, -2.0} (bit set: +2.0), four dwords, same order.
+// 32 sign bits -> 32 fp4 values {+2.0, -2.0} (bit set: +2.0; 0xC ^ 0x8 = 0x4), same order.
 __device__ __forceinline__ void unpack_signs32_f4x2(uint32_t w, uint32_t out[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = 0xCCCCCCCCu ^ (spread8_nib((w >> (8 * i)) & 0xFFu) << 3);
+    out[0] = 0xCCCCCCCCu ^ ((w << 3) & 0x88888888u);
+    out[1] = 0xCCCCCCCCu ^ ((w << 2) & 0x88888888u);
+    out[2] = 0xCCCCCCCCu ^ ((w << 1) & 0x88888888u);
+    out[3] = 0xCCCCCCCCu ^ (w & 0x88888888u);
 }
 
 // Raw buffer resource over [base, base + bytes): loads past the end read as zero.

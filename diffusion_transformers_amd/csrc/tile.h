@@ -228,13 +228,15 @@ __device__ __forceinline__ void colsum_store(const int (&cs)[VCH], int* sCol) {
 }
 
 // Q operand (B of the QK MFMA) for one lane from word g of its query's signs: fp4 2*sign of
-// channels 32g .. 32g+31, 0 past d (d is a multiple of 8, so whole dwords are dropped).
+// channels 32g .. 32g+31; all zero for a group wholly past d (whose lanes read group 0's K rows).
+// Channels past d inside the last group keep a nonzero code: their K codes are 0 (the K words
+// are masked to d before unpacking), so those products vanish.
 __device__ __forceinline__ v4i q_operand(uint32_t word, bool live, int d, int g) {
     uint32_t o[4];
     unpack_signs32_f4x2(word, o);
     v4i q;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = (live && 32 * g + 8 * i < d) ? (int)o[i] : 0;
+    for (int i = 0; i < 4; ++i) q[i] = (live && 32 * g < d) ? (int)o[i] : 0;
     return q;
 }
 
