@@ -87,6 +87,71 @@ def _p(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t, name, shape, dtypes, device=None):
+    """Marshalling check: t is a dense (contiguous) device tensor of the given shape and dtype.
+    The library reads raw pointers as dense row-major storage, so a strided view (for example a
+    permuted qkv projection) would be read as the wrong elements: it is refused here instead."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise ValueError(f"{name} must live on {device or 'a cuda device'} (got {t.device})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {[str(x) for x in dtypes]}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (call .contiguous() on strided views)")
+
+
+_FLOATS = (torch.float16, torch.float32)
+
+
+def _need_qkv(*xs, names=("q", "k", "v")):
+    """q, k, v: 4-D [B,H,N,d], contiguous, one dtype (fp16 or fp32), one device."""
+    x0 = xs[0]
+    if not isinstance(x0, torch.Tensor) or x0.dim() != 4:
+        raise ValueError(f"{names[0]} must be a 4-D tensor [B,H,N,d]")
+    for x, n in zip(xs, names):
+        _need(x, n, x0.shape, (x0.dtype,) if x0.dtype in _FLOATS else _FLOATS, x0.device)
+    return x0.shape
+
+
+def _need_bias(bias, bias_kind, grid, H, N, device):
+    """Bias marshalling: None for BIAS_NONE; dense [H,N,ld] with ld >= N; table [H,(2gh-1)(2gw-1)]."""
+    if bias_kind == BIAS_NONE:
+        if bias is not None:
+            raise ValueError("bias given with bias_kind BIAS_NONE")
+        return
+    if bias is None:
+        raise ValueError("bias_kind needs a bias tensor")
+    if bias_kind == BIAS_DENSE:
+        if bias.dim() != 3 or bias.shape[0] != H or bias.shape[1] != N or bias.shape[2] < N:
+            raise ValueError(f"dense bias must be [H={H}, N={N}, ld>=N], got {tuple(bias.shape)}")
+        _need(bias, "bias", bias.shape, _FLOATS, device)
+    elif bias_kind == BIAS_RELPOS:
+        if grid is None or len(grid) != 2:
+            raise ValueError("relative-position bias needs grid=(gh, gw)")
+        gh, gw = grid
+        _need(bias, "bias", (H, (2 * gh - 1) * (2 * gw - 1)), _FLOATS, device)
+    else:
+        raise ValueError(f"unknown bias_kind {bias_kind}")
+
+
+def _need_packed(q_bits, q_mu, k_bits, k_mu, vq, vamax, d):
+    """Packed forward inputs: bits [B,H,N,W] int32, mu [B,H,N] fp32, vq [B,H,d,ldv] int8, vamax [B,H,d]."""
+    if not isinstance(q_bits, torch.Tensor) or q_bits.dim() != 4:
+        raise ValueError("q_bits must be a 4-D tensor [B,H,N,W]")
+    B, H, N, _ = q_bits.shape
+    dev = q_bits.device
+    _need(q_bits, "q_bits", (B, H, N, words(d)), (torch.int32,), dev)
+    _need(k_bits, "k_bits", (B, H, N, words(d)), (torch.int32,), dev)
+    _need(q_mu, "q_mu", (B, H, N), (torch.float32,), dev)
+    _need(k_mu, "k_mu", (B, H, N), (torch.float32,), dev)
+    _need(vq, "vq", (B, H, d, vq_ld(N)), (torch.int8,), dev)
+    _need(vamax, "vamax", (B, H, d), (torch.float32,), dev)
+    return B, H, N, dev
+
+
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -112,11 +177,13 @@ def vq_token_major(vq: torch.Tensor, N: int) -> torch.Tensor:
 
 def pack_qk(x: torch.Tensor, bits=None, mu=None):
     """x [B,H,N,d] (fp16/fp32, cuda, contiguous) -> (bits uint32-as-int32 [B,H,N,W], mu fp32 [B,H,N])."""
-    B, H, N, d = x.shape
+    B, H, N, d = _need_qkv(x, names=("x",))
     if bits is None:
         bits = torch.empty((B, H, N, words(d)), dtype=torch.int32, device=x.device)
     if mu is None:
         mu = torch.empty((B, H, N), dtype=torch.float32, device=x.device)
+    _need(bits, "bits", (B, H, N, words(d)), (torch.int32,), x.device)
+    _need(mu, "mu", (B, H, N), (torch.float32,), x.device)
     _check("binattn_pack_qk", _lib.binattn_pack_qk(_p(x), _dt(x), B, H, N, d, _p(bits), _p(mu), _stream()))
     return bits, mu
 
@@ -125,11 +192,13 @@ def quant_v(v: torch.Tensor, vq=None, vamax=None):
     """v [B,H,N,d] -> (vq int8 [B,H,d,ldv] channel-major, vamax fp32 [B,H,d] channel absmax).
 
     The dequantisation scale of channel c is vamax[..., c] / 127 (fp32 division)."""
-    B, H, N, d = v.shape
+    B, H, N, d = _need_qkv(v, names=("v",))
     if vq is None:
         vq = torch.empty((B, H, d, vq_ld(N)), dtype=torch.int8, device=v.device)
     if vamax is None:
         vamax = torch.empty((B, H, d), dtype=torch.float32, device=v.device)
+    _need(vq, "vq", (B, H, d, vq_ld(N)), (torch.int8,), v.device)
+    _need(vamax, "vamax", (B, H, d), (torch.float32,), v.device)
     _check("binattn_quant_v", _lib.binattn_quant_v(_p(v), _dt(v), B, H, N, d, _p(vq), _p(vamax), _stream()))
     return vq, vamax
 
@@ -153,9 +222,11 @@ def forward(q_bits, q_mu, k_bits, k_mu, vq, vamax, d, bias=None, bias_kind=BIAS_
     bias: None; dense [H,N,ld] (ld >= N, 16-byte rows; see aligned_dense_bias); or a
     relative-position table [H,(2gh-1)(2gw-1)] with grid=(gh, gw).
     """
-    B, H, N, _ = q_bits.shape
+    B, H, N, dev = _need_packed(q_bits, q_mu, k_bits, k_mu, vq, vamax, d)
     if out is None:
-        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q_bits.device)
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=dev)
+    _need(out, "out", (B, H, N, d), _FLOATS, dev)
+    _need_bias(bias, bias_kind, grid, H, N, dev)
     bdt, ld, gh, gw = F16, 0, 0, 0
     if bias is not None:
         bdt = _dt(bias)
@@ -172,8 +243,11 @@ def forward(q_bits, q_mu, k_bits, k_mu, vq, vamax, d, bias=None, bias_kind=BIAS_
 def scores_i32(q_bits, k_bits, d, D=None):
     """Integer sign scores D [B,H,N,N] int32 through the forward kernel's QK tile code."""
     B, H, N, _ = q_bits.shape
+    _need(q_bits, "q_bits", (B, H, N, words(d)), (torch.int32,))
+    _need(k_bits, "k_bits", (B, H, N, words(d)), (torch.int32,), q_bits.device)
     if D is None:
         D = torch.empty((B, H, N, N), dtype=torch.int32, device=q_bits.device)
+    _need(D, "D", (B, H, N, N), (torch.int32,), q_bits.device)
     _check("binattn_scores_i32", _lib.binattn_scores_i32(_p(q_bits), _p(k_bits), B, H, N, d, _p(D), _stream()))
     return D
 
@@ -181,6 +255,8 @@ def scores_i32(q_bits, k_bits, d, D=None):
 def qk_rowstats(q_bits, k_bits, d, method=QK_MFMA, rowmax=None, rowsum=None):
     """Binary QK tile probe: (max_j D_ij, sum_j D_ij) per query row, fp32 [B,H,N] each."""
     B, H, N, _ = q_bits.shape
+    _need(q_bits, "q_bits", (B, H, N, words(d)), (torch.int32,))
+    _need(k_bits, "k_bits", (B, H, N, words(d)), (torch.int32,), q_bits.device)
     if rowmax is None:
         rowmax = torch.empty((B, H, N), dtype=torch.float32, device=q_bits.device)
     if rowsum is None:
@@ -192,7 +268,7 @@ def qk_rowstats(q_bits, k_bits, d, method=QK_MFMA, rowmax=None, rowsum=None):
 
 def prepare(q, k, v, qbits=None, qmu=None, kbits=None, kmu=None, vq=None, vamax=None):
     """The three input-side steps in one call: (q_bits, q_mu, k_bits, k_mu, vq, vamax)."""
-    B, H, N, d = q.shape
+    B, H, N, d = _need_qkv(q, k, v)
     dev = q.device
     if qbits is None:
         qbits = torch.empty((B, H, N, words(d)), dtype=torch.int32, device=dev)
@@ -201,6 +277,7 @@ def prepare(q, k, v, qbits=None, qmu=None, kbits=None, kmu=None, vq=None, vamax=
         kmu = torch.empty_like(qmu)
         vq = torch.empty((B, H, d, vq_ld(N)), dtype=torch.int8, device=dev)
         vamax = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    _need_packed(qbits, qmu, kbits, kmu, vq, vamax, d)
     _check("binattn_prepare", _lib.binattn_prepare(_p(q), _p(k), _p(v), _dt(q), B, H, N, d, _p(qbits), _p(qmu), _p(kbits), _p(kmu),
                                                    _p(vq), _p(vamax), _stream()))
     return qbits, qmu, kbits, kmu, vq, vamax
@@ -234,11 +311,14 @@ def attention_one_kernel(B, H, N, d, dtype, bias_kind=BIAS_NONE, bias_dtype=None
 
 def attention(q, k, v, bias=None, bias_kind=BIAS_NONE, grid=None, out_dtype=None, out=None, workspace=None):
     """Whole BinaryAttention forward from q, k, v [B,H,N,d] (fp16/fp32) -> O [B,H,N,d]."""
-    B, H, N, d = q.shape
+    B, H, N, d = _need_qkv(q, k, v)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=out_dtype or q.dtype, device=q.device)
+    _need(out, "out", (B, H, N, d), _FLOATS, q.device)
     if workspace is None:
         workspace = attention_workspace(B, H, N, d, q.device)
+    _need(workspace, "workspace", (workspace.numel(),), (torch.uint8,), q.device)
+    _need_bias(bias, bias_kind, grid, H, N, q.device)
     bdt, ld, gh, gw = F16, 0, 0, 0
     if bias is not None:
         bdt = _dt(bias)
@@ -250,3 +330,4 @@ def attention(q, k, v, bias=None, bias_kind=BIAS_NONE, grid=None, out_dtype=None
                                 _dt(out), _p(workspace), workspace.numel(), _stream())
     _check("binattn_attention", rc)
     return out
+

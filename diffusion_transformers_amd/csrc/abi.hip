@@ -42,7 +42,10 @@ int check_bias(int bias_kind, int bias_dtype, const void* bias, int64_t bias_ld,
             if (!bias) return BINATTN_EINVAL;
             if (!dtype_ok(bias_dtype)) return BINATTN_EUNSUPPORTED;
             if (bias_ld < N) return BINATTN_EINVAL;
+            if (bias_ld > ((int64_t)1 << 40)) return BINATTN_EUNSUPPORTED;
             const int64_t row_bytes = bias_ld * (bias_dtype == BINATTN_F32 ? 4 : 2);
+            // the kernels address the 16 bias rows of a wave through one 32-bit buffer extent
+            if (16 * row_bytes >= ((int64_t)1 << 31)) return BINATTN_EUNSUPPORTED;
             if (row_bytes % 16 != 0 || !aligned16(bias)) return BINATTN_EALIGN;
             break;
         }

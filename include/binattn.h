@@ -130,10 +130,13 @@ int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t
  *   m = row max of S, l = sum_j exp(S_ij - m) (fp32),
  *   P^_ij = rint(255 * exp(S_ij - m)) in [0,255],
  *   O_ic = s_c * sum_j P^_ij vq_cj / (255 * l_i)                (integer PV)
- * For N <= 256 m is the exact row max (two passes).  Longer rows are streamed over
- * key tiles with a running max: a tile is quantised against the max known after it
- * and earlier tiles are rescaled, so P^ may differ by one rounding from the
- * exact-max result.
+ * m is the exact row max (two passes over scores held on chip) for rows of at most
+ * 256 keys at any d, and for rows of at most 640 keys at d <= 64 with no bias or the
+ * dense bias.  Other rows are streamed over key tiles with a running max: a tile is
+ * quantised against the max known after it and earlier tiles are rescaled, so P^ may
+ * differ by one rounding from the exact-max result.
+ * A dense bias whose 16-row extent (16 * bias_ld * element size) reaches 2^31 bytes is
+ * BINATTN_EUNSUPPORTED.
  */
 int binattn_forward(const uint32_t* q_bits, const float* q_mu, const uint32_t* k_bits, const float* k_mu,
                     const int8_t* vq, const float* vamax, int bias_kind, int bias_dtype, const void* bias,

@@ -82,6 +82,10 @@ def test_forward_validation(lib):
     assert _fwd(lib, kind=1, bias=_a(4096), ld=255) == -1    # ld < N
     assert _fwd(lib, kind=1, bias=_a(4096), ld=260, N=257) == -3  # 520-byte rows are not 16-byte multiples
     assert _fwd(lib, kind=1, bias=_a(4100), ld=256) == -3    # misaligned base
+    # a dense bias whose 16-row byte extent does not fit a 32-bit buffer extent
+    assert _fwd(lib, kind=1, bias=_a(4096), ld=1 << 26) == -2           # fp16: 16 * 2^27 bytes = 2^31
+    assert _fwd(lib, kind=1, bias=_a(4096), ld=1 << 25, bdt=0) == -2    # fp32: 16 * 2^27 bytes
+    assert _fwd(lib, kind=1, bias=_a(4096), ld=(1 << 62)) == -2         # no 64-bit wrap in the check
     assert _fwd(lib, kind=2, bias=_a(4096), gh=16, gw=15) == -1   # grid does not cover N
     assert _fwd(lib, kind=2, bias=_a(4096), N=240, gh=16, gw=15) == -2  # gw % 16 != 0
     assert _fwd(lib, kind=2, bias=_a(4096), N=1024, gh=1, gw=1024) == -2  # window of one tile too wide
@@ -150,6 +154,7 @@ def test_valid_arguments_without_a_device_report_enodevice(lib):
     assert lib.binattn_pack_qk(_a(256), 1, 2, 3, 5, 64, _a(512), _a(1024), None) == -4
     assert _fwd(lib) == -4
     assert _fwd(lib, kind=2, bias=_a(4096), gh=16, gw=16) == -4
+    assert _fwd(lib, kind=1, bias=_a(4096), ld=(1 << 26) - 8) == -4  # the largest fp16 dense-bias stride accepted
     assert lib.binattn_prepare(_a(256), _a(512), _a(768), 1, 2, 3, 197, 64, _a(1024), _a(1280), _a(1536),
                                _a(1792), _a(2048), _a(2304), None) == -4
 

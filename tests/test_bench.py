@@ -22,11 +22,14 @@ def test_bench_refuses_more_than_one_gpu():
 
 @pytest.mark.gpu
 def test_bench_prints_one_json_line():
-    """A short default-workload run: exactly one JSON line on stdout, with the fields the
-    metric needs and a roofline whose fraction is achieved / peak."""
-    print("bench.py --steps 8 (subprocess)", flush=True)
-    r = subprocess.run([sys.executable, "-u", BENCH, "--steps", "8", "--warmup", "4", "--rotate", "2",
-                        "--cpu-seconds", "1"], capture_output=True, text=True, timeout=300, cwd=ROOT)
+    """A short default-workload run: exactly one JSON line on stdout, with the fields the metric
+    needs, the requested step and warm-up counts exactly (7 steps over 2 rotated sets: three
+    whole cycles and one more), a roofline whose fraction is achieved / peak, and the target
+    shape's own record."""
+    print("bench.py --steps 7 --warmup 3 (subprocess)", flush=True)
+    r = subprocess.run([sys.executable, "-u", BENCH, "--steps", "7", "--warmup", "3", "--rotate", "2",
+                        "--targets", "dit_xl2_256", "--cpu-seconds", "1"], capture_output=True, text=True,
+                       timeout=300, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.strip()]
     assert len(lines) == 1, r.stdout[-2000:]
@@ -34,11 +37,13 @@ def test_bench_prints_one_json_line():
     sys.path.insert(0, ROOT)
     import bench
     assert res["metric"] == bench.METRIC
-    assert res["n_gpus"] == 1 and res["steps"] == 8 and res["higher_is_better"] is True
+    assert res["n_gpus"] == 1 and res["steps"] == 7 and res["warmup"] == 3 and res["higher_is_better"] is True
     assert res["unit"] == "TOPS" and res["value"] > 0 and res["ms_per_step"] > 0
     assert res["vs_baseline"] is None and res["data"] == "synthetic"
-    assert res["config"]["workload"] == "deit_s_224"
-    ops = 4.0 * 64 * 6 * 197 * 197 * 64
+    cfg = res["config"]
+    assert cfg["workload"] == "highres_16k" and (cfg["B"], cfg["H"], cfg["N"], cfg["d"]) == (2, 16, 16384, 64)
+    assert cfg["rotated_input_sets"] == 2
+    ops = 4.0 * 2 * 16 * 16384 * 16384 * 64
     assert abs(res["value"] - ops / (res["ms_per_step"] * 1e-3) / 1e12) <= 1e-6 * res["value"]
     roof = res["roofline"]
     assert roof["bound"] in ("hbm", "mfma")
@@ -46,5 +51,15 @@ def test_bench_prints_one_json_line():
     assert 0 < roof["achieved"] and 0 < roof["frac"] < 1
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) <= 1e-9
     assert roof["traffic"] is None or roof["traffic"] > 0
+    t = res["targets"]["dit_xl2_256"]
+    assert (t["B"], t["H"], t["N"], t["d"]) == (64, 16, 256, 72)
+    assert t["ms_per_step"] > 0 and t["fwd_ms_per_call"] > 0 and 0 < t["fwd_hbm_frac"] < 1
     cpu = res["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
+
+
+def test_bench_refuses_bad_counts():
+    """--steps below 1 or a negative --warmup exit with status 2 before any device is touched."""
+    for extra in (["--steps", "0"], ["--warmup", "-1"]):
+        r = subprocess.run([sys.executable, BENCH, *extra], capture_output=True, text=True, timeout=120)
+        assert r.returncode == 2 and r.stdout == ""

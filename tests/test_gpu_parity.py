@@ -51,9 +51,22 @@ def gpu_pipeline(inp, out_dtype=None):
         bias, kind, grid = _t(inp["bias"]), b.BIAS_RELPOS, w.grid
     if out_dtype is None:
         out_dtype = torch.float32 if w.dtype == "f32" else torch.float16
-    o = b.forward(qb, qm, kb, km, vq, vs, w.d, bias, kind, grid, out_dtype=out_dtype)
+    o = nan_out(q.shape, out_dtype)
+    b.forward(qb, qm, kb, km, vq, vs, w.d, bias, kind, grid, out=o)
     torch.cuda.synchronize()
+    assert_written(o)
     return dict(qb=qb, qm=qm, kb=kb, km=km, vq=vq, vs=vs, o=o)
+
+
+def nan_out(shape, dtype):
+    """An output buffer pre-filled with NaN, so that any element a launch leaves unwritten shows."""
+    return torch.full(tuple(shape), float("nan"), dtype=dtype, device=DEV)
+
+
+def assert_written(o):
+    """Every element of a NaN-prefilled output was written (and is finite)."""
+    bad = int((~torch.isfinite(o)).sum())
+    assert bad == 0, f"{bad} of {o.numel()} output elements unwritten or not finite"
 
 
 def oracle_kind(w):
@@ -173,9 +186,10 @@ def test_prepare_equals_separate_calls(dtype, B, H, N, d):
         assert torch.equal(x, y), name
 
 
-@pytest.mark.parametrize("name", ["deit_t_toy", "deit_s_224", "dit_xl2_256"])
+@pytest.mark.parametrize("name", ["deit_t_toy", "deit_s_224", "deit_b_384", "dit_xl2_256", "highres_16k"])
 def test_attention_equals_pipeline(name):
-    """binattn_attention gives exactly the output of the four separate calls, and the oracle's."""
+    """binattn_attention gives exactly the output of the four separate calls, and the oracle's:
+    every row of O for the model shapes, one whole head plus sampled rows at high resolution."""
     _say(f"attention {name}")
     w = W.BY_NAME[name]
     inp = W.make(w, seed=3)
@@ -186,12 +200,33 @@ def test_attention_equals_pipeline(name):
         bias, kind = b.aligned_dense_bias(_t(inp["bias"])), b.BIAS_DENSE
     elif w.bias == "relpos":
         bias, kind, grid = _t(inp["bias"]), b.BIAS_RELPOS, w.grid
-    o = b.attention(_t(inp["q"]), _t(inp["k"]), _t(inp["v"]), bias, kind, grid)
+    o = nan_out(g["o"].shape, g["o"].dtype)
+    b.attention(_t(inp["q"]), _t(inp["k"]), _t(inp["v"]), bias, kind, grid, out=o)
     torch.cuda.synchronize()
+    assert_written(o)
     assert torch.equal(o, g["o"])
-    rows = _sample_rows(w.B, w.H, w.N, 256, seed=2)
-    ref = oracle.forward_rows(inp["q"], inp["k"], inp["v"], rows, inp["bias"], oracle_kind(w), grid=grid)
-    assert_o(o.cpu().numpy().reshape(-1, w.d)[rows], ref, float(np.abs(inp["v"].astype(np.float64)).max()), name)
+    _check_all_rows(o.cpu().numpy(), inp, w, name)
+
+
+def _check_all_rows(o, inp, w, tag):
+    """O against the oracle on every row where the oracle takes seconds (all shapes but high
+    resolution); at high resolution on one whole head (every query of the last (b, h)) and on
+    sampled rows of the others."""
+    vmax = float(np.abs(inp["v"].astype(np.float64)).max())
+    kind, grid = oracle_kind(w), w.grid or None
+    if w.N <= 1024:
+        _say(f"  oracle: all {w.B * w.H * w.N} rows")
+        ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["bias"], kind, grid=grid)
+        assert_o(o, ref, vmax, tag + " (all rows)")
+        return
+    last = w.B * w.H - 1
+    head = np.arange(last * w.N, (last + 1) * w.N, dtype=np.int64)
+    _say(f"  oracle: whole head {last} ({w.N} rows)")
+    ref = oracle.forward_rows(inp["q"], inp["k"], inp["v"], head, inp["bias"], kind, grid=grid)
+    assert_o(o.reshape(-1, w.d)[head], ref, vmax, tag + f" (head {last}, every query)")
+    rows = _sample_rows(w.B, w.H, w.N, 384, seed=1)
+    ref = oracle.forward_rows(inp["q"], inp["k"], inp["v"], rows, inp["bias"], kind, grid=grid)
+    assert_o(o.reshape(-1, w.d)[rows], ref, vmax, tag + " (sampled rows)")
 
 
 @pytest.mark.parametrize("B,H,N,d,bias,grid", [(1, 1, 1, 64, "dense", ()), (2, 3, 17, 64, "none", ()),
@@ -332,18 +367,8 @@ def test_workload_full_size(name):
     w = W.BY_NAME[name]
     _say(f"workload {name} B={w.B} H={w.H} N={w.N} d={w.d}")
     inp = W.make(w)
-    g = gpu_pipeline(inp)
-    vmax = float(np.abs(inp["v"].astype(np.float64)).max())
-    o = g["o"].cpu().numpy()
-    kind = oracle_kind(w)
-    grid = w.grid or None
-    if w.B * w.H * w.N * w.N <= 2e6:
-        ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["bias"], kind, grid=grid)
-        assert_o(o, ref, vmax, name)
-    else:
-        rows = _sample_rows(w.B, w.H, w.N, 384, seed=1)
-        ref = oracle.forward_rows(inp["q"], inp["k"], inp["v"], rows, inp["bias"], kind, grid=grid)
-        assert_o(o.reshape(-1, w.d)[rows], ref, vmax, name + " (sampled rows)")
+    g = gpu_pipeline(inp)  # O pre-filled with NaN: every element must be written
+    _check_all_rows(g["o"].cpu().numpy(), inp, w, name)
     # packed inputs and V^ exactly as the oracle computes them
     oq, oqm = oracle.pack_qk(inp["q"].astype(np.float64))
     np.testing.assert_array_equal(_u32(g["qb"]), oq)
@@ -453,3 +478,34 @@ def test_attention_fp32_output_and_bias(B, H, N, d, bias, grid, bias_f32):
     assert o.dtype == torch.float32 and torch.equal(o, o2)
     ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["bias"], oracle_kind(inp["workload"]), grid=grid or None)
     assert_o(o.cpu().numpy(), ref, float(np.abs(inp["v"].astype(np.float64)).max()), f"{B}x{H}x{N}x{d}-{bias}")
+
+
+def test_binding_refuses_strided_and_mismatched_inputs():
+    """The binding passes raw pointers, so it refuses what the library would misread: a permuted
+    view of a [B,N,H,d] projection, q/k/v of different shapes or dtypes, and packed inputs of the
+    wrong dtype or shape -- before any launch."""
+    b = _b()
+    x = torch.randn(2, 197, 3, 64, device=DEV, dtype=torch.float16)
+    xv = x.permute(0, 2, 1, 3)  # [B,H,N,d] view, not contiguous
+    with pytest.raises(ValueError, match="contiguous"):
+        b.pack_qk(xv)
+    q = xv.contiguous()
+    with pytest.raises(ValueError, match="contiguous"):
+        b.attention(q, q, xv)
+    with pytest.raises(ValueError, match="shape"):
+        b.attention(q, q, q[:, :, :100].contiguous())
+    with pytest.raises(TypeError, match="dtype"):
+        b.attention(q, q, q.float())
+    qb, qm = b.pack_qk(q)
+    vq, va = b.quant_v(q)
+    with pytest.raises(TypeError, match="dtype"):
+        b.forward(qb, qm, qb, qm.half(), vq, va, 64)
+    with pytest.raises(ValueError, match="shape"):
+        b.forward(qb, qm, qb, qm, vq[..., :64].contiguous(), va, 64)
+    with pytest.raises(ValueError, match="dense bias"):
+        b.forward(qb, qm, qb, qm, vq, va, 64, torch.zeros(3, 197, 100, device=DEV, dtype=torch.float16),
+                  b.BIAS_DENSE)
+    torch.cuda.synchronize()
+    o = b.forward(qb, qm, qb, qm, vq, va, 64)  # the same tensors, well formed, still run
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()

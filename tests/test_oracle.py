@@ -107,6 +107,29 @@ def test_scores_equal_pm1_float_matmul(d):
     assert np.all(np.abs(D) <= d) and np.all((D - d) % 2 == 0)
 
 
+@pytest.mark.parametrize("d,N", [(72, 37), (64, 65), (33, 16)])
+def test_scores_rows_equal_pm1_float_matmul(d, N):
+    """scores_rows (the selected-rows export used to check long launches) gives, for every
+    requested flattened (b, h, i) row -- first and last head, first and last query, a ragged N --
+    the row of the +-1 float product sigma(Q) sigma(K)^T, in the order requested, and the rows of
+    scores_i32.  A row index outside [0, B*H*N) leaves its output row untouched."""
+    B, H = 2, 3
+    q = _rand((B, H, N, d), seed=300 + d)
+    k = _rand((B, H, N, d), seed=400 + d)
+    qb, _ = oracle.pack_qk(q)
+    kb, _ = oracle.pack_qk(k)
+    sq, sk = _signs_from_bits(qb, d), _signs_from_bits(kb, d)
+    brute = np.einsum("bhic,bhjc->bhij", sq, sk).astype(np.int32).reshape(B * H * N, N)
+    last = B * H * N - 1
+    rows = np.array([last, 0, N - 1, N, (B * H - 1) * N, 5 * N + N // 2, last - 1], dtype=np.int64)
+    got = oracle.scores_rows(qb, kb, d, rows)
+    np.testing.assert_array_equal(got, brute[rows])
+    np.testing.assert_array_equal(got, oracle.scores_i32(qb, kb, d).reshape(B * H * N, N)[rows])
+    out = oracle.scores_rows(qb, kb, d, np.array([-1, last + 1, 3], dtype=np.int64))
+    assert not out[:2].any()
+    np.testing.assert_array_equal(out[2], brute[3])
+
+
 def test_scores_special_cases():
     d = 72
     rng = np.random.default_rng(3)
