@@ -58,6 +58,9 @@ def _load():
     lib.binattn_attention.restype = i32
     lib.binattn_attention_one_kernel.argtypes = [i32] * 9
     lib.binattn_attention_one_kernel.restype = i32
+    lib.binattn_attention_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, vp,
+                                              i32, vp]
+    lib.binattn_attention_noalloc.restype = i32
     lib.binattn_keep_plan.argtypes = [i64, i32, i32, i32, ctypes.POINTER(ctypes.c_int)]
     lib.binattn_keep_plan.restype = i32
     return lib
@@ -67,7 +70,8 @@ _lib = _load()
 EXPORTS = ["binattn_abi_version", "binattn_strerror", "binattn_words", "binattn_vq_ld", "binattn_pack_qk",
            "binattn_quant_v", "binattn_forward", "binattn_scores_i32", "binattn_qk_rowstats",
            "binattn_prepare", "binattn_attention_workspace", "binattn_attention", "binattn_attention_one_kernel",
-           "binattn_keep_plan"]
+           "binattn_keep_plan", "binattn_attention_noalloc"]
+NOALLOC_SCRATCH_BYTES = 64 << 20  # BINATTN_NOALLOC_SCRATCH_BYTES
 QK_MFMA, QK_POPCOUNT = 0, 1
 
 
@@ -331,3 +335,24 @@ def attention(q, k, v, bias=None, bias_kind=BIAS_NONE, grid=None, out_dtype=None
     _check("binattn_attention", rc)
     return out
 
+
+def attention_noalloc(q, k, v, bias=None, bias_kind=BIAS_NONE, grid=None, out_dtype=None, out=None):
+    """attention() without a workspace: the library's own per-device scratch holds the packed
+    intermediates (binattn_attention_noalloc), so the call allocates nothing when `out` is given.
+    Calls that overlap on one device share that scratch and must be ordered by the caller."""
+    B, H, N, d = _need_qkv(q, k, v)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype or q.dtype, device=q.device)
+    _need(out, "out", (B, H, N, d), _FLOATS, q.device)
+    _need_bias(bias, bias_kind, grid, H, N, q.device)
+    bdt, ld, gh, gw = F16, 0, 0, 0
+    if bias is not None:
+        bdt = _dt(bias)
+        if bias_kind == BIAS_DENSE:
+            ld = bias.shape[-1]
+        elif bias_kind == BIAS_RELPOS:
+            gh, gw = grid
+    rc = _lib.binattn_attention_noalloc(_p(q), _p(k), _p(v), _dt(q), bias_kind, bdt, _p(bias), ld, gh, gw, B, H, N, d,
+                                        _p(out), _dt(out), _stream())
+    _check("binattn_attention_noalloc", rc)
+    return out

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "binattn.h"
 #include "internal.h"
 
@@ -93,6 +95,74 @@ WorkspaceLayout workspace_layout(int B, int H, int N, int d) {
     l.vamax = l.vq + up((int64_t)B * H * d * ldv);
     l.total = l.vamax + up((int64_t)B * H * d * 4);
     return l;
+}
+
+// The whole forward into caller memory: one kernel from fp16 Q, K, V where the shape allows it,
+// else the preparation launch into the workspace `ws` (laid out by workspace_layout(B,H,N,d))
+// followed by the forward from the packed inputs.  Arguments are already validated.
+int run_attention(const void* q, const void* k, const void* v, int dtype, int bias_kind, int bias_dtype,
+                  const void* bias, int64_t bias_ld, int grid_h, int grid_w, int B, int H, int N, int d, void* out,
+                  int out_dtype, char* ws, hipStream_t stream) {
+    if (dtype == BINATTN_F16) {  // short rows: one kernel straight from Q, K, V
+        FwdArgs f = forward_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, bias_dtype, bias, bias_ld,
+                                 grid_h, grid_w, B, H, N, d, out, out_dtype);
+        f.q_raw = static_cast<const _Float16*>(q);
+        f.k_raw = static_cast<const _Float16*>(k);
+        f.v_raw = static_cast<const _Float16*>(v);
+        const hipError_t e = launch_attention_fused(f, bias_kind, stream);
+        if (e != hipErrorNotSupported) return launched(e);
+    }
+    const WorkspaceLayout l = workspace_layout(B, H, N, d);
+    uint32_t* qb = reinterpret_cast<uint32_t*>(ws + l.qbits);
+    uint32_t* kb = reinterpret_cast<uint32_t*>(ws + l.kbits);
+    float* qm = reinterpret_cast<float*>(ws + l.qmu);
+    float* km = reinterpret_cast<float*>(ws + l.kmu);
+    int8_t* vq = reinterpret_cast<int8_t*>(ws + l.vq);
+    float* va = reinterpret_cast<float*>(ws + l.vamax);
+    hipError_t e = launch_prepare(q, k, v, dtype == BINATTN_F32, B * H, N, d, binattn_vq_ld(N), qb, qm, kb, km, vq,
+                                  va, stream);
+    if (e != hipSuccess) return BINATTN_ELAUNCH;
+    const FwdArgs a = forward_args(qb, qm, kb, km, vq, va, bias_dtype, bias, bias_ld, grid_h, grid_w, B, H, N, d,
+                                   out, out_dtype);
+    return launched(launch_forward(a, bias_kind, stream));
+}
+
+// ---- Scratch of the no-allocation entry point (binattn_attention_noalloc).  Each device the
+// library runs on holds its own copy of this array from the code object's load until the process
+// ends.  `scratch` names a host-side stand-in in host code: its device address on the current
+// device comes from hipGetSymbolAddress (scratch_on_current_device), and only that address is
+// handed to kernels.
+constexpr int64_t kScratchBytes = BINATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept; nullptr when the lookup fails.
+char* scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = static_cast<char*>(p);
+    }
+    return g_scratch_ptr[dev];
+}
+
+// Batch items whose packed inputs fit the scratch together (0: not even one).
+int noalloc_chunk(int B, int H, int N, int d) {
+    if (workspace_layout(1, H, N, d).total > kScratchBytes) return 0;
+    int lo = 1, hi = B;  // the workspace grows with the batch: largest nb that fits
+    while (lo < hi) {
+        const int mid = lo + (hi - lo + 1) / 2;
+        if (workspace_layout(mid, H, N, d).total <= kScratchBytes) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
 }
 
 }  // namespace
@@ -238,35 +308,46 @@ int binattn_attention(const void* q, const void* k, const void* v, int dtype, in
     int rc = check_dims(B, H, N, d);
     if (rc) return rc;
     if (!dtype_ok(dtype) || !dtype_ok(out_dtype)) return BINATTN_EUNSUPPORTED;
-    const WorkspaceLayout l = workspace_layout(B, H, N, d);
-    if (workspace_bytes < l.total) return BINATTN_EINVAL;
+    if (workspace_bytes < workspace_layout(B, H, N, d).total) return BINATTN_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return BINATTN_EALIGN;
     if ((rc = check_bias(bias_kind, bias_dtype, bias, bias_ld, grid_h, grid_w, N))) return rc;
     if ((rc = device_ready())) return rc;
-    if (dtype == BINATTN_F16) {  // short rows: one kernel straight from Q, K, V
-        FwdArgs f = forward_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, bias_dtype, bias, bias_ld,
-                                 grid_h, grid_w, B, H, N, d, out, out_dtype);
-        f.q_raw = static_cast<const _Float16*>(q);
-        f.k_raw = static_cast<const _Float16*>(k);
-        f.v_raw = static_cast<const _Float16*>(v);
-        const hipError_t e = launch_attention_fused(f, bias_kind, (hipStream_t)stream);
-        if (e != hipErrorNotSupported) return launched(e);
+    return run_attention(q, k, v, dtype, bias_kind, bias_dtype, bias, bias_ld, grid_h, grid_w, B, H, N, d, out,
+                         out_dtype, static_cast<char*>(workspace), (hipStream_t)stream);
+}
+
+int binattn_attention_noalloc(const void* q, const void* k, const void* v, int dtype, int bias_kind, int bias_dtype,
+                              const void* bias, int64_t bias_ld, int grid_h, int grid_w, int B, int H, int N, int d,
+                              void* out, int out_dtype, void* stream) {
+    if (!q || !k || !v || !out) return BINATTN_EINVAL;
+    int rc = check_dims(B, H, N, d);
+    if (rc) return rc;
+    if (!dtype_ok(dtype) || !dtype_ok(out_dtype)) return BINATTN_EUNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return BINATTN_EALIGN;
+    if ((rc = check_bias(bias_kind, bias_dtype, bias, bias_ld, grid_h, grid_w, N))) return rc;
+    const int one = binattn_attention_one_kernel(dtype, bias_kind, bias_dtype, grid_h, grid_w, B, H, N, d);
+    if (one < 0) return one;
+    const int nb = one ? B : noalloc_chunk(B, H, N, d);  // the one-kernel path uses no scratch
+    if (nb == 0) return BINATTN_EUNSUPPORTED;            // one batch item's packed inputs exceed the scratch
+    if ((rc = device_ready())) return rc;
+    char* ws = one ? nullptr : scratch_on_current_device();
+    if (!one && !ws) return BINATTN_ELAUNCH;
+    // Batch items are independent (the bias is shared over the batch), so the batch runs in
+    // chunks of nb items through the same scratch, in stream order.
+    const int64_t in_item = (int64_t)H * N * d * (dtype == BINATTN_F32 ? 4 : 2);
+    const int64_t out_item = (int64_t)H * N * d * (out_dtype == BINATTN_F32 ? 4 : 2);
+    for (int b0 = 0; b0 < B; b0 += nb) {
+        const int n = B - b0 < nb ? B - b0 : nb;
+        const int64_t io = b0 * in_item;
+        rc = run_attention(static_cast<const char*>(q) + io, static_cast<const char*>(k) + io,
+                           static_cast<const char*>(v) + io, dtype, bias_kind, bias_dtype, bias, bias_ld, grid_h,
+                           grid_w, n, H, N, d, static_cast<char*>(out) + b0 * out_item, out_dtype, ws,
+                           (hipStream_t)stream);
+        if (rc) return rc;
     }
-    char* ws = static_cast<char*>(workspace);
-    uint32_t* qb = reinterpret_cast<uint32_t*>(ws + l.qbits);
-    uint32_t* kb = reinterpret_cast<uint32_t*>(ws + l.kbits);
-    float* qm = reinterpret_cast<float*>(ws + l.qmu);
-    float* km = reinterpret_cast<float*>(ws + l.kmu);
-    int8_t* vq = reinterpret_cast<int8_t*>(ws + l.vq);
-    float* va = reinterpret_cast<float*>(ws + l.vamax);
-    hipError_t e = launch_prepare(q, k, v, dtype == BINATTN_F32, B * H, N, d, binattn_vq_ld(N), qb, qm, kb, km, vq,
-                                  va, (hipStream_t)stream);
-    if (e != hipSuccess) return BINATTN_ELAUNCH;
-    const FwdArgs a = forward_args(qb, qm, kb, km, vq, va, bias_dtype, bias, bias_ld, grid_h, grid_w, B, H, N, d,
-                                   out, out_dtype);
-    return launched(launch_forward(a, bias_kind, (hipStream_t)stream));
+    return BINATTN_OK;
 }
 
 }  // extern "C"

@@ -208,6 +208,26 @@ int binattn_attention(const void* q, const void* k, const void* v, int dtype, in
                       void* out, int out_dtype, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * binattn_attention_noalloc -- binattn_attention for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments without the workspace, the same results bit for bit, and no allocation of any
+ * kind.  The packed intermediates go to a scratch array of BINATTN_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every device it runs on (allocated when its code object loads, kept until
+ * the process ends).  The batch runs in chunks of as many batch items as fit the scratch
+ * (binattn_attention_workspace(chunk, H, N, d) bytes), in stream order; a shape that runs as
+ * one kernel (binattn_attention_one_kernel) uses no scratch.
+ *   q, k, v, bias..., out, stream   as binattn_attention
+ * Errors as binattn_attention; BINATTN_EUNSUPPORTED (before any launch) when the packed inputs
+ * of a single batch item exceed the scratch.  Every call on one device shares that device's
+ * scratch: calls that overlap on one device (other streams, other threads) race and must be
+ * ordered by the caller.  The scratch needs no clearing: every byte a call reads it wrote first.
+ */
+#define BINATTN_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+int binattn_attention_noalloc(const void* q, const void* k, const void* v, int dtype, int bias_kind, int bias_dtype,
+                              const void* bias, int64_t bias_ld, int grid_h, int grid_w, int B, int H, int N, int d,
+                              void* out, int out_dtype, void* stream);
+
+/*
  * binattn_keep_plan -- inspection export (host only, no device call): how the head-resident
  * forward splits the query blocks of every (b, h) over workgroups.  nheads = B*H heads of
  * nqb = ceil(N / 64) query blocks (1 <= nqb <= 10, the rows that kernel takes), `slots` resident

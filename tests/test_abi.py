@@ -147,6 +147,33 @@ def test_attention_one_kernel_query(lib):
     assert q(7, NONE, F16, 0, 0, 2, 2, 100, 64) == -2
 
 
+def _noalloc(lib, **kw):
+    args = dict(q=_a(256), k=_a(512), v=_a(768), dt=1, kind=0, bdt=1, bias=None, ld=0, gh=0, gw=0, B=2, H=3, N=1000,
+                d=64, out=_a(1024), odt=1, stream=None)
+    args.update(kw)
+    return lib.binattn_attention_noalloc(*args.values())
+
+
+def test_noalloc_validation(lib):
+    """binattn_attention_noalloc checks its arguments as binattn_attention does, and refuses a
+    batch item whose packed inputs exceed the scratch, all before touching a device."""
+    import ctypes as C
+    lib.binattn_attention_noalloc.argtypes = [C.c_void_p] * 3 + [C.c_int] * 3 + [C.c_void_p, C.c_int64] + \
+        [C.c_int] * 6 + [C.c_void_p, C.c_int, C.c_void_p]
+    lib.binattn_attention_workspace.restype = C.c_int64
+    assert _noalloc(lib, q=None) == -1
+    assert _noalloc(lib, out=None) == -1
+    assert _noalloc(lib, B=0) == -1
+    assert _noalloc(lib, dt=3) == -2
+    assert _noalloc(lib, d=60) == -2
+    assert _noalloc(lib, v=_a(770)) == -3
+    assert _noalloc(lib, kind=1, bias=None, ld=1000) == -1
+    # one batch item of 64 heads x 8192 tokens x 128 channels: V^ alone fills the 64 MiB scratch
+    assert lib.binattn_attention_workspace(1, 64, 8192, 128) > 64 << 20
+    assert _noalloc(lib, B=1, H=64, N=8192, d=128) == -2
+    assert _noalloc(lib, B=4, H=64, N=8192, d=128) == -2
+
+
 def test_valid_arguments_without_a_device_report_enodevice(lib):
     import torch
     if torch.cuda.is_available():
@@ -155,6 +182,9 @@ def test_valid_arguments_without_a_device_report_enodevice(lib):
     assert _fwd(lib) == -4
     assert _fwd(lib, kind=2, bias=_a(4096), gh=16, gw=16) == -4
     assert _fwd(lib, kind=1, bias=_a(4096), ld=(1 << 26) - 8) == -4  # the largest fp16 dense-bias stride accepted
+    assert _noalloc(lib) == -4                    # two-launch shape, batch items fit the scratch
+    assert _noalloc(lib, B=64, H=16, N=4096) == -4  # several chunks of batch items
+    assert _noalloc(lib, N=197) == -4             # one kernel, no scratch
     assert lib.binattn_prepare(_a(256), _a(512), _a(768), 1, 2, 3, 197, 64, _a(1024), _a(1280), _a(1536),
                                _a(1792), _a(2048), _a(2304), None) == -4
 
