@@ -57,7 +57,7 @@ struct TileRegs {
     uint32_t kw[KT];
     uint4 v[VCH];
     float mu;
-    float tw[TW / 256 > 0 ? TW / 256 : 1];
+    uint32_t tw[TW / 256 > 0 ? TW / 256 : 1];  // raw table bits (fp16 or fp32), converted when stored
 };
 
 // LDS of one tile (a multiple of 16 bytes, so consecutive tiles keep 16-byte alignment).
@@ -115,19 +115,33 @@ __device__ __forceinline__ void load_window_at(float (&dst)[PER], const FwdArgs&
     }
 }
 
-// Loads PER window entries per thread (entry tid + 256 i) of a head's relative-position table,
-// starting at element off, as fp32.  Entries past the table read as 0.
+// Raw bits of PER window entries per thread (entry tid + 256 i) of a head's relative-position
+// table from element off; entries past the table read as 0.  Left unconverted so that no wait
+// for these loads sits where they are issued.
 template <int PER>
-__device__ __forceinline__ void load_window(float (&dst)[PER], const FwdArgs& a, const void* table, int off) {
-    int eo[PER];
+__device__ __forceinline__ void load_window_raw(uint32_t (&dst)[PER], const FwdArgs& a, const void* table, int off) {
+    const int tsz = (2 * a.gh - 1) * (2 * a.gw - 1);
+    if (a.bias_f32) {
+        const __amdgpu_buffer_rsrc_t tr = buffer_rsrc((const float*)table + off, (tsz - off) * 4);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) eo[i] = threadIdx.x + 256 * i;
-    load_window_at<PER>(dst, a, table, off, eo);
+        for (int i = 0; i < PER; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b32(tr, (threadIdx.x + 256 * i) * 4, 0, 0);
+    } else {
+        const __amdgpu_buffer_rsrc_t tr = buffer_rsrc((const _Float16*)table + off, (tsz - off) * 2);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b16(tr, (threadIdx.x + 256 * i) * 2, 0, 0);
+    }
 }
 
+template <bool F32>
+__device__ __forceinline__ float table_value(uint32_t raw) {
+    return F32 ? __uint_as_float(raw) : (float)__builtin_bit_cast(_Float16, (uint16_t)raw);
+}
+
+// Loads of key tile j0 into registers: sign words, V^ chunks, mu_k and (TW >= 256) the
+// relative-position window starting at table element woff.
 template <int NT, int TW>
-__device__ __forceinline__ void load_tile(TileRegs<NT, TW>& r, const FwdArgs& a, const HeadPtrs& hp, int q0,
-                                          int j0) {
+__device__ __forceinline__ void load_tile(TileRegs<NT, TW>& r, const FwdArgs& a, const HeadPtrs& hp, int j0,
+                                          int woff) {
     typedef TileRegs<NT, TW> R;
     const int tid = threadIdx.x, N = a.N, d = a.d;
     // sign words of keys j0.. (keys >= N read as 0)
@@ -146,16 +160,14 @@ __device__ __forceinline__ void load_tile(TileRegs<NT, TW>& r, const FwdArgs& a,
     }
     const __amdgpu_buffer_rsrc_t mr = buffer_rsrc(hp.kmu + j0, (N - j0) * 4);
     r.mu = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mr, (tid & 63) * 4, 0, 0));
-    if constexpr (TW >= 256) {
-        const RelposWin w = relpos_window(q0, j0, j0 + kBC, N, a.gh, a.gw);
-        load_window<TW / 256>(r.tw, a, hp.table, w.dr_lo * w.row_len);
-    }
+    if constexpr (TW >= 256) load_window_raw<TW / 256>(r.tw, a, hp.table, woff);
 }
 
 // NARROW: the tile holds at most 16 valid keys (the last tile of a row) and is staged for the
 // narrow score tile: key j is K operand row j of MFMA 0, and the V^ dword of keys 4q..4q+3 is the
 // first dword of operand lane (slot, q) -- those lanes' other bytes meet zero P^ bytes.
-template <int NT, int TW, bool NARROW = false>
+// TF32: the relative-position table (TW >= 256) is fp32, else fp16.
+template <int NT, int TW, bool NARROW = false, bool TF32 = false>
 __device__ __forceinline__ void store_tile(const TileRegs<NT, TW>& r, TileLds<NT, TW>& s, int d) {
     typedef TileRegs<NT, TW> R;
     const int tid = threadIdx.x;
@@ -195,7 +207,7 @@ __device__ __forceinline__ void store_tile(const TileRegs<NT, TW>& r, TileLds<NT
     if (tid < kBC) s.mu[tid] = r.mu;
     if constexpr (TW >= 256) {
 #pragma unroll
-        for (int i = 0; i < TW / 256; ++i) s.tw[tid + 256 * i] = r.tw[i];
+        for (int i = 0; i < TW / 256; ++i) s.tw[tid + 256 * i] = table_value<TF32>(r.tw[i]);
     }
 }
 
@@ -825,7 +837,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
         Regs regs[NTL];
 #pragma unroll
         for (int t = 0; t < NTL; ++t)
-            if (!LONG || t < nt) load_tile<NT, 4>(regs[t], a, hp, 0, t * kBC);
+            if (!LONG || t < nt) load_tile<NT, 4>(regs[t], a, hp, t * kBC, 0);
         stage_common(a, bh, sScale);
         int cs[Regs::VCH];
 #pragma unroll
