@@ -55,7 +55,7 @@ int check_bias(int bias_kind, int bias_dtype, const void* bias, int64_t bias_ld,
             if (!bias) return BINATTN_EINVAL;
             if (!dtype_ok(bias_dtype)) return BINATTN_EUNSUPPORTED;
             if (grid_h <= 0 || grid_w <= 0 || (int64_t)grid_h * grid_w != N) return BINATTN_EINVAL;
-            if (grid_w % 16 != 0 || !relpos_window_fits(grid_w)) return BINATTN_EUNSUPPORTED;
+            if (!relpos_window_fits(grid_w)) return BINATTN_EUNSUPPORTED;
             if (!aligned16(bias)) return BINATTN_EALIGN;
             break;
         default:
@@ -285,7 +285,7 @@ int binattn_attention_one_kernel(int dtype, int bias_kind, int bias_dtype, int g
     if (bias_kind != BINATTN_BIAS_NONE && !dtype_ok(bias_dtype)) return BINATTN_EUNSUPPORTED;
     if (bias_kind == BINATTN_BIAS_RELPOS) {  // as check_bias
         if (grid_h <= 0 || grid_w <= 0 || (int64_t)grid_h * grid_w != N) return BINATTN_EINVAL;
-        if (grid_w % 16 != 0 || !relpos_window_fits(grid_w)) return BINATTN_EUNSUPPORTED;
+        if (!relpos_window_fits(grid_w)) return BINATTN_EUNSUPPORTED;
     }
     if (dtype != BINATTN_F16) return 0;
     FwdArgs f = {};

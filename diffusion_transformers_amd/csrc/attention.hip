@@ -26,6 +26,7 @@ static hipError_t launch_fused_nt(const FwdArgs& a, int bk, hipStream_t s) {
 bool attention_fused_applies(const FwdArgs& a, int bias_kind) {
     const int ntiles = (a.N + kBC - 1) / kBC;
     if (ntiles > kKeepTiles || (bias_kind == 2 && !keep_window_fits(a))) return false;
+    if (bias_kind == 2 && relpos_kind(a.gw) == BK_RELPOS_G) return false;  // gathered grids: two launches
     const int nt = (a.d + 15) / 16;
     return nt == 4 || nt == 5 || nt == 8;
 }

@@ -37,6 +37,8 @@ hipError_t launch_prepare(const void* q, const void* k, const void* v, int f32, 
                           uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu, int8_t* vq, float* vamax,
                           hipStream_t s);
 hipError_t launch_forward(const FwdArgs& a, int bias_kind, hipStream_t s);
+// The forward with the relative-position bias on a grid whose width is not a multiple of 16.
+hipError_t launch_forward_gather(const FwdArgs& a, hipStream_t s);
 // Whole attention from fp16 Q, K, V in one kernel where the shape allows it (short rows);
 // returns hipErrorNotSupported, launching nothing, where it does not.
 hipError_t launch_attention_fused(const FwdArgs& a, int bias_kind, hipStream_t s);

@@ -24,7 +24,13 @@ constexpr int kDeferTiles = 16;             // streamed rows of at least this ma
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2_255 = 7.99435343685886f;
 
-enum { BK_NONE = 0, BK_DENSE_F16 = 1, BK_DENSE_F32 = 2, BK_RELPOS = 3 };
+// Bias kinds of the kernels: none, dense fp16 / fp32, relative position on grids whose width
+// is a multiple of 16 (a lane's 16-key run lies in one grid row, so its table entries are
+// consecutive), and relative position on any other grid (RELPOS_G: each key's table offset is
+// staged in LDS and gathered per element).
+enum { BK_NONE = 0, BK_DENSE_F16 = 1, BK_DENSE_F32 = 2, BK_RELPOS = 3, BK_RELPOS_G = 4 };
+constexpr bool is_relpos(int bk) { return bk == BK_RELPOS || bk == BK_RELPOS_G; }
+inline int relpos_kind(int gw) { return gw % 16 == 0 ? BK_RELPOS : BK_RELPOS_G; }
 
 // How the short-row kernel splits the query blocks of a head over workgroups: `a` segments of f
 // blocks, then `b` segments of r blocks (the last segment of each kind clipped to the row).
@@ -69,6 +75,7 @@ struct alignas(16) TileLds {
     uint32_t v[NT * kWave * 4];            // [ct][lane] x 16 B: A operand of PV MFMA ct
     float mu[kBC];
     float tw[TW];
+    int kk[TW >= 256 ? kBC : 4];           // streamed relative position, any grid: per key, its window byte offset
 };
 
 struct RelposWin {
@@ -346,10 +353,13 @@ __device__ __forceinline__ LaneQ lane_query(const FwdArgs& a, int bh, int qw0, i
 // 0: their Q operand is zero, so those products vanish whatever the K codes are (every fp4 code
 // is finite).  wrun: relative-position window entry of key jg + 15 (the run's bias for key jg + k
 // is wrun[15 - k]: a grid row holds whole runs, and the column offset falls as the key rises).
+// RELPOS_G: wrun is the window entry of the lane's query part, and kk (LDS) holds the byte
+// offsets from it of the entries of keys jg .. jg + 15 (any grid width).
 template <int NT, int BIAS>
 __device__ __forceinline__ void tile_scores(const uint32_t* __restrict__ sk, const float* __restrict__ smu,
                                             const LaneQ& lq, const BiasRegs<BIAS>& bias, const float* wrun,
-                                            bool tail, int nvalid, float (&S)[16], float& mloc) {
+                                            bool tail, int nvalid, float (&S)[16], float& mloc,
+                                            const int* kk = nullptr) {
     constexpr int W = (NT + 1) / 2;
     const int lane = threadIdx.x & 63, g = lane >> 4, m16 = lane & 15;
     const int koff = ((g < W ? g : 0) * 16 + m16) * 4;  // lane-constant
@@ -368,11 +378,21 @@ __device__ __forceinline__ void tile_scores(const uint32_t* __restrict__ sk, con
         const float4 m4 = *reinterpret_cast<const float4*>(&smu[16 * g + k]);
         muk[k] = m4.x; muk[k + 1] = m4.y; muk[k + 2] = m4.z; muk[k + 3] = m4.w;
     }
+    int koffs[BIAS == BK_RELPOS_G ? 16 : 1];
+    if constexpr (BIAS == BK_RELPOS_G) {
+#pragma unroll
+        for (int k = 0; k < 16; k += 4) {
+            const int4 o4 = *reinterpret_cast<const int4*>(&kk[k]);
+            koffs[k] = o4.x; koffs[k + 1] = o4.y; koffs[k + 2] = o4.z; koffs[k + 3] = o4.w;
+        }
+    }
+    typedef const char __attribute__((address_space(3)))* lds_ccptr;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         float b = 0.0f;
         if (BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32) b = bias_at<BIAS>(bias, k);
         if (BIAS == BK_RELPOS) b = wl[15 - k];
+        if constexpr (BIAS == BK_RELPOS_G) b = *(lds_cfptr)((lds_ccptr)wrun + koffs[k]);
         S[k] = __builtin_fmaf(D[k >> 2][k & 3] * muk[k], lq.cq, b);
     }
     // The max is taken separately on the two paths: on the common one every S is an fma
@@ -749,7 +769,9 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
     typedef TileRegs<NT, 4> Regs;
     typedef TileLds<NT, 4> Lds;
     __shared__ Lds lds[NTL];
-    __shared__ __attribute__((aligned(16))) float sWin[BIAS == BK_RELPOS ? kRelposWin : 4];
+    __shared__ __attribute__((aligned(16))) float sWin[is_relpos(BIAS) ? kRelposWin : 4];
+    // RELPOS_G: per key of the head, the byte offset of its part of the window index
+    __shared__ __attribute__((aligned(16))) int sKk[BIAS == BK_RELPOS_G ? NTL * kBC : 4];
     __shared__ __attribute__((aligned(16))) float sScale[128];
     __shared__ __attribute__((aligned(16))) int sCol[128];  // 128 * sum_j V^_jc per channel slot
     // whole-attention path only: the prepared Q of every query block, and staging scratch
@@ -795,7 +817,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
     hp.kmu = a.kmu + (int64_t)bh * N;
     hp.vq = a.vq + (int64_t)bh * d * a.ldv;
     hp.table = nullptr;
-    if (BIAS == BK_RELPOS) {
+    if (is_relpos(BIAS)) {
         const int64_t tsz = (int64_t)(2 * a.gh - 1) * (2 * a.gw - 1);
         hp.table = a.bias_f32 ? (const void*)((const float*)a.bias + h * tsz)
                               : (const void*)((const _Float16*)a.bias + h * tsz);
@@ -858,7 +880,14 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
     // slots past a row's 2 gw - 1 entries are padding, loaded but never read)
     float wv[kRelposWin / 256];
     int weo[kRelposWin / 256];
-    if (BIAS == BK_RELPOS) {
+    if (BIAS == BK_RELPOS_G) {  // key j at grid (rj, cj): (gh - 1 - rj) row stride + gw - 1 - cj, in bytes
+        for (int j = tid; j < NTL * kBC; j += 256) {
+            const int jj = min(j, N - 1);  // keys past N are masked: any in-window offset will do
+            const int rj = jj / a.gw, cj = jj - rj * a.gw;
+            sKk[j] = 4 * ((a.gh - 1 - rj) * a.wrs + a.gw - 1 - cj);
+        }
+    }
+    if (is_relpos(BIAS)) {
 #pragma unroll
         for (int i = 0; i < kRelposWin / 256; ++i) {
             const int slot = tid + 256 * i, r = slot / a.wrs;
@@ -899,7 +928,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
         const int q0 = qb * kBR, qw0 = q0 + wave * 16;
         const bool live = qw0 < N;  // some query of this wave is < N (wave-uniform)
         const bool more = qb + 1 < qb_hi;
-        if (BIAS == BK_RELPOS && more)
+        if (is_relpos(BIAS) && more)
             load_window_at<kRelposWin / 256>(wv, a, hp.table, window_lo(qb + 1) * (2 * a.gw - 1), weo);
 
         // the lane's query: Q operand (fp4 2*sign of channels 32g..32g+31, 0 past d) and seed
@@ -915,7 +944,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
             lq.cq = qmu * a.qk_scale;
         }
         int qrel = 0;  // relative position: the query's part of the window offsets
-        if (BIAS == BK_RELPOS) {
+        if (is_relpos(BIAS)) {
             const int ri = lq.qi / a.gw, ci = lq.qi % a.gw;
             qrel = (ri - window_lo(qb)) * a.wrs + ci;
         }
@@ -935,12 +964,13 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
                     int idx0 = run - 1;
                     if (BIAS == BK_RELPOS)  // (a run wholly past N is masked; its reads stay in the window)
                         idx0 = jg >= N ? run - 1 : qrel + krel[t];
+                    if (BIAS == BK_RELPOS_G) idx0 = qrel + 15;  // window base of the query; keys via sKk
                     if (nar)
                         tile_scores4<NT, BIAS>(L[t].k, L[t].mu, lq, bias[LONG ? (t & 1) : t], sWin + idx0 - 3, N - jg,
                                                S4, mloc);
                     else
                         tile_scores<NT, BIAS>(L[t].k, L[t].mu, lq, bias[LONG ? (t & 1) : t], sWin + idx0 - 15,
-                                              TAIL == 1 && t == nt - 1, N - jg, S[t], mloc);
+                                              TAIL == 1 && t == nt - 1, N - jg, S[t], mloc, sKk + jg);
                 }
                 __builtin_amdgcn_sched_barrier(0);  // one tile's operands live at a time
             }
@@ -953,7 +983,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
                 for (int t = 0; t < (LONG ? 1 : NTL); ++t) load_bias_tile(qb + 1, t, bias[t]);
             }
         }
-        if (BIAS == BK_RELPOS) {
+        if (is_relpos(BIAS)) {
             __syncthreads();  // every wave is done with this block's window
             if (more) {
 #pragma unroll
@@ -988,7 +1018,7 @@ __global__ __launch_bounds__(256) void binattn_fwd_keep_kernel(FwdArgs a, KeepPl
                 for (int r = 0; r < 4; ++r) accf[ct][r] = (float)acc[ct][r];
             store_out<NT>(a, bh, lq, sScale, accf, rows4_sum(lsum));
         }
-        if (BIAS == BK_RELPOS) __syncthreads();  // the next block's window is in place
+        if (is_relpos(BIAS)) __syncthreads();  // the next block's window is in place
     }
 }
 
@@ -1007,6 +1037,7 @@ inline int keep_window_stride(const FwdArgs& a) {
         const int ri_min = q0 / gw, ri_max = (min(q0 + kBR, N) - 1) / gw;
         rows = max(rows, ri_max - ri_min + gh);
     }
+    if (gw % 16 != 0) return rows * row <= kRelposWin ? row : 0;  // gathered per key: no run layout to place
     auto conflict_free = [&](int rs) {
         for (int j0 = 0; j0 < N; j0 += kBC) {
             int st[4];
@@ -1117,7 +1148,7 @@ inline void launch_keep_inst(const FwdArgs& a, hipStream_t s) {
     const KeepPlan p = keep_plan(nheads, nqb, per_cu * device_cus(), FUSED ? 3.0 : 0.5);
     const int64_t grid = 8 * ((nheads + 7) / 8) * (p.a + p.b);
     FwdArgs ka = a;
-    if (BK == BK_RELPOS) ka.wrs = keep_window_stride(a);
+    if (is_relpos(BK)) ka.wrs = keep_window_stride(a);
     hipLaunchKernelGGL((binattn_fwd_keep_kernel<NT, BK, NTL, FUSED, TAIL>), dim3((unsigned)grid), dim3(256), 0, s,
                        ka, p);
 }
@@ -1161,7 +1192,7 @@ inline void launch_keep(const FwdArgs& a, hipStream_t s) {
         launch_keep_tail<NT, BK, FUSED, 0>(a, ntiles, s);
         return;
     }
-    if constexpr (BK != BK_RELPOS) {  // relative-position grids give a narrow tail only for N = 64k + 16
+    if constexpr (!is_relpos(BK)) {  // relative position: the last tile is masked, never narrow
         if (tail == 2) {
             launch_keep_tail<NT, BK, FUSED, 2>(a, ntiles, s);
             return;

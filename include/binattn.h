@@ -120,8 +120,9 @@ int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t
  *                       bias_dtype; token n sits at (n / gw, n % gw) on a
  *                       gh x gw grid (gh*gw == N) and
  *                       b_ij = T[h, (r_i-r_j+gh-1)*(2gw-1) + (c_i-c_j+gw-1)].
- *                       Requires gw % 16 == 0 and gw <= 160 (the rows of T one
- *                       key tile touches are staged on chip).  bias_ld ignored.
+ *                       Requires gw <= 171 (the rows of T that 64 queries and
+ *                       64 keys touch are staged on chip; any gh).  bias_ld
+ *                       ignored.
  *   out             [B,H,N,d] of out_dtype
  *
  * Computes, per (b, h, query i):

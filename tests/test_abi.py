@@ -87,7 +87,7 @@ def test_forward_validation(lib):
     assert _fwd(lib, kind=1, bias=_a(4096), ld=1 << 25, bdt=0) == -2    # fp32: 16 * 2^27 bytes
     assert _fwd(lib, kind=1, bias=_a(4096), ld=(1 << 62)) == -2         # no 64-bit wrap in the check
     assert _fwd(lib, kind=2, bias=_a(4096), gh=16, gw=15) == -1   # grid does not cover N
-    assert _fwd(lib, kind=2, bias=_a(4096), N=240, gh=16, gw=15) == -2  # gw % 16 != 0
+    assert _fwd(lib, kind=2, bias=_a(4096), N=344, gh=2, gw=172) == -2  # staged table rows of one tile too wide
     assert _fwd(lib, kind=2, bias=_a(4096), N=1024, gh=1, gw=1024) == -2  # window of one tile too wide
     assert _fwd(lib, kind=2, bias=_a(4096), N=1056, gh=6, gw=176) == -2
     assert _fwd(lib, kind=3, bias=_a(4096)) == -2
@@ -142,7 +142,9 @@ def test_attention_one_kernel_query(lib):
     assert q(F16, NONE, F16, 0, 0, 2, 2, 100, 32) == 0        # d = 32
     assert q(F16, NONE, F16, 0, 0, 2, 2, 257, 64) == 0
     assert q(F16, NONE, F16, 0, 0, 2, 2, 100, 60) == -2       # d not a multiple of 8
-    assert q(F16, REL, F16, 32, 8, 2, 2, 256, 64) == -2       # grid width not a multiple of 16
+    assert q(F16, REL, F16, 32, 8, 2, 2, 256, 64) == 0        # grid width not a multiple of 16: two launches
+    assert q(F16, REL, F16, 14, 14, 2, 2, 196, 64) == 0       # the 14 x 14 grid of a 224^2 image, 16-pixel patches
+    assert q(F16, REL, F16, 2, 172, 2, 2, 344, 64) == -2      # staged table rows of one tile too wide
     assert q(F16, REL, F16, 16, 16, 2, 2, 255, 64) == -1      # grid does not cover N
     assert q(7, NONE, F16, 0, 0, 2, 2, 100, 64) == -2
 

@@ -290,6 +290,18 @@ SMALL = [
     (1, 2, 1024, 96, "f32", "relpos", (8, 128)),
     (1, 1, 2400, 64, "f16", "relpos", (15, 160)),
     (1, 1, 2048, 64, "f16", "relpos", (16, 128)),
+    # relative-position grids whose width is not a multiple of 16 (each key's table offset gathered):
+    # the 14 x 14 grid of a 224^2 image with 16-pixel patches, the 24 x 24 grid at 384^2, odd and
+    # one-wide grids, head-resident (<= 4 tiles), streamed and int32-deferred (>= 16 tiles) rows
+    (2, 3, 196, 64, "f16", "relpos", (14, 14)),
+    (1, 2, 196, 72, "f32", "relpos", (14, 14)),
+    (1, 2, 100, 128, "f16", "relpos", (10, 10)),
+    (2, 1, 63, 8, "f16", "relpos", (7, 9)),
+    (1, 2, 576, 64, "f16", "relpos", (24, 24)),
+    (1, 1, 300, 40, "f32", "relpos", (300, 1)),
+    (1, 1, 1225, 64, "f16", "relpos", (35, 35)),
+    (1, 1, 2000, 32, "f16", "relpos", (40, 50)),
+    (1, 1, 1700, 64, "f32", "relpos", (10, 170)),
 ]
 
 
@@ -421,7 +433,7 @@ def _random_cases(n, seed):
         dt = "f16" if rng.random() < 0.75 else "f32"
         bias = str(rng.choice(["none", "dense", "relpos"]))
         if bias == "relpos":
-            gw = int(rng.choice([16, 32, 48]))
+            gw = int(rng.choice([16, 32, 48, 14, 7, 24, 50, 1]))
             gh = int(rng.integers(1, max(2, 1200 // gw)))
             N, grid = gh * gw, (gh, gw)
         else:
@@ -509,3 +521,20 @@ def test_binding_refuses_strided_and_mismatched_inputs():
     o = b.forward(qb, qm, qb, qm, vq, va, 64)  # the same tensors, well formed, still run
     torch.cuda.synchronize()
     assert torch.isfinite(o).all()
+
+
+def test_attention_deit_224_relative_position_grid():
+    """A DeiT-S-shaped batch (B=16, H=6, d=64) on the 14 x 14 token grid of a 224^2 image with
+    16-pixel patches and a relative-position table bias: binattn_attention against the oracle on
+    every row, equal bit for bit to the four separate calls."""
+    _say("attention deit 224 relpos 14x14")
+    inp = W.custom(16, 6, 196, 64, "f16", "relpos", (14, 14), seed=224)
+    b = _b()
+    g = gpu_pipeline(inp)
+    o = nan_out(g["o"].shape, g["o"].dtype)
+    b.attention(_t(inp["q"]), _t(inp["k"]), _t(inp["v"]), _t(inp["bias"]), b.BIAS_RELPOS, (14, 14), out=o)
+    torch.cuda.synchronize()
+    assert_written(o)
+    assert torch.equal(o, g["o"])
+    ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["bias"], oracle.BIAS_RELPOS, grid=(14, 14))
+    assert_o(o.cpu().numpy(), ref, float(np.abs(inp["v"].astype(np.float64)).max()), "deit 224 relpos")
