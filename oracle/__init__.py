@@ -65,6 +65,9 @@ def _load():
     lib.oracle_forward.restype = i32
     lib.oracle_forward_rows.argtypes = [vp, vp, vp, i32, vp, i32, i32, i64, i64, i64, i32, i32, vp, i64, vp]
     lib.oracle_forward_rows.restype = i32
+    lib.oracle_backward.argtypes = [vp, vp, vp, i32, vp, i32, i32, i64, i64, i64, i32, vp, ctypes.c_double, vp, vp, vp,
+                                    vp]
+    lib.oracle_backward.restype = i32
     _lib = lib
     return lib
 
@@ -181,3 +184,24 @@ def forward_rows(q, k, v, rows, bias=None, bias_kind=BIAS_NONE, grid=None, flags
     if rc != 0:
         raise ValueError(f"oracle_forward_rows failed with code {rc}")
     return out
+
+
+def backward(q, k, v, dout, bias=None, bias_kind=BIAS_NONE, grid=None, ste_clip=0.0, with_bias_grad=True):
+    """Gradients of the quantisation-aware forward (straight-through sign; see binattn_oracle.c)
+    for an output gradient dout [B,H,N,d] -> (dq, dk, dv [B,H,N,d], db) in fp64, with db the
+    dense [H,N,N] or table [H,(2gh-1)(2gw-1)] bias gradient (None without a bias).
+    ste_clip > 0 passes the sign's gradient only where |x| <= ste_clip."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, d = q.shape
+    kind, b, gh, gw = _bias_args(bias, bias_kind, grid)
+    dq, dk, dv = (np.zeros((B, H, N, d), dtype=np.float64) for _ in range(3))
+    db = None
+    if kind == BIAS_DENSE and with_bias_grad:
+        db = np.zeros((H, N, N), dtype=np.float64)
+    elif kind == BIAS_RELPOS and with_bias_grad:
+        db = np.zeros((H, (2 * gh - 1) * (2 * gw - 1)), dtype=np.float64)
+    rc = _load().oracle_backward(_ptr(q), _ptr(k), _ptr(v), kind, _ptr(b), gh, gw, B, H, N, d, _ptr(dout),
+                                 float(ste_clip), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db))
+    if rc != 0:
+        raise ValueError(f"oracle_backward failed with code {rc}")
+    return dq, dk, dv, db

@@ -261,15 +261,17 @@ int oracle_forward(const double* q, const double* k, const double* v, int bias_k
     {
         double* S = (double*)malloc(sizeof(double) * N);
         double* ph = (double*)malloc(sizeof(double) * N);
-        if (!S || !ph) {
+        const int ok = S && ph;
+        if (!ok) {
 #pragma omp atomic write
             fail = 1;
-        } else {
+        }
+        /* every thread reaches the worksharing loop; one without its buffers only skips work */
 #pragma omp for schedule(static)
-            for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t r = 0; r < rows; ++r) {
+            if (ok)
                 forward_row(&c, r / N, r % N, S, ph, out + r * d, m_out ? m_out + r : NULL,
                             l_out ? l_out + r : NULL, phat_out ? phat_out + r * N : NULL);
-            }
         }
         free(S);
         free(ph);
@@ -291,19 +293,183 @@ int oracle_forward_rows(const double* q, const double* k, const double* v, int b
     {
         double* S = (double*)malloc(sizeof(double) * N);
         double* ph = (double*)malloc(sizeof(double) * N);
-        if (!S || !ph) {
+        const int ok = S && ph;
+        if (!ok) {
 #pragma omp atomic write
             fail = 1;
-        } else {
+        }
 #pragma omp for schedule(static)
-            for (int64_t t = 0; t < nrows; ++t) {
-                const int64_t r = rows[t];
-                if (r < 0 || r >= B * H * N) continue;
-                forward_row(&c, r / N, r % N, S, ph, out_rows + t * d, NULL, NULL, NULL);
-            }
+        for (int64_t t = 0; t < nrows; ++t) {
+            const int64_t r = rows[t];
+            if (!ok || r < 0 || r >= B * H * N) continue;
+            forward_row(&c, r / N, r % N, S, ph, out_rows + t * d, NULL, NULL, NULL);
         }
         free(S);
         free(ph);
+    }
+    ctx_free(&c);
+    return fail ? -2 : 0;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Backward of the quantisation-aware forward (key design 4: QAT with a straight-through
+ * estimator for sign).  The forward above is the model; its backward, given dO, is derived here
+ * step by step under these readings (the pages only say that the sign is passed straight
+ * through):
+ *   - sign: d sign(x)/dx := ste(x) = 1, or 1 when |x| <= clip and 0 otherwise (clip > 0);
+ *   - mu = mean|x| is differentiated exactly: d mu/dx_c = sgn(x_c)/d with sgn(0) = 0;
+ *   - the P and V quantisers are straight-through: P^/255 passes its gradient to P~ and
+ *     s_c V^ to v, while their forward values are the quantised ones;
+ *   - the row max m is a constant (it only shifts the exponent: FlashAttention-2's convention);
+ *   - the row sum l = sum P~ is differentiated.
+ * With A = P^/255, Vt = s V^ (dequantised), O = A Vt / l:
+ *   dVt_j = sum_i A_ij dO_i / l_i,   Delta_i = dO_i . O_i,   dP_ij = dO_i . Vt_j,
+ *   dS_ij = (P~_ij / l_i) (dP_ij - Delta_i),   db_ij = dS_ij (summed over the batch; the
+ *   relative-position table entry of (i, j) collects every dS_ij that indexes it),
+ *   with s_i = mu_q sign(q_i) and t_j = mu_k sign(k_j):
+ *   ds_i = sum_j dS_ij t_j / sqrt(d),   dt_j = sum_i dS_ij s_i / sqrt(d),
+ *   dq_ic = mu_q ds_ic ste(q_ic) + sgn(q_ic)/d sum_e ds_ie sign(q_ie)   (likewise dk), dv = dVt.
+ * Outputs: dq, dk, dv [B,H,N,d]; db dense [H,N,N] or table [H,(2gh-1)(2gw-1)] (NULL: skipped). */
+static int team_size(void) {
+#ifdef _OPENMP
+    return omp_get_num_threads();
+#else
+    return 1;
+#endif
+}
+
+static double ste_grad(double x, double clip) { return (clip > 0.0 && fabs(x) > clip) ? 0.0 : 1.0; }
+
+static double sgn0(double x) { return x > 0.0 ? 1.0 : (x < 0.0 ? -1.0 : 0.0); }
+
+static int64_t table_index(const fwd_ctx* c, int64_t i, int64_t j) {
+    const int64_t ri = i / c->gw, ci = i % c->gw, rj = j / c->gw, cj = j % c->gw;
+    return (ri - rj + c->gh - 1) * (2 * c->gw - 1) + (ci - cj + c->gw - 1);
+}
+
+int oracle_backward(const double* q, const double* k, const double* v, int bias_kind, const double* bias,
+                    int gh, int gw, int64_t B, int64_t H, int64_t N, int d, const double* dout, double clip,
+                    double* dq, double* dk, double* dv, double* db) {
+    fwd_ctx c;
+    int rc = ctx_init(&c, q, k, v, bias_kind, bias, gh, gw, B, H, N, d, 0);
+    if (rc) { if (rc == -2) ctx_free(&c); return rc; }
+    const int W = c.W;
+    const double sqrt_d = sqrt((double)d);
+    const int64_t tsz = (int64_t)(2 * gh - 1) * (2 * gw - 1);
+    const int64_t dbn = bias_kind == BIAS_DENSE ? H * N * N : (bias_kind == BIAS_RELPOS ? H * tsz : 0);
+    if (db) memset(db, 0, sizeof(double) * (size_t)dbn);
+    int fail = 0;
+    /* one (b, h) at a time per thread; the bias gradient is summed over the batch, so each thread
+     * keeps its own copy and the copies are added at the end in thread order */
+#pragma omp parallel
+    {
+        const int64_t nn = N * N;
+        double* S = (double*)malloc(sizeof(double) * nn);      /* S, then P~ */
+        double* dS = (double*)malloc(sizeof(double) * nn);
+        double* l = (double*)malloc(sizeof(double) * N);
+        double* O = (double*)malloc(sizeof(double) * N * d);
+        double* Vt = (double*)malloc(sizeof(double) * N * d);
+        double* sv = (double*)malloc(sizeof(double) * N * d);  /* s_i (queries) */
+        double* tv = (double*)malloc(sizeof(double) * N * d);  /* t_j (keys) */
+        double* ds = (double*)malloc(sizeof(double) * N * d);
+        double* dt = (double*)malloc(sizeof(double) * N * d);
+        double* dbl = db ? (double*)calloc((size_t)(dbn > 0 ? dbn : 1), sizeof(double)) : NULL;
+        const int ok = S && dS && l && O && Vt && sv && tv && ds && dt && (!db || dbl);
+        if (!ok) {
+#pragma omp atomic write
+            fail = 1;
+        }
+        /* every thread reaches the worksharing loops; one without its buffers only skips work */
+#pragma omp for schedule(static)
+        for (int64_t bh = 0; bh < B * H; ++bh) {
+            if (ok) {
+                const int64_t h = bh % H, base = bh * N;
+                for (int64_t n = 0; n < N; ++n)
+                    for (int ch = 0; ch < d; ++ch) {
+                        const double sq = (c.qb[(base + n) * W + ch / 32] >> (ch % 32)) & 1u ? 1.0 : -1.0;
+                        const double sk = (c.kb[(base + n) * W + ch / 32] >> (ch % 32)) & 1u ? 1.0 : -1.0;
+                        sv[n * d + ch] = (double)c.qmu[base + n] * sq;
+                        tv[n * d + ch] = (double)c.kmu[base + n] * sk;
+                        Vt[n * d + ch] = (double)c.vs[bh * d + ch] * (double)c.vq[(base + n) * d + ch];
+                    }
+                /* forward: S, P~ (in S), l, O with A = P^/255 */
+                for (int64_t i = 0; i < N; ++i) {
+                    double m = -INFINITY;
+                    for (int64_t j = 0; j < N; ++j) {
+                        double dot = 0.0;
+                        for (int ch = 0; ch < d; ++ch) dot += sv[i * d + ch] * tv[j * d + ch];
+                        S[i * N + j] = dot / sqrt_d + bias_at(&c, h, i, j);
+                        if (S[i * N + j] > m) m = S[i * N + j];
+                    }
+                    double li = 0.0;
+                    for (int64_t j = 0; j < N; ++j) {
+                        S[i * N + j] = exp(S[i * N + j] - m);
+                        li += S[i * N + j];
+                    }
+                    l[i] = li;
+                    for (int ch = 0; ch < d; ++ch) {
+                        double acc = 0.0;
+                        for (int64_t j = 0; j < N; ++j) acc += nearbyint(255.0 * S[i * N + j]) / 255.0 * Vt[j * d + ch];
+                        O[i * d + ch] = acc / li;
+                    }
+                }
+                /* dVt, dS, db */
+                const double* dO = dout + base * d;
+                for (int64_t j = 0; j < N; ++j)
+                    for (int ch = 0; ch < d; ++ch) {
+                        double acc = 0.0;
+                        for (int64_t i = 0; i < N; ++i) acc += nearbyint(255.0 * S[i * N + j]) / 255.0 / l[i] * dO[i * d + ch];
+                        dv[(base + j) * d + ch] = acc;
+                    }
+                for (int64_t i = 0; i < N; ++i) {
+                    double delta = 0.0;
+                    for (int ch = 0; ch < d; ++ch) delta += dO[i * d + ch] * O[i * d + ch];
+                    for (int64_t j = 0; j < N; ++j) {
+                        double dp = 0.0;
+                        for (int ch = 0; ch < d; ++ch) dp += dO[i * d + ch] * Vt[j * d + ch];
+                        const double g = S[i * N + j] / l[i] * (dp - delta);
+                        dS[i * N + j] = g;
+                        if (dbl && bias_kind == BIAS_DENSE) dbl[(h * N + i) * N + j] += g;
+                        if (dbl && bias_kind == BIAS_RELPOS) dbl[h * tsz + table_index(&c, i, j)] += g;
+                    }
+                }
+                /* ds, dt, then dq, dk through mu and the straight-through sign */
+                for (int64_t i = 0; i < N; ++i)
+                    for (int ch = 0; ch < d; ++ch) {
+                        double a = 0.0, b2 = 0.0;
+                        for (int64_t j = 0; j < N; ++j) {
+                            a += dS[i * N + j] * tv[j * d + ch];
+                            b2 += dS[j * N + i] * sv[j * d + ch];
+                        }
+                        ds[i * d + ch] = a / sqrt_d;
+                        dt[i * d + ch] = b2 / sqrt_d;
+                    }
+                for (int64_t n = 0; n < N; ++n) {
+                    const double* xq = q + (base + n) * d;
+                    const double* xk = k + (base + n) * d;
+                    double gq = 0.0, gk = 0.0;  /* sum_e ds_e sign_e: the gradient of mu */
+                    for (int ch = 0; ch < d; ++ch) {
+                        gq += ds[n * d + ch] * (xq[ch] >= 0.0 ? 1.0 : -1.0);
+                        gk += dt[n * d + ch] * (xk[ch] >= 0.0 ? 1.0 : -1.0);
+                    }
+                    for (int ch = 0; ch < d; ++ch) {
+                        dq[(base + n) * d + ch] = (double)c.qmu[base + n] * ds[n * d + ch] * ste_grad(xq[ch], clip) +
+                                                  sgn0(xq[ch]) / d * gq;
+                        dk[(base + n) * d + ch] = (double)c.kmu[base + n] * dt[n * d + ch] * ste_grad(xk[ch], clip) +
+                                                  sgn0(xk[ch]) / d * gk;
+                    }
+                }
+            }
+        }
+        if (db) {  /* the per-thread bias gradients, added in thread order */
+#pragma omp for ordered schedule(static, 1)
+            for (int t = 0; t < team_size(); ++t) {
+#pragma omp ordered
+                if (dbl)
+                    for (int64_t e = 0; e < dbn; ++e) db[e] += dbl[e];
+            }
+        }
+        free(S); free(dS); free(l); free(O); free(Vt); free(sv); free(tv); free(ds); free(dt); free(dbl);
     }
     ctx_free(&c);
     return fail ? -2 : 0;
