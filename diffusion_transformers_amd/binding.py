@@ -61,6 +61,11 @@ def _load():
     lib.binattn_attention_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, vp,
                                               i32, vp]
     lib.binattn_attention_noalloc.restype = i32
+    lib.binattn_backward_workspace.argtypes = [i32, i32, i32, i32]
+    lib.binattn_backward_workspace.restype = i64
+    lib.binattn_backward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i64, i32, i32, i32, i32, i32, i32,
+                                     ctypes.c_float, vp, vp, vp, vp, vp, i64, vp]
+    lib.binattn_backward.restype = i32
     lib.binattn_keep_plan.argtypes = [i64, i32, i32, i32, ctypes.POINTER(ctypes.c_int)]
     lib.binattn_keep_plan.restype = i32
     return lib
@@ -70,7 +75,7 @@ _lib = _load()
 EXPORTS = ["binattn_abi_version", "binattn_strerror", "binattn_words", "binattn_vq_ld", "binattn_pack_qk",
            "binattn_quant_v", "binattn_forward", "binattn_scores_i32", "binattn_qk_rowstats",
            "binattn_prepare", "binattn_attention_workspace", "binattn_attention", "binattn_attention_one_kernel",
-           "binattn_keep_plan", "binattn_attention_noalloc"]
+           "binattn_keep_plan", "binattn_attention_noalloc", "binattn_backward_workspace", "binattn_backward"]
 NOALLOC_SCRATCH_BYTES = 64 << 20  # BINATTN_NOALLOC_SCRATCH_BYTES
 QK_MFMA, QK_POPCOUNT = 0, 1
 
@@ -356,3 +361,40 @@ def attention_noalloc(q, k, v, bias=None, bias_kind=BIAS_NONE, grid=None, out_dt
                                         _p(out), _dt(out), _stream())
     _check("binattn_attention_noalloc", rc)
     return out
+
+
+def backward(q, k, v, o, dout, bias=None, bias_kind=BIAS_NONE, grid=None, ste_clip=0.0, bias_grad=True,
+             workspace=None):
+    """Gradients of the quantisation-aware forward (binattn_backward): q, k, v [B,H,N,d] the forward's
+    inputs, o its output and dout the loss gradient in it (both of one dtype) -> (dq, dk, dv fp32
+    [B,H,N,d], dbias fp32 dense [H,N,N] or table [H,(2gh-1)(2gw-1)], or None)."""
+    B, H, N, d = _need_qkv(q, k, v)
+    _need_qkv(o, dout, names=("o", "dout"))
+    if tuple(o.shape) != (B, H, N, d):
+        raise ValueError(f"o has shape {tuple(o.shape)}, expected {(B, H, N, d)}")
+    _need_bias(bias, bias_kind, grid, H, N, q.device)
+    dev = q.device
+    dq, dk, dv = (torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for _ in range(3))
+    db = None
+    bdt, ld, gh, gw = F16, 0, 0, 0
+    if bias is not None:
+        bdt = _dt(bias)
+        if bias_kind == BIAS_DENSE:
+            ld = bias.shape[-1]
+            if bias_grad:
+                db = torch.empty((H, N, N), dtype=torch.float32, device=dev)
+        elif bias_kind == BIAS_RELPOS:
+            gh, gw = grid
+            if bias_grad:
+                db = torch.empty((H, (2 * gh - 1) * (2 * gw - 1)), dtype=torch.float32, device=dev)
+    n = _lib.binattn_backward_workspace(B, H, N, d)
+    if n < 0:
+        raise BinAttnError("binattn_backward_workspace", -2)
+    if workspace is None:
+        workspace = torch.empty((n,), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (workspace.numel(),), (torch.uint8,), dev)
+    rc = _lib.binattn_backward(_p(q), _p(k), _p(v), _p(o), _p(dout), _dt(q), _dt(o), bias_kind, bdt, _p(bias), ld, gh,
+                               gw, B, H, N, d, float(ste_clip), _p(dq), _p(dk), _p(dv), _p(db), _p(workspace),
+                               workspace.numel(), _stream())
+    _check("binattn_backward", rc)
+    return dq, dk, dv, db

@@ -318,6 +318,54 @@ int binattn_attention(const void* q, const void* k, const void* v, int dtype, in
                          out_dtype, static_cast<char*>(workspace), (hipStream_t)stream);
 }
 
+int64_t binattn_backward_workspace(int B, int H, int N, int d) {
+    if (check_dims(B, H, N, d)) return -1;
+    return workspace_layout(B, H, N, d).total + backward_fp32_arrays_bytes(B, H, N, d);
+}
+
+int binattn_backward(const void* q, const void* k, const void* v, const void* o, const void* dout, int dtype,
+                     int grad_dtype, int bias_kind, int bias_dtype, const void* bias, int64_t bias_ld, int grid_h,
+                     int grid_w, int B, int H, int N, int d, float ste_clip, float* dq, float* dk, float* dv,
+                     float* dbias, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !o || !dout || !dq || !dk || !dv || !workspace) return BINATTN_EINVAL;
+    int rc = check_dims(B, H, N, d);
+    if (rc) return rc;
+    if (!dtype_ok(dtype) || !dtype_ok(grad_dtype)) return BINATTN_EUNSUPPORTED;
+    if (!(ste_clip >= 0.0f) || ste_clip > 3.0e38f) return BINATTN_EINVAL;  // NaN or infinite clip
+    const WorkspaceLayout l = workspace_layout(B, H, N, d);
+    if (workspace_bytes < l.total + backward_fp32_arrays_bytes(B, H, N, d)) return BINATTN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv) || (dbias && !aligned16(dbias)) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return BINATTN_EALIGN;
+    if ((rc = check_bias(bias_kind, bias_dtype, bias, bias_ld, grid_h, grid_w, N))) return rc;
+    if (bias_kind == BINATTN_BIAS_NONE && dbias) return BINATTN_EINVAL;
+    if ((rc = device_ready())) return rc;
+    char* ws = static_cast<char*>(workspace);
+    BwLaunch L = {};
+    L.qbits = reinterpret_cast<uint32_t*>(ws + l.qbits);
+    L.kbits = reinterpret_cast<uint32_t*>(ws + l.kbits);
+    L.qmu = reinterpret_cast<float*>(ws + l.qmu);
+    L.kmu = reinterpret_cast<float*>(ws + l.kmu);
+    L.vq = reinterpret_cast<int8_t*>(ws + l.vq);
+    L.vamax = reinterpret_cast<float*>(ws + l.vamax);
+    hipError_t e = launch_prepare(q, k, v, dtype == BINATTN_F32, B * H, N, d, binattn_vq_ld(N),
+                                  const_cast<uint32_t*>(L.qbits), const_cast<float*>(L.qmu),
+                                  const_cast<uint32_t*>(L.kbits), const_cast<float*>(L.kmu),
+                                  const_cast<int8_t*>(L.vq), const_cast<float*>(L.vamax), (hipStream_t)stream);
+    if (e != hipSuccess) return BINATTN_ELAUNCH;
+    L.q = q; L.k = k; L.o = o; L.dout = dout;
+    L.in_f32 = dtype == BINATTN_F32; L.g_f32 = grad_dtype == BINATTN_F32;
+    L.bias = bias; L.bias_ld = bias_ld; L.bias_f32 = bias_dtype == BINATTN_F32; L.bias_kind = bias_kind;
+    L.gh = grid_h; L.gw = grid_w;
+    L.B = B; L.H = H; L.N = N; L.d = d; L.clip = ste_clip;
+    L.scratch = reinterpret_cast<float*>(ws + l.total);
+    L.dq = dq; L.dk = dk; L.dv = dv; L.db = dbias;
+    if (bias_kind == BINATTN_BIAS_DENSE) L.db_count = (int64_t)H * N * N;
+    if (bias_kind == BINATTN_BIAS_RELPOS) L.db_count = (int64_t)H * (2 * grid_h - 1) * (2 * grid_w - 1);
+    return launched(launch_backward(L, (hipStream_t)stream));
+}
+
 int binattn_attention_noalloc(const void* q, const void* k, const void* v, int dtype, int bias_kind, int bias_dtype,
                               const void* bias, int64_t bias_ld, int grid_h, int grid_w, int B, int H, int N, int d,
                               void* out, int out_dtype, void* stream) {

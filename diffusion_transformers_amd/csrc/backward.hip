@@ -1,0 +1,609 @@
+// backward.hip -- gradients of the quantisation-aware BinaryAttention forward.
+//
+// "BinaryAttention" paper notes (CVPR 2026), Method details, key design 4 and the section on the
+// loss and training strategy: the model is fine-tuned with quantisation-aware training, the
+// forward keeps sign(Q), sign(K) and the backward passes the gradient through sign with a
+// straight-through estimator.  Readings where the pages are silent (the same as the CPU oracle):
+//   - sign: d sign(x)/dx := 1, or 1{|x| <= clip} when a clip > 0 is given;
+//   - mu = mean|x| is differentiated exactly (d mu/dx_c = sgn(x_c)/d, sgn(0) = 0);
+//   - the P (u8, 1/255) and V (int8, per channel) quantisers are straight-through: their forward
+//     values are the quantised ones, their gradients those of the identity;
+//   - the row max is a constant; the row sum l = sum exp(S - m) is differentiated.
+// With P = exp(S - m) / l, A = P^/255 / l (the weights the forward applies), Vt = s V^:
+//   dV_j = sum_i A_ij dO_i,   Delta_i = dO_i . O_i,   dP_ij = dO_i . Vt_j,
+//   dS_ij = P_ij (dP_ij - Delta_i) = db_ij (summed over the batch, or into the table entry (i, j)
+//   indexes),   ds_i = sum_j dS_ij t_j / sqrt(d),   dt_j = sum_i dS_ij s_i / sqrt(d)
+//   (s = mu_q sign(q), t = mu_k sign(k)),   dq_ic = mu_q ds_ic ste(q_ic) + sgn(q_ic)/d sum_e ds_ie
+//   sign(q_ie) (likewise dk), dv = dV.
+//
+// gfx950 design (one workgroup = 4 waves x 16 rows; tiles of 64 keys or queries):
+//  * bw_prep_kernel writes, from the packed Q/K and int8 V of the forward's preparation, fp32
+//    operand arrays already in the lane order of v_mfma_f32_16x16x4_f32 (Vt, mu_k sign(k)/sqrt(d),
+//    mu_q sign(q)/sqrt(d), dO twice), so that tiles are staged in LDS by plain 16-byte copies and
+//    every operand read is one ds_read_b128 of four consecutive k steps.
+//  * bw_q_kernel (a workgroup per 64 queries): the exact row max and row sum over all key tiles
+//    (scores by the forward's fp4 QK tile), Delta, then per key tile: scores again, P, dP on the
+//    fp32 MFMA, dS, dQ accumulated on the fp32 MFMA, and the bias gradient (dense: fp32 atomics
+//    over the batch; relative position: an LDS window of the tile's table entries, flushed with
+//    atomics).  Writes m, l and Delta for the second kernel.
+//  * bw_k_kernel (a workgroup per 64 keys): per query tile the transposed score tile (queries as
+//    MFMA rows, the lane's key as the column), P and P^, dP, dS, then dV and dK on the fp32 MFMA.
+#include "tile.h"
+
+namespace binattn {
+
+struct BwArgs {
+    const void* q;        // [B,H,N,d] input dtype
+    const void* k;
+    const void* o;        // forward output, grad dtype
+    const void* dout;     // grad dtype
+    int in_f32, g_f32;
+    const uint32_t* qbits;
+    const float* qmu;
+    const uint32_t* kbits;
+    const float* kmu;
+    const int8_t* vq;
+    const float* vamax;
+    int64_t ldv;
+    const void* bias;
+    int64_t bias_ld;
+    int bias_f32;
+    int gh, gw;
+    int B, H, N, d, W, Np;  // Np: N rounded up to a multiple of 64
+    float qk_scale;
+    float clip;
+    float* vt;   // [BH][Np][CP], channel c at (c % 4) KS + c / 4 (KS = CP / 4)
+    float* tt;   // [BH][Np/16][CP][16]: mu_k sign(k_c) / sqrt(d)
+    float* st;   // [BH][Np/16][CP][16]: mu_q sign(q_c) / sqrt(d)
+    float* do1;  // [BH][Np][CP], the order of vt
+    float* do2;  // [BH][Np/16][CP][16]
+    float* m;    // [BH][N] row max, row sum, Delta
+    float* l;
+    float* delta;
+    float* dq;   // [B,H,N,d] fp32
+    float* dk;
+    float* dv;
+    float* db;   // dense [H,N,N] or table [H,(2gh-1)(2gw-1)], fp32, zeroed first; may be null
+};
+
+__device__ __forceinline__ v4f mfma_f32x4(float a, float b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float ld_any(const void* p, int64_t i, int f32) {
+    return f32 ? static_cast<const float*>(p)[i] : (float)static_cast<const _Float16*>(p)[i];
+}
+
+__device__ __forceinline__ float ste_grad(float x, float clip) { return (clip > 0.0f && fabsf(x) > clip) ? 0.0f : 1.0f; }
+
+__device__ __forceinline__ float sgn0(float x) { return x > 0.0f ? 1.0f : (x < 0.0f ? -1.0f : 0.0f); }
+
+__device__ __forceinline__ bool sign_bit(const uint32_t* bits, int64_t tok, int W, int c) {
+    return (bits[tok * W + (c >> 5)] >> (c & 31)) & 1u;
+}
+
+// Row (query or key) slot of MFMA t's A operand row m: after the MFMA, lane (n, g) register r of
+// tile t holds row 16 g + 4 t + r (the forward's key_slot order).
+__device__ __forceinline__ int slot_row(int t, int m) { return 16 * (m >> 2) + 4 * t + (m & 3); }
+
+__global__ __launch_bounds__(256) void bw_zero_kernel(float* p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------------------------
+// fp32 operand arrays, 64 rows of one head per workgroup; rows >= N and channels >= d are zero.
+template <int CP>
+__global__ __launch_bounds__(256) void bw_prep_kernel(BwArgs a) {
+    constexpr int KS = CP / 4;
+    const int nb = a.Np / kBC;
+    const int64_t bh = blockIdx.x / nb;
+    const int j0 = (blockIdx.x % nb) * kBC;
+    const int N = a.N, d = a.d, W = a.W;
+    for (int e = threadIdx.x; e < kBC * CP; e += 256) {
+        const int jl = e / CP, c = e - jl * CP, j = j0 + jl;
+        const bool ok = j < N && c < d;
+        const int64_t tok = bh * N + j;
+        float vv = 0.0f, tk = 0.0f, sq = 0.0f, go = 0.0f;
+        if (ok) {
+            vv = a.vamax[bh * d + c] / 127.0f * (float)a.vq[(bh * d + c) * a.ldv + j];
+            tk = a.kmu[tok] * (sign_bit(a.kbits, tok, W, c) ? 1.0f : -1.0f) * a.qk_scale;
+            sq = a.qmu[tok] * (sign_bit(a.qbits, tok, W, c) ? 1.0f : -1.0f) * a.qk_scale;
+            go = ld_any(a.dout, tok * d + c, a.g_f32);
+        }
+        const int64_t lin = (bh * a.Np + j) * CP + (c & 3) * KS + (c >> 2);
+        const int64_t grp = bh * (int64_t)a.Np * CP + (int64_t)(j >> 4) * 16 * CP + c * 16 + (j & 15);
+        a.vt[lin] = vv;
+        a.do1[lin] = go;
+        a.tt[grp] = tk;
+        a.st[grp] = sq;
+        a.do2[grp] = go;
+    }
+}
+
+// 16-byte copy of n floats (a multiple of 4) from global to LDS by the workgroup.
+__device__ __forceinline__ void copy_to_lds(float* dst, const float* src, int n) {
+    for (int i = threadIdx.x; i < n / 4; i += 256)
+        reinterpret_cast<float4*>(dst)[i] = reinterpret_cast<const float4*>(src)[i];
+}
+
+// Sign words of 64 rows starting at row r0 of a head as fp4 {0, 1} A-operand rows (the forward's
+// K staging), rows >= N zero.
+template <int W>
+__device__ __forceinline__ void stage_bits_f4(uint32_t* dst, const uint32_t* bits, int r0, int N, int d) {
+    for (int id = threadIdx.x; id < kBC * W; id += 256) {
+        const int r = id / W, w = id - r * W;
+        uint32_t word = r0 + r < N ? bits[(int64_t)(r0 + r) * W + w] : 0u;
+        const int left = d - 32 * w;
+        if (left < 32) word &= (1u << left) - 1u;
+        uint32_t o[4];
+        unpack_bits32_f4(word, o);
+        const int t = (r & 15) >> 2, m = 4 * (r >> 4) + (r & 3);
+        *reinterpret_cast<uint4*>(&dst[((t * W + w) * 16 + m) * 4]) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+// Relative position on any grid: the table rows that queries [q0, q0 + 64) and keys [j0, j0 + 64)
+// touch, from row ri_min - rjm + gh - 1 (rjm: grid row of the tile's last key), at row stride
+// 2 gw - 1; returns that start's element offset in the head's table.
+__device__ __forceinline__ int stage_window(float* win, const BwArgs& a, const void* table, int q0, int j0) {
+    const int gw = a.gw, row_len = 2 * gw - 1, tsz = (2 * a.gh - 1) * row_len;
+    const int ri_min = q0 / gw, rjm = min((j0 + kBC - 1) / gw, a.gh - 1);
+    const int off = (ri_min - rjm + a.gh - 1) * row_len;
+    for (int e = threadIdx.x; e < kRelposWin; e += 256)
+        win[e] = off + e < tsz ? ld_any(table, off + e, a.bias_f32) : 0.0f;
+    return off;
+}
+
+// ---------------------------------------------------------------------------------------------
+template <int NT, int BIAS>
+struct alignas(16) BwQLds {
+    static constexpr int W = (NT + 1) / 2, CP = 16 * NT;
+    uint32_t k[4 * W * 16 * 4];
+    float mu[kBC];
+    float vt[kBC * CP];
+    float tt[kBC * CP];
+    float tw[BIAS == BK_RELPOS_G ? kRelposWin : 4];
+    float dwin[BIAS == BK_RELPOS_G ? kRelposWin : 4];
+    int kk[kBC];
+};
+
+template <int NT, int BIAS>
+__global__ __launch_bounds__(256) void bw_q_kernel(BwArgs a) {
+    constexpr int W = (NT + 1) / 2, CP = 16 * NT, KS = CP / 4;
+    constexpr bool DENSE = BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32;
+    __shared__ BwQLds<NT, BIAS> L;
+    const int N = a.N, d = a.d;
+    const int nqb = (N + kBR - 1) / kBR;
+    const int lb = xcd_logical_block(blockIdx.x, a.B * a.H * nqb);
+    const int bh = lb / nqb, q0 = (lb % nqb) * kBR, h = bh % a.H;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ntiles = (N + kBC - 1) / kBC;
+
+    FwdArgs fa = {};
+    fa.qbits = a.qbits; fa.qmu = a.qmu; fa.N = N; fa.d = d; fa.qk_scale = a.qk_scale;
+    const int qw0 = q0 + wave * 16;
+    const LaneQ lq = lane_query<NT>(fa, bh, qw0, g, n16);
+    const int i = lq.qi;
+    const int64_t tok = (int64_t)bh * N + i;
+
+    // dO of the lane's query, channels g + 4 s: the B operand of dP for every key tile
+    float doreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) doreg[s] = a.do1[((int64_t)bh * a.Np + i) * CP + g * KS + s];
+
+    const int gw = a.gw, row_len = 2 * gw - 1;
+    const int64_t tsz = (int64_t)(2 * a.gh - 1) * row_len;
+    const void* table = nullptr;
+    int aq = 0;
+    if (BIAS == BK_RELPOS_G) {
+        table = a.bias_f32 ? (const void*)((const float*)a.bias + h * tsz) : (const void*)((const _Float16*)a.bias + h * tsz);
+        const int ri = i / gw, ci = i - ri * gw;
+        aq = (ri - q0 / gw) * row_len + ci + gw - 1;
+    }
+    const int esz = BIAS == BK_DENSE_F32 ? 4 : 2;
+    const char* brow = nullptr;
+    int brow_bytes = 0;
+    if (DENSE) {
+        const int r0 = min(qw0, N);
+        brow = (const char*)a.bias + ((int64_t)h * N + r0) * a.bias_ld * esz;
+        brow_bytes = min(N - r0, 16) * (int)a.bias_ld * esz;
+    }
+    const int bvoff = (n16 * (int)a.bias_ld + 16 * g) * esz;
+
+    // Stage key tile j0: fp4 K operand, mu_k, (relative position) window and key parts, and
+    // (with_mm) the fp32 Vt and t tiles.  Returns the window's table offset.
+    auto stage = [&](int j0, bool with_mm) {
+        stage_bits_f4<W>(L.k, a.kbits + (int64_t)bh * N * W, j0, N, d);
+        if (tid < kBC) L.mu[tid] = j0 + tid < N ? a.kmu[(int64_t)bh * N + j0 + tid] : 0.0f;
+        int woff = 0;
+        if (BIAS == BK_RELPOS_G) {
+            woff = stage_window(L.tw, a, table, q0, j0);
+            if (tid < kBC) {
+                const int j = min(j0 + tid, N - 1);  // keys past N are masked: any in-window entry
+                const int rj = j / gw;
+                L.kk[tid] = -4 * (rj * row_len + j - rj * gw);
+            }
+            for (int e = tid; e < kRelposWin; e += 256) L.dwin[e] = 0.0f;
+        }
+        if (with_mm) {
+            copy_to_lds(L.vt, a.vt + ((int64_t)bh * a.Np + j0) * CP, kBC * CP);
+            copy_to_lds(L.tt, a.tt + ((int64_t)bh * a.Np + j0) * CP, kBC * CP);
+        }
+        return woff;
+    };
+    // Scores of key tile j0 for the lane's query (keys >= N: -inf), the forward's tile code.
+    auto scores = [&](int j0, float (&S)[16], float& mloc) {
+        const int jg = j0 + 16 * g;
+        BiasRegs<BIAS> br;
+        if (DENSE) load_bias<BIAS>(br, buffer_rsrc(brow + j0 * esz, brow_bytes - j0 * esz), bvoff);
+        const float* wrun = L.tw;
+        if (BIAS == BK_RELPOS_G) {
+            const int rjm = min((j0 + kBC - 1) / gw, a.gh - 1);
+            wrun = L.tw + aq + rjm * row_len;  // the keys' parts (L.kk) are gathered from here
+        }
+        tile_scores<NT, BIAS>(L.k, L.mu, lq, br, wrun, true, N - jg, S, mloc, L.kk + 16 * g);
+    };
+
+    // ---- pass 1: exact row max and row sum (online over the tiles), Delta
+    float mrun = -INFINITY, lpart = 0.0f;
+    for (int t = 0; t < ntiles; ++t) {
+        stage(t * kBC, false);
+        __syncthreads();
+        float S[16], mloc = -INFINITY;
+        scores(t * kBC, S, mloc);
+        const float mnew = fmaxf(mrun, rows4_max(mloc));
+        float sum = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) sum += fast_exp2((S[k] - mnew) * kLog2e);
+        lpart = lpart * fast_exp2((mrun - mnew) * kLog2e) + sum;
+        mrun = mnew;
+        __syncthreads();
+    }
+    const float mrow = mrun, lrow = rows4_sum(lpart);
+    float dpart = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int c = g + 4 * s;
+        if (c < d) dpart += doreg[s] * ld_any(a.o, tok * d + c, a.g_f32);
+    }
+    const float delta = rows4_sum(dpart);
+    if (lq.live && g == 0) {
+        a.m[tok] = mrow;
+        a.l[tok] = lrow;
+        a.delta[tok] = delta;
+    }
+    const float inv_l = lq.live ? 1.0f / lrow : 0.0f;
+
+    // ---- pass 2: P, dP, dS, the bias gradient, dQ
+    v4f dqacc[NT];
+#pragma unroll
+    for (int cb = 0; cb < NT; ++cb) dqacc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < ntiles; ++t) {
+        const int j0 = t * kBC, jg = j0 + 16 * g;
+        const int woff = stage(j0, true);
+        __syncthreads();
+        float S[16], mloc = -INFINITY;
+        scores(j0, S, mloc);
+        // dP: keys as MFMA rows (the score tile's order), channels as k
+        float dS[16];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+            const float* arow = &L.vt[slot_row(tt, n16) * CP + g * KS];
+#pragma unroll
+            for (int s = 0; s < KS; s += 4) {
+                const float4 a4 = *reinterpret_cast<const float4*>(arow + s);
+                acc = mfma_f32x4(a4.x, doreg[s], acc);
+                acc = mfma_f32x4(a4.y, doreg[s + 1], acc);
+                acc = mfma_f32x4(a4.z, doreg[s + 2], acc);
+                acc = mfma_f32x4(a4.w, doreg[s + 3], acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int kx = 4 * tt + r;
+                const float p = fast_exp2((S[kx] - mrow) * kLog2e) * inv_l;  // 0 for keys >= N and queries >= N
+                dS[kx] = p * (acc[r] - delta);
+            }
+        }
+        // the bias gradient: dS summed over the batch (dense), or into the table entries
+        if (DENSE && a.db && lq.live) {
+            float* drow = a.db + ((int64_t)h * N + i) * N;
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                if (jg + k < N) atomicAdd(drow + jg + k, dS[k]);
+        }
+        if (BIAS == BK_RELPOS_G && a.db) {
+            if (lq.live) {
+                const int rjm = min((j0 + kBC - 1) / gw, a.gh - 1);
+                const int base = aq + rjm * row_len;
+#pragma unroll
+                for (int k = 0; k < 16; ++k)
+                    if (jg + k < N) atomicAdd(&L.dwin[base + L.kk[16 * g + k] / 4], dS[k]);
+            }
+        }
+        // dQ: channels as MFMA rows, keys as k (step r: keys 16 g + r of the lanes' groups)
+#pragma unroll
+        for (int cb = 0; cb < NT; ++cb) {
+            const float* arow = &L.tt[(g * CP + 16 * cb + n16) * 16];
+#pragma unroll
+            for (int r = 0; r < 16; r += 4) {
+                const float4 a4 = *reinterpret_cast<const float4*>(arow + r);
+                dqacc[cb] = mfma_f32x4(a4.x, dS[r], dqacc[cb]);
+                dqacc[cb] = mfma_f32x4(a4.y, dS[r + 1], dqacc[cb]);
+                dqacc[cb] = mfma_f32x4(a4.z, dS[r + 2], dqacc[cb]);
+                dqacc[cb] = mfma_f32x4(a4.w, dS[r + 3], dqacc[cb]);
+            }
+        }
+        __syncthreads();
+        if (BIAS == BK_RELPOS_G && a.db) {  // flush the tile's table entries
+            float* dtab = a.db + h * tsz;
+            for (int e = tid; e < kRelposWin; e += 256) {
+                const float v = L.dwin[e];
+                if (v != 0.0f && woff + e < tsz) atomicAdd(dtab + woff + e, v);
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---- dq = mu_q ds ste(q) + sgn(q)/d sum_e ds_e sign(q_e); the lane has channels 16 cb + 4 g + r
+    float gpart = 0.0f;
+#pragma unroll
+    for (int cb = 0; cb < NT; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int c = 16 * cb + 4 * g + r;
+            if (c < d) gpart += dqacc[cb][r] * (sign_bit(a.qbits, tok, W, c) ? 1.0f : -1.0f);
+        }
+    const float gsum = rows4_sum(gpart);
+    if (!lq.live) return;
+    const float mu = a.qmu[tok];
+#pragma unroll
+    for (int cb = 0; cb < NT; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int c = 16 * cb + 4 * g + r;
+            if (c < d) {
+                const float x = ld_any(a.q, tok * d + c, a.in_f32);
+                a.dq[tok * d + c] = mu * dqacc[cb][r] * ste_grad(x, a.clip) + sgn0(x) / (float)d * gsum;
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------------------------
+template <int NT, int BIAS>
+struct alignas(16) BwKLds {
+    static constexpr int W = (NT + 1) / 2, CP = 16 * NT;
+    uint32_t q[4 * W * 16 * 4];
+    float cq[kBR], mx[kBR], il[kBR], dl[kBR];
+    float do1[kBR * CP];
+    float do2[kBR * CP];
+    float st[kBR * CP];
+    float bt[BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32 ? kBR * kBC : 4];  // dense bias tile [query][key]
+    float tw[BIAS == BK_RELPOS_G ? kRelposWin : 4];
+    int qq[kBR];
+};
+
+template <int NT, int BIAS>
+__global__ __launch_bounds__(256) void bw_k_kernel(BwArgs a) {
+    constexpr int W = (NT + 1) / 2, CP = 16 * NT, KS = CP / 4;
+    constexpr bool DENSE = BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32;
+    __shared__ BwKLds<NT, BIAS> L;
+    const int N = a.N, d = a.d;
+    const int nkb = (N + kBC - 1) / kBC;
+    const int lb = xcd_logical_block(blockIdx.x, a.B * a.H * nkb);
+    const int bh = lb / nkb, k0 = (lb % nkb) * kBC, h = bh % a.H;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nqt = (N + kBR - 1) / kBR;
+
+    // the lane's key: fp4 sign operand (+-2) of word g, seed -sum sign(k), mu_k, Vt channels g + 4 s
+    const int jraw = k0 + wave * 16 + n16;
+    const bool klive = jraw < N;
+    const int j = klive ? jraw : N - 1;
+    const int64_t tok = (int64_t)bh * N + j;
+    v4i kop;
+    const float seed = load_q<W>(a.kbits + tok * W, klive, d, g, kop);
+    const v4f dseed = v4f{seed, seed, seed, seed};
+    const float muk = a.kmu[tok];
+    float vreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) vreg[s] = a.vt[((int64_t)bh * a.Np + j) * CP + g * KS + s];
+
+    const int gw = a.gw, row_len = 2 * gw - 1;
+    const int64_t tsz = (int64_t)(2 * a.gh - 1) * row_len;
+    const void* table = nullptr;
+    int kpart = 0;
+    if (BIAS == BK_RELPOS_G) {
+        table = a.bias_f32 ? (const void*)((const float*)a.bias + h * tsz) : (const void*)((const _Float16*)a.bias + h * tsz);
+        const int rjm = min((k0 + kBC - 1) / gw, a.gh - 1);
+        const int rj = j / gw, cj = j - rj * gw;
+        kpart = (rjm - rj) * row_len + gw - 1 - cj;
+    }
+
+    v4f dvacc[NT], dkacc[NT];
+#pragma unroll
+    for (int cb = 0; cb < NT; ++cb) dvacc[cb] = dkacc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int qt = 0; qt < nqt; ++qt) {
+        const int i0 = qt * kBR;
+        // ---- stage the query tile
+        stage_bits_f4<W>(L.q, a.qbits + (int64_t)bh * N * W, i0, N, d);
+        if (tid < kBR) {
+            const int i = i0 + tid;
+            const bool ok = i < N;
+            const int64_t qt_ = (int64_t)bh * N + (ok ? i : N - 1);
+            L.cq[tid] = ok ? a.qmu[qt_] * a.qk_scale : 0.0f;
+            L.mx[tid] = ok ? a.m[qt_] : 0.0f;
+            L.il[tid] = ok ? 1.0f / a.l[qt_] : 0.0f;
+            L.dl[tid] = ok ? a.delta[qt_] : 0.0f;
+            if (BIAS == BK_RELPOS_G) {
+                const int ii = ok ? i : N - 1, ri = ii / gw;
+                L.qq[tid] = (ri - i0 / gw) * row_len + ii - ri * gw;
+            }
+        }
+        copy_to_lds(L.do1, a.do1 + ((int64_t)bh * a.Np + i0) * CP, kBR * CP);
+        copy_to_lds(L.do2, a.do2 + ((int64_t)bh * a.Np + i0) * CP, kBR * CP);
+        copy_to_lds(L.st, a.st + ((int64_t)bh * a.Np + i0) * CP, kBR * CP);
+        if (DENSE) {
+            for (int e = tid; e < kBR * kBC; e += 256) {
+                const int r = e / kBC, c = e - r * kBC;
+                const bool ok = i0 + r < N && k0 + c < N;
+                L.bt[e] = ok ? ld_any(a.bias, ((int64_t)h * N + i0 + r) * a.bias_ld + k0 + c, a.bias_f32) : 0.0f;
+            }
+        }
+        if (BIAS == BK_RELPOS_G) stage_window(L.tw, a, table, i0, k0);
+        __syncthreads();
+
+        // ---- scores: queries as MFMA rows (slot order), the lane's key as the column
+        const int koff = ((g < W ? g : 0) * 16 + n16) * 4;
+        float S[16], P[16], Pq[16], dS[16];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const v4f D = mfma_f4(*reinterpret_cast<const v4i*>(&L.q[tt * W * 64 + koff]), kop, dseed);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int kx = 4 * tt + r, il = 16 * g + kx;  // query i0 + il
+                float b = 0.0f;
+                if (DENSE) b = L.bt[il * kBC + wave * 16 + n16];
+                if (BIAS == BK_RELPOS_G) b = L.tw[L.qq[il] + kpart];
+                S[kx] = __builtin_fmaf(D[r] * muk, L.cq[il], b);
+            }
+        }
+        // ---- P, P^ (for dV), dP, dS
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+            const float* arow = &L.do1[slot_row(tt, n16) * CP + g * KS];
+#pragma unroll
+            for (int s = 0; s < KS; s += 4) {
+                const float4 a4 = *reinterpret_cast<const float4*>(arow + s);
+                acc = mfma_f32x4(a4.x, vreg[s], acc);
+                acc = mfma_f32x4(a4.y, vreg[s + 1], acc);
+                acc = mfma_f32x4(a4.z, vreg[s + 2], acc);
+                acc = mfma_f32x4(a4.w, vreg[s + 3], acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int kx = 4 * tt + r, il = 16 * g + kx;
+                const float p255 = fast_exp2(__builtin_fmaf(S[kx], kLog2e, kLog2_255 - L.mx[il] * kLog2e));
+                const float iv = L.il[il];  // 0 for queries >= N
+                P[kx] = p255 * (1.0f / 255.0f) * iv;
+                Pq[kx] = __builtin_rintf(p255) * (1.0f / 255.0f) * iv;
+                dS[kx] = P[kx] * (acc[r] - L.dl[il]);
+            }
+        }
+        // ---- dV (B = P^ / (255 l)) and dK (B = dS): channels as MFMA rows, queries 16 g + r as k
+#pragma unroll
+        for (int cb = 0; cb < NT; ++cb) {
+            const float* arow_o = &L.do2[(g * CP + 16 * cb + n16) * 16];
+            const float* arow_s = &L.st[(g * CP + 16 * cb + n16) * 16];
+#pragma unroll
+            for (int r = 0; r < 16; r += 4) {
+                const float4 o4 = *reinterpret_cast<const float4*>(arow_o + r);
+                const float4 s4 = *reinterpret_cast<const float4*>(arow_s + r);
+                dvacc[cb] = mfma_f32x4(o4.x, Pq[r], dvacc[cb]);
+                dvacc[cb] = mfma_f32x4(o4.y, Pq[r + 1], dvacc[cb]);
+                dvacc[cb] = mfma_f32x4(o4.z, Pq[r + 2], dvacc[cb]);
+                dvacc[cb] = mfma_f32x4(o4.w, Pq[r + 3], dvacc[cb]);
+                dkacc[cb] = mfma_f32x4(s4.x, dS[r], dkacc[cb]);
+                dkacc[cb] = mfma_f32x4(s4.y, dS[r + 1], dkacc[cb]);
+                dkacc[cb] = mfma_f32x4(s4.z, dS[r + 2], dkacc[cb]);
+                dkacc[cb] = mfma_f32x4(s4.w, dS[r + 3], dkacc[cb]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- dk = mu_k dt ste(k) + sgn(k)/d sum_e dt_e sign(k_e), dv; channels 16 cb + 4 g + r
+    float gpart = 0.0f;
+#pragma unroll
+    for (int cb = 0; cb < NT; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int c = 16 * cb + 4 * g + r;
+            if (c < d) gpart += dkacc[cb][r] * (sign_bit(a.kbits, tok, W, c) ? 1.0f : -1.0f);
+        }
+    const float gsum = rows4_sum(gpart);
+    if (!klive) return;
+#pragma unroll
+    for (int cb = 0; cb < NT; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int c = 16 * cb + 4 * g + r;
+            if (c < d) {
+                const float x = ld_any(a.k, tok * d + c, a.in_f32);
+                a.dk[tok * d + c] = muk * dkacc[cb][r] * ste_grad(x, a.clip) + sgn0(x) / (float)d * gsum;
+                a.dv[tok * d + c] = dvacc[cb][r];
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------------------------
+template <int NT, int BK>
+static void launch_bw_bk(const BwArgs& a, hipStream_t s) {
+    const unsigned nb = (unsigned)((int64_t)a.B * a.H * ((a.N + kBC - 1) / kBC));
+    hipLaunchKernelGGL((bw_q_kernel<NT, BK>), dim3(nb), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bw_k_kernel<NT, BK>), dim3(nb), dim3(256), 0, s, a);
+}
+
+template <int NT>
+static void launch_bw_nt(const BwArgs& a, int bk, hipStream_t s) {
+    const unsigned np = (unsigned)((int64_t)a.B * a.H * (a.Np / kBC));
+    hipLaunchKernelGGL((bw_prep_kernel<16 * NT>), dim3(np), dim3(256), 0, s, a);
+    switch (bk) {
+        case BK_NONE: launch_bw_bk<NT, BK_NONE>(a, s); break;
+        case BK_DENSE_F16: launch_bw_bk<NT, BK_DENSE_F16>(a, s); break;
+        case BK_DENSE_F32: launch_bw_bk<NT, BK_DENSE_F32>(a, s); break;
+        default: launch_bw_bk<NT, BK_RELPOS_G>(a, s); break;
+    }
+}
+
+int64_t backward_fp32_arrays_bytes(int B, int H, int N, int d) {
+    const int64_t Np = ((int64_t)N + kBC - 1) / kBC * kBC, CP = 16 * ((d + 15) / 16);
+    return 5 * (int64_t)B * H * Np * CP * 4 + 3 * (int64_t)B * H * N * 4 + 8 * 256;
+}
+
+hipError_t launch_backward(const BwLaunch& L, hipStream_t s) {
+    BwArgs a = {};
+    a.q = L.q; a.k = L.k; a.o = L.o; a.dout = L.dout; a.in_f32 = L.in_f32; a.g_f32 = L.g_f32;
+    a.qbits = L.qbits; a.qmu = L.qmu; a.kbits = L.kbits; a.kmu = L.kmu; a.vq = L.vq; a.vamax = L.vamax;
+    a.ldv = ((int64_t)L.N + 63) / 64 * 64;
+    a.bias = L.bias; a.bias_ld = L.bias_ld; a.bias_f32 = L.bias_f32; a.gh = L.gh; a.gw = L.gw;
+    a.B = L.B; a.H = L.H; a.N = L.N; a.d = L.d; a.W = (L.d + 31) / 32; a.Np = (int)(((int64_t)L.N + kBC - 1) / kBC * kBC);
+    a.qk_scale = (float)(1.0 / sqrt((double)L.d));
+    a.clip = L.clip;
+    // fp32 arrays in the scratch region, each 256-byte aligned
+    const int64_t BH = (int64_t)L.B * L.H, CP = 16 * ((L.d + 15) / 16);
+    auto up = [](int64_t x) { return (x + 63) / 64 * 64; };  // floats
+    float* p = L.scratch;
+    const int64_t arr = up(BH * a.Np * CP), vec = up(BH * L.N);
+    a.vt = p; p += arr;
+    a.tt = p; p += arr;
+    a.st = p; p += arr;
+    a.do1 = p; p += arr;
+    a.do2 = p; p += arr;
+    a.m = p; p += vec;
+    a.l = p; p += vec;
+    a.delta = p;
+    a.dq = L.dq; a.dk = L.dk; a.dv = L.dv; a.db = L.db;
+    if (L.db && L.db_count > 0)
+        hipLaunchKernelGGL(bw_zero_kernel, dim3((unsigned)((L.db_count + 255) / 256)), dim3(256), 0, s, L.db, L.db_count);
+    int bk = BK_NONE;
+    if (L.bias_kind == 1) bk = L.bias_f32 ? BK_DENSE_F32 : BK_DENSE_F16;
+    if (L.bias_kind == 2) bk = BK_RELPOS_G;
+    switch ((L.d + 15) / 16) {
+        case 1: launch_bw_nt<1>(a, bk, s); break;
+        case 2: launch_bw_nt<2>(a, bk, s); break;
+        case 3: launch_bw_nt<3>(a, bk, s); break;
+        case 4: launch_bw_nt<4>(a, bk, s); break;
+        case 5: launch_bw_nt<5>(a, bk, s); break;
+        case 6: launch_bw_nt<6>(a, bk, s); break;
+        case 7: launch_bw_nt<7>(a, bk, s); break;
+        default: launch_bw_nt<8>(a, bk, s); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace binattn

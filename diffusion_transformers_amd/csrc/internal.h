@@ -44,6 +44,35 @@ hipError_t launch_forward_gather(const FwdArgs& a, hipStream_t s);
 hipError_t launch_attention_fused(const FwdArgs& a, int bias_kind, hipStream_t s);
 bool attention_fused_applies(const FwdArgs& a, int bias_kind);
 hipError_t launch_scores(const FwdArgs& a, hipStream_t s);
+
+// Backward of the quantisation-aware forward (backward.hip): packed inputs from launch_prepare,
+// fp32 scratch of backward_fp32_arrays_bytes(B, H, N, d) bytes (256-byte aligned).
+struct BwLaunch {
+    const void* q;
+    const void* k;
+    const void* o;
+    const void* dout;
+    int in_f32, g_f32;
+    const uint32_t* qbits;
+    const float* qmu;
+    const uint32_t* kbits;
+    const float* kmu;
+    const int8_t* vq;
+    const float* vamax;
+    const void* bias;
+    int64_t bias_ld;
+    int bias_f32, bias_kind, gh, gw;
+    int B, H, N, d;
+    float clip;
+    float* scratch;
+    float* dq;
+    float* dk;
+    float* dv;
+    float* db;
+    int64_t db_count;
+};
+int64_t backward_fp32_arrays_bytes(int B, int H, int N, int d);
+hipError_t launch_backward(const BwLaunch& L, hipStream_t s);
 hipError_t launch_qk_stats(const FwdArgs& a, int method, float* rowmax, float* rowsum, hipStream_t s);
 bool relpos_window_fits(int gw);
 // The head-resident kernel's workgroup plan {a, f, b, r} for nheads heads of nqb query blocks

@@ -229,6 +229,40 @@ int binattn_attention_noalloc(const void* q, const void* k, const void* v, int d
                               void* out, int out_dtype, void* stream);
 
 /*
+ * binattn_backward -- gradients of the quantisation-aware forward for training (QAT).
+ * Passages: key design 4 (quantisation-aware training: the forward keeps sign(Q), sign(K), and
+ * a straight-through estimator (STE) makes sign differentiable) and key designs 1-3 (the forward
+ * being differentiated).  The pages fix no more; the readings taken:
+ *   d sign(x)/dx := 1 (ste_clip == 0) or 1{|x| <= ste_clip} (ste_clip > 0);
+ *   mu = mean|x| is differentiated exactly (d mu/dx_c = sgn(x_c)/d, sgn(0) = 0);
+ *   the P (u8, scale 1/255) and V (int8 per channel) quantisers are straight-through;
+ *   the row max is a constant, the row sum l = sum_j exp(S_ij - m_i) is differentiated.
+ * With P = exp(S - m)/l, A = P^/(255 l), Vt = s V^, O the forward output:
+ *   dv_j = sum_i A_ij dO_i;  dS_ij = P_ij (dO_i . Vt_j - dO_i . O_i);  dbias = dS (dense: summed
+ *   over the batch; relative position: each table entry sums the dS_ij that index it);
+ *   ds_i = sum_j dS_ij mu_k_j sign(k_j)/sqrt(d);  dq_ic = mu_q_i ds_ic ste(q_ic) +
+ *   sgn(q_ic)/d sum_e ds_ie sign(q_ie);  dk likewise with dt_j = sum_i dS_ij mu_q_i sign(q_i)/sqrt(d).
+ * The row statistics and P^ are recomputed with the exact row max.
+ *
+ *   q, k, v        [B,H,N,d] of dtype (the forward's inputs)
+ *   o, dout        [B,H,N,d] of grad_dtype: the forward's output and the gradient of the loss in it
+ *   bias...        as binattn_forward
+ *   ste_clip       >= 0 (0: no clip)
+ *   dq, dk, dv     [B,H,N,d] fp32, fully overwritten
+ *   dbias          fp32 dense [H,N,N] (row stride N) or table [H,(2gh-1)(2gw-1)]; fully overwritten;
+ *                  may be NULL to skip the bias gradient; must be NULL for BINATTN_BIAS_NONE
+ *   workspace      at least binattn_backward_workspace(B,H,N,d) bytes, 256-byte aligned, caller-owned
+ * Errors as binattn_attention; a NaN or infinite ste_clip, a dbias with no bias or a small
+ * workspace is BINATTN_EINVAL.  The dense and table gradients are summed with fp32 atomics, so
+ * their rounding can vary from call to call.
+ */
+int64_t binattn_backward_workspace(int B, int H, int N, int d);
+int binattn_backward(const void* q, const void* k, const void* v, const void* o, const void* dout, int dtype,
+                     int grad_dtype, int bias_kind, int bias_dtype, const void* bias, int64_t bias_ld, int grid_h,
+                     int grid_w, int B, int H, int N, int d, float ste_clip, float* dq, float* dk, float* dv,
+                     float* dbias, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * binattn_keep_plan -- inspection export (host only, no device call): how the head-resident
  * forward splits the query blocks of every (b, h) over workgroups.  nheads = B*H heads of
  * nqb = ceil(N / 64) query blocks (1 <= nqb <= 10, the rows that kernel takes), `slots` resident
