@@ -61,7 +61,7 @@ def _load():
     lib.binattn_attention_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, vp,
                                               i32, vp]
     lib.binattn_attention_noalloc.restype = i32
-    lib.binattn_backward_workspace.argtypes = [i32, i32, i32, i32]
+    lib.binattn_backward_workspace.argtypes = [i32, i32, i32, i32, i32]
     lib.binattn_backward_workspace.restype = i64
     lib.binattn_backward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i64, i32, i32, i32, i32, i32, i32,
                                      ctypes.c_float, vp, vp, vp, vp, vp, i64, vp]
@@ -387,7 +387,7 @@ def backward(q, k, v, o, dout, bias=None, bias_kind=BIAS_NONE, grid=None, ste_cl
             gh, gw = grid
             if bias_grad:
                 db = torch.empty((H, (2 * gh - 1) * (2 * gw - 1)), dtype=torch.float32, device=dev)
-    n = _lib.binattn_backward_workspace(B, H, N, d)
+    n = _lib.binattn_backward_workspace(B, H, N, d, bias_kind)
     if n < 0:
         raise BinAttnError("binattn_backward_workspace", -2)
     if workspace is None:

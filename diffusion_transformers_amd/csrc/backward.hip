@@ -63,8 +63,13 @@ struct BwArgs {
     float* dq;   // [B,H,N,d] fp32
     float* dk;
     float* dv;
-    float* db;   // dense [H,N,N] or table [H,(2gh-1)(2gw-1)], fp32, zeroed first; may be null
+    float* db;   // dense [H,N,N] or table [H,(2gh-1)(2gw-1)], fp32; may be null
+    float* dsb;  // dense bias gradient: dS of every batch item [B][H][N][Np], summed over B afterwards
+    float* dtp;  // table gradient of each query-block workgroup [B H nqb][kTabMax] when the table has
+                 // at most kTabMax entries (else null: the entries go to db by atomics per key tile)
 };
+
+constexpr int kTabMax = 4096;  // table entries a workgroup accumulates whole in LDS
 
 __device__ __forceinline__ v4f mfma_f32x4(float a, float b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -85,6 +90,35 @@ __device__ __forceinline__ bool sign_bit(const uint32_t* bits, int64_t tok, int 
 // Row (query or key) slot of MFMA t's A operand row m: after the MFMA, lane (n, g) register r of
 // tile t holds row 16 g + 4 t + r (the forward's key_slot order).
 __device__ __forceinline__ int slot_row(int t, int m) { return 16 * (m >> 2) + 4 * t + (m & 3); }
+
+// db[h][i][j] = sum over b of dS[b][h][i][j], in batch order (deterministic).
+__global__ __launch_bounds__(256) void bw_dbias_kernel(const float* __restrict__ dsb, float* __restrict__ db, int B,
+                                                       int H, int N, int Np) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t hn = (int64_t)H * N;
+    if (e >= hn * N) return;
+    const int64_t r = e / N, j = e - r * N;  // r = h N + i
+    const int64_t stride = hn * Np;
+    const float* p = dsb + r * Np + j;
+    float acc = 0.0f;
+    for (int b = 0; b < B; ++b) acc += p[b * stride];
+    db[e] = acc;
+}
+
+// Table gradient: db[h][e] = sum of the partial tables of the query-block workgroups of head h
+// (stored at logical block (b H + h) nqb + query block), in batch and block order (deterministic).
+__global__ __launch_bounds__(256) void bw_dtable_kernel(const float* __restrict__ dtp, float* __restrict__ db, int B,
+                                                        int H, int nqb, int tsz) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)H * tsz) return;
+    const int h = (int)(e / tsz), t = (int)(e - (int64_t)h * tsz);
+    float acc = 0.0f;
+    for (int b = 0; b < B; ++b) {
+        const float* p = dtp + ((int64_t)(b * H + h) * nqb) * kTabMax + t;
+        for (int qb = 0; qb < nqb; ++qb) acc += p[(int64_t)qb * kTabMax];
+    }
+    db[e] = acc;
+}
 
 __global__ __launch_bounds__(256) void bw_zero_kernel(float* p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -164,7 +198,7 @@ struct alignas(16) BwQLds {
     float vt[kBC * CP];
     float tt[kBC * CP];
     float tw[BIAS == BK_RELPOS_G ? kRelposWin : 4];
-    float dwin[BIAS == BK_RELPOS_G ? kRelposWin : 4];
+    float dwin[BIAS == BK_RELPOS_G ? kTabMax : 4];  // the whole table's gradient, or one tile's window
     int kk[kBC];
 };
 
@@ -225,7 +259,6 @@ __global__ __launch_bounds__(256) void bw_q_kernel(BwArgs a) {
                 const int rj = j / gw;
                 L.kk[tid] = -4 * (rj * row_len + j - rj * gw);
             }
-            for (int e = tid; e < kRelposWin; e += 256) L.dwin[e] = 0.0f;
         }
         if (with_mm) {
             copy_to_lds(L.vt, a.vt + ((int64_t)bh * a.Np + j0) * CP, kBC * CP);
@@ -277,6 +310,9 @@ __global__ __launch_bounds__(256) void bw_q_kernel(BwArgs a) {
     const float inv_l = lq.live ? 1.0f / lrow : 0.0f;
 
     // ---- pass 2: P, dP, dS, the bias gradient, dQ
+    const bool whole = BIAS == BK_RELPOS_G && a.db && a.dtp;  // the table's gradient accumulates in LDS
+    if (BIAS == BK_RELPOS_G && a.db)
+        for (int e = tid; e < (whole ? kTabMax : kRelposWin); e += 256) L.dwin[e] = 0.0f;
     v4f dqacc[NT];
 #pragma unroll
     for (int cb = 0; cb < NT; ++cb) dqacc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -307,17 +343,18 @@ __global__ __launch_bounds__(256) void bw_q_kernel(BwArgs a) {
                 dS[kx] = p * (acc[r] - delta);
             }
         }
-        // the bias gradient: dS summed over the batch (dense), or into the table entries
+        // the bias gradient: dS of this batch item stored whole (dense; summed over the batch by
+        // bw_dbias_kernel), or into the table entries
         if (DENSE && a.db && lq.live) {
-            float* drow = a.db + ((int64_t)h * N + i) * N;
+            float* drow = a.dsb + ((int64_t)bh * N + i) * a.Np + jg;  // keys past N hold 0
 #pragma unroll
-            for (int k = 0; k < 16; ++k)
-                if (jg + k < N) atomicAdd(drow + jg + k, dS[k]);
+            for (int k = 0; k < 16; k += 4)
+                *reinterpret_cast<float4*>(drow + k) = make_float4(dS[k], dS[k + 1], dS[k + 2], dS[k + 3]);
         }
         if (BIAS == BK_RELPOS_G && a.db) {
             if (lq.live) {
                 const int rjm = min((j0 + kBC - 1) / gw, a.gh - 1);
-                const int base = aq + rjm * row_len;
+                const int base = aq + rjm * row_len + (whole ? woff : 0);  // window index (+ its table offset)
 #pragma unroll
                 for (int k = 0; k < 16; ++k)
                     if (jg + k < N) atomicAdd(&L.dwin[base + L.kk[16 * g + k] / 4], dS[k]);
@@ -337,14 +374,19 @@ __global__ __launch_bounds__(256) void bw_q_kernel(BwArgs a) {
             }
         }
         __syncthreads();
-        if (BIAS == BK_RELPOS_G && a.db) {  // flush the tile's table entries
+        if (BIAS == BK_RELPOS_G && a.db && !whole) {  // flush the tile's window entries
             float* dtab = a.db + h * tsz;
             for (int e = tid; e < kRelposWin; e += 256) {
                 const float v = L.dwin[e];
                 if (v != 0.0f && woff + e < tsz) atomicAdd(dtab + woff + e, v);
+                L.dwin[e] = 0.0f;
             }
             __syncthreads();
         }
+    }
+    if (whole) {  // this workgroup's share of the table gradient, summed over workgroups afterwards
+        float* dst = a.dtp + (int64_t)lb * kTabMax;  // logical block: (b H + h) nqb + query block
+        for (int e = tid; e < kTabMax; e += 256) dst[e] = L.dwin[e];
     }
 
     // ---- dq = mu_q ds ste(q) + sgn(q)/d sum_e ds_e sign(q_e); the lane has channels 16 cb + 4 g + r
@@ -560,9 +602,10 @@ static void launch_bw_nt(const BwArgs& a, int bk, hipStream_t s) {
     }
 }
 
-int64_t backward_fp32_arrays_bytes(int B, int H, int N, int d) {
-    const int64_t Np = ((int64_t)N + kBC - 1) / kBC * kBC, CP = 16 * ((d + 15) / 16);
-    return 5 * (int64_t)B * H * Np * CP * 4 + 3 * (int64_t)B * H * N * 4 + 8 * 256;
+int64_t backward_fp32_arrays_bytes(int B, int H, int N, int d, int bias_kind) {
+    const int64_t Np = ((int64_t)N + kBC - 1) / kBC * kBC, CP = 16 * ((d + 15) / 16), BH = (int64_t)B * H;
+    const int64_t extra = bias_kind == 1 ? BH * N * Np : (bias_kind == 2 ? BH * (Np / kBR) * kTabMax : 0);
+    return 5 * BH * Np * CP * 4 + 3 * BH * N * 4 + extra * 4 + 9 * 256;
 }
 
 hipError_t launch_backward(const BwLaunch& L, hipStream_t s) {
@@ -586,9 +629,12 @@ hipError_t launch_backward(const BwLaunch& L, hipStream_t s) {
     a.do2 = p; p += arr;
     a.m = p; p += vec;
     a.l = p; p += vec;
-    a.delta = p;
+    a.delta = p; p += vec;
+    a.dsb = L.bias_kind == 1 ? p : nullptr;
+    const int64_t tsz = (int64_t)(2 * L.gh - 1) * (2 * L.gw - 1);
+    a.dtp = L.bias_kind == 2 && tsz <= kTabMax ? p : nullptr;
     a.dq = L.dq; a.dk = L.dk; a.dv = L.dv; a.db = L.db;
-    if (L.db && L.db_count > 0)
+    if (L.db && L.db_count > 0 && L.bias_kind == 2 && !a.dtp)  // table entries collect atomics
         hipLaunchKernelGGL(bw_zero_kernel, dim3((unsigned)((L.db_count + 255) / 256)), dim3(256), 0, s, L.db, L.db_count);
     int bk = BK_NONE;
     if (L.bias_kind == 1) bk = L.bias_f32 ? BK_DENSE_F32 : BK_DENSE_F16;
@@ -603,6 +649,12 @@ hipError_t launch_backward(const BwLaunch& L, hipStream_t s) {
         case 7: launch_bw_nt<7>(a, bk, s); break;
         default: launch_bw_nt<8>(a, bk, s); break;
     }
+    if (L.db && L.bias_kind == 1)
+        hipLaunchKernelGGL(bw_dbias_kernel, dim3((unsigned)((L.db_count + 255) / 256)), dim3(256), 0, s, a.dsb, L.db,
+                           L.B, L.H, L.N, a.Np);
+    if (L.db && a.dtp)
+        hipLaunchKernelGGL(bw_dtable_kernel, dim3((unsigned)((L.db_count + 255) / 256)), dim3(256), 0, s, a.dtp, L.db,
+                           L.B, L.H, a.Np / kBR, (int)tsz);
     return hipGetLastError();
 }
 

@@ -251,12 +251,16 @@ int binattn_attention_noalloc(const void* q, const void* k, const void* v, int d
  *   dq, dk, dv     [B,H,N,d] fp32, fully overwritten
  *   dbias          fp32 dense [H,N,N] (row stride N) or table [H,(2gh-1)(2gw-1)]; fully overwritten;
  *                  may be NULL to skip the bias gradient; must be NULL for BINATTN_BIAS_NONE
- *   workspace      at least binattn_backward_workspace(B,H,N,d) bytes, 256-byte aligned, caller-owned
+ *   workspace      at least binattn_backward_workspace(B,H,N,d,bias_kind) bytes, 256-byte aligned,
+ *                  caller-owned (with the dense bias it holds every batch item's dS, B*H*N*ceil64(N)
+ *                  floats, summed over the batch in order; with the table, each 64-query block's
+ *                  share of a table of at most 4096 entries, summed in order)
  * Errors as binattn_attention; a NaN or infinite ste_clip, a dbias with no bias or a small
- * workspace is BINATTN_EINVAL.  The dense and table gradients are summed with fp32 atomics, so
- * their rounding can vary from call to call.
+ * workspace is BINATTN_EINVAL.  A table of more than 4096 entries collects its gradient with
+ * fp32 atomics, so its rounding can vary from call to call; every other output is deterministic.
+ * binattn_backward_workspace returns -1 for unsupported sizes or an unknown bias kind.
  */
-int64_t binattn_backward_workspace(int B, int H, int N, int d);
+int64_t binattn_backward_workspace(int B, int H, int N, int d, int bias_kind);
 int binattn_backward(const void* q, const void* k, const void* v, const void* o, const void* dout, int dtype,
                      int grad_dtype, int bias_kind, int bias_dtype, const void* bias, int64_t bias_ld, int grid_h,
                      int grid_w, int B, int H, int N, int d, float ste_clip, float* dq, float* dk, float* dv,

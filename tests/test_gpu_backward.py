@@ -117,7 +117,7 @@ def test_backward_without_bias_gradient_and_workspace_reuse():
     bt = b.aligned_dense_bias(_t(inp["bias"]))
     o = b.attention(q, k, v, bt, b.BIAS_DENSE, out_dtype=torch.float32)
     do = torch.randn(q.shape, dtype=torch.float32, device=DEV)
-    ws = torch.empty((b.lib().binattn_backward_workspace(1, 2, 150, 64),), dtype=torch.uint8, device=DEV)
+    ws = torch.empty((b.lib().binattn_backward_workspace(1, 2, 150, 64, b.BIAS_DENSE),), dtype=torch.uint8, device=DEV)
     r1 = b.backward(q, k, v, o, do, bt, b.BIAS_DENSE, bias_grad=False, workspace=ws)
     r2 = b.backward(q, k, v, o, do, bt, b.BIAS_DENSE, bias_grad=True, workspace=ws)
     torch.cuda.synchronize()
