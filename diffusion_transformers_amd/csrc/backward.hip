@@ -127,31 +127,54 @@ __global__ __launch_bounds__(256) void bw_zero_kernel(float* p, int64_t n) {
 
 // ---------------------------------------------------------------------------------------------
 // fp32 operand arrays, 64 rows of one head per workgroup; rows >= N and channels >= d are zero.
+// The tile is gathered into LDS with reads that follow each source's layout (V^ channel-major,
+// dO row-major), then written out contiguously in each destination layout.
 template <int CP>
 __global__ __launch_bounds__(256) void bw_prep_kernel(BwArgs a) {
-    constexpr int KS = CP / 4;
+    constexpr int KS = CP / 4, TP = CP + 1;  // odd LDS row pitch: column walks are conflict-free
+    __shared__ float sv[kBC * TP], sd[kBC * TP];
+    __shared__ float ssc[CP], smk[kBC], smq[kBC];
+    __shared__ uint32_t skb[kBC * 4], sqb[kBC * 4];
     const int nb = a.Np / kBC;
     const int64_t bh = blockIdx.x / nb;
     const int j0 = (blockIdx.x % nb) * kBC;
-    const int N = a.N, d = a.d, W = a.W;
-    for (int e = threadIdx.x; e < kBC * CP; e += 256) {
+    const int N = a.N, d = a.d, W = a.W, tid = threadIdx.x;
+    for (int c = tid; c < CP; c += 256) ssc[c] = c < d ? a.vamax[bh * d + c] / 127.0f : 0.0f;
+    if (tid < kBC) {
+        const bool ok = j0 + tid < N;
+        smk[tid] = ok ? a.kmu[bh * N + j0 + tid] : 0.0f;
+        smq[tid] = ok ? a.qmu[bh * N + j0 + tid] : 0.0f;
+    }
+    for (int e = tid; e < kBC * W; e += 256) {
+        const int jl = e / W, w = e - jl * W;
+        const bool ok = j0 + jl < N;
+        skb[jl * 4 + w] = ok ? a.kbits[(bh * N + j0 + jl) * W + w] : 0u;
+        sqb[jl * 4 + w] = ok ? a.qbits[(bh * N + j0 + jl) * W + w] : 0u;
+    }
+    __syncthreads();
+    for (int e = tid; e < CP * kBC; e += 256) {  // V^ rows of channels: consecutive threads, consecutive tokens
+        const int c = e / kBC, jl = e - c * kBC, j = j0 + jl;
+        sv[jl * TP + c] = c < d && j < N ? ssc[c] * (float)a.vq[(bh * d + c) * a.ldv + j] : 0.0f;
+    }
+    for (int e = tid; e < kBC * CP; e += 256) {  // dO rows: consecutive threads, consecutive channels
         const int jl = e / CP, c = e - jl * CP, j = j0 + jl;
-        const bool ok = j < N && c < d;
-        const int64_t tok = bh * N + j;
-        float vv = 0.0f, tk = 0.0f, sq = 0.0f, go = 0.0f;
-        if (ok) {
-            vv = a.vamax[bh * d + c] / 127.0f * (float)a.vq[(bh * d + c) * a.ldv + j];
-            tk = a.kmu[tok] * (sign_bit(a.kbits, tok, W, c) ? 1.0f : -1.0f) * a.qk_scale;
-            sq = a.qmu[tok] * (sign_bit(a.qbits, tok, W, c) ? 1.0f : -1.0f) * a.qk_scale;
-            go = ld_any(a.dout, tok * d + c, a.g_f32);
-        }
-        const int64_t lin = (bh * a.Np + j) * CP + (c & 3) * KS + (c >> 2);
-        const int64_t grp = bh * (int64_t)a.Np * CP + (int64_t)(j >> 4) * 16 * CP + c * 16 + (j & 15);
-        a.vt[lin] = vv;
-        a.do1[lin] = go;
-        a.tt[grp] = tk;
-        a.st[grp] = sq;
-        a.do2[grp] = go;
+        sd[jl * TP + c] = c < d && j < N ? ld_any(a.dout, (bh * N + j) * d + c, a.g_f32) : 0.0f;
+    }
+    __syncthreads();
+    const int64_t lin0 = (bh * a.Np + j0) * CP;  // the tile's 64 CP floats in either layout
+    for (int o = tid; o < kBC * CP; o += 256) {  // [row][(c % 4) KS + c / 4]
+        const int jl = o / CP, pp = o - jl * CP, c = (pp % KS) * 4 + pp / KS;
+        a.vt[lin0 + o] = sv[jl * TP + c];
+        a.do1[lin0 + o] = sd[jl * TP + c];
+    }
+    for (int o = tid; o < kBC * CP; o += 256) {  // [row / 16][c][row % 16]
+        const int j16 = o & 15, c = (o >> 4) % CP, jl = (o / (16 * CP)) * 16 + j16;
+        const bool ok = c < d && j0 + jl < N;
+        const float sk = (skb[jl * 4 + (c >> 5)] >> (c & 31)) & 1u ? 1.0f : -1.0f;
+        const float sq = (sqb[jl * 4 + (c >> 5)] >> (c & 31)) & 1u ? 1.0f : -1.0f;
+        a.tt[lin0 + o] = ok ? smk[jl] * sk * a.qk_scale : 0.0f;
+        a.st[lin0 + o] = ok ? smq[jl] * sq * a.qk_scale : 0.0f;
+        a.do2[lin0 + o] = sd[jl * TP + c];
     }
 }
 
