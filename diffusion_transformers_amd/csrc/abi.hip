@@ -320,7 +320,7 @@ int binattn_attention(const void* q, const void* k, const void* v, int dtype, in
 
 int64_t binattn_backward_workspace(int B, int H, int N, int d, int bias_kind) {
     if (check_dims(B, H, N, d) || bias_kind < BINATTN_BIAS_NONE || bias_kind > BINATTN_BIAS_RELPOS) return -1;
-    return workspace_layout(B, H, N, d).total + backward_fp32_arrays_bytes(B, H, N, d, bias_kind);
+    return workspace_layout(B, H, N, d).total + backward_arrays_bytes(B, H, N, d, bias_kind);
 }
 
 int binattn_backward(const void* q, const void* k, const void* v, const void* o, const void* dout, int dtype,
@@ -333,7 +333,7 @@ int binattn_backward(const void* q, const void* k, const void* v, const void* o,
     if (!dtype_ok(dtype) || !dtype_ok(grad_dtype)) return BINATTN_EUNSUPPORTED;
     if (!(ste_clip >= 0.0f) || ste_clip > 3.0e38f) return BINATTN_EINVAL;  // NaN or infinite clip
     const WorkspaceLayout l = workspace_layout(B, H, N, d);
-    if (workspace_bytes < l.total + backward_fp32_arrays_bytes(B, H, N, d, bias_kind))
+    if (workspace_bytes < l.total + backward_arrays_bytes(B, H, N, d, bias_kind))
         return BINATTN_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
         !aligned16(dk) || !aligned16(dv) || (dbias && !aligned16(dbias)) ||

@@ -16,21 +16,34 @@
 //   (s = mu_q sign(q), t = mu_k sign(k)),   dq_ic = mu_q ds_ic ste(q_ic) + sgn(q_ic)/d sum_e ds_ie
 //   sign(q_ie) (likewise dk), dv = dV.
 //
-// gfx950 design (one workgroup = 4 waves x 16 rows; tiles of 64 keys or queries):
-//  * bw_prep_kernel writes, from the packed Q/K and int8 V of the forward's preparation, fp32
-//    operand arrays already in the lane order of v_mfma_f32_16x16x4_f32 (Vt, mu_k sign(k)/sqrt(d),
-//    mu_q sign(q)/sqrt(d), dO twice), so that tiles are staged in LDS by plain 16-byte copies and
-//    every operand read is one ds_read_b128 of four consecutive k steps.
-//  * bw_q_kernel (a workgroup per 64 queries): the exact row max and row sum over all key tiles
-//    (scores by the forward's fp4 QK tile), Delta, then per key tile: scores again, P, dP on the
-//    fp32 MFMA, dS, dQ accumulated on the fp32 MFMA, and the bias gradient (dense: fp32 atomics
-//    over the batch; relative position: an LDS window of the tile's table entries, flushed with
-//    atomics).  Writes m, l and Delta for the second kernel.
+// gfx950 design (one workgroup = 4 waves x 16 rows; tiles of 64 keys or queries).  The four
+// dense products run on the bf16 MFMA v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  bf16
+// keeps fp32's exponent range, so gradients of any scale enter without overflow or underflow;
+// every operand that is not exact in bf16 (V^ and P^ are integers below 256, the signs are +-1)
+// is split into two bf16 terms x = hi + lo (hi = bf16(x), lo = bf16(x - hi), about 16
+// significant bits) and multiplied as two MFMAs, so that the products keep near-fp32 accuracy:
+//   dP_ij = sum_c (dO_ic s_c) V^_jc                      (dO s split, V^ exact)
+//   dV_j  = sum_i (dO_i / (255 l_i)) P^_ij               (dO / (255 l) split, P^ exact)
+//   dQ_i  = sum_j (dS_ij mu_kj / sqrt(d)) sign(k_j)      (dS mu split, sign exact)
+//   dK_j  = sum_i (dS_ij mu_qi / sqrt(d)) sign(q_i)
+// (rows of dS sum to about zero, so rounding dS and mu k separately to 8 bits would cancel badly
+// for short rows; the split keeps that cancellation exact to ~2^-16).
+//  * bw_rows_kernel<STATS = true> (a workgroup per 64 queries): the exact row max and row sum
+//    over all key tiles (scores by the forward's fp4 QK tile) and Delta = dO . O.
+//  * bw_prep_kernel writes, from the packed Q/K and int8 V of the forward's preparation and the
+//    row sums, the bf16 operand arrays in the layouts the lanes read (rows of channels, or
+//    channels by 64-row tile), so that tiles are staged in LDS by 16-byte copies and every
+//    operand read is one ds_read_b128.
+//  * bw_rows_kernel<STATS = false> (a workgroup per 64 queries): per key tile the scores, P, dP,
+//    dS, dQ and the bias gradient (dense: each batch item's dS stored and summed over the batch
+//    afterwards; relative position: the table's entries accumulated in LDS).
 //  * bw_k_kernel (a workgroup per 64 keys): per query tile the transposed score tile (queries as
-//    MFMA rows, the lane's key as the column), P and P^, dP, dS, then dV and dK on the fp32 MFMA.
+//    MFMA rows, the lane's key as the column), P and P^, dP, dS, then dV and dK.
 #include "tile.h"
 
 namespace binattn {
+
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 
 struct BwArgs {
     const void* q;        // [B,H,N,d] input dtype
@@ -49,31 +62,32 @@ struct BwArgs {
     int64_t bias_ld;
     int bias_f32;
     int gh, gw;
-    int B, H, N, d, W, Np;  // Np: N rounded up to a multiple of 64
+    int B, H, N, d, W, Np;  // Np: N rounded up to a multiple of 64; channels padded to CP = 32 W
     float qk_scale;
     float clip;
-    float* vt;   // [BH][Np][CP], channel c at (c % 4) KS + c / 4 (KS = CP / 4)
-    float* tt;   // [BH][Np/16][CP][16]: mu_k sign(k_c) / sqrt(d)
-    float* st;   // [BH][Np/16][CP][16]: mu_q sign(q_c) / sqrt(d)
-    float* do1;  // [BH][Np][CP], the order of vt
-    float* do2;  // [BH][Np/16][CP][16]
-    float* m;    // [BH][N] row max, row sum, Delta
+    // bf16 operand arrays; "row" arrays are [BH][Np][CP], "tile" arrays [BH][Np/64][CP][64]
+    __bf16* vh;      // row: V^ (exact)
+    __bf16* dos_hi;  // row: dO_ic s_c, two terms
+    __bf16* dos_lo;
+    __bf16* sk;      // tile: sign(k_c) (+-1; 0 past N and d)
+    __bf16* sq;      // tile: sign(q_c)
+    __bf16* dot_hi;  // tile: dO_ic / (255 l_i), two terms
+    __bf16* dot_lo;
+    float* m;        // [BH][N] row max, row sum, Delta
     float* l;
     float* delta;
-    float* dq;   // [B,H,N,d] fp32
+    float* dq;       // [B,H,N,d] fp32
     float* dk;
     float* dv;
-    float* db;   // dense [H,N,N] or table [H,(2gh-1)(2gw-1)], fp32; may be null
-    float* dsb;  // dense bias gradient: dS of every batch item [B][H][N][Np], summed over B afterwards
-    float* dtp;  // table gradient of each query-block workgroup [B H nqb][kTabMax] when the table has
-                 // at most kTabMax entries (else null: the entries go to db by atomics per key tile)
+    float* db;       // dense [H,N,N] or table [H,(2gh-1)(2gw-1)], fp32; may be null
+    float* dsb;      // dense bias gradient: dS of every batch item [B][H][N][Np], summed over B afterwards
+    float* dtp;      // table gradient of each query-block workgroup [B H nqb][kTabMax] when the table has
+                     // at most kTabMax entries (else null: the entries go to db by atomics per key tile)
 };
 
 constexpr int kTabMax = 4096;  // table entries a workgroup accumulates whole in LDS
 
-__device__ __forceinline__ v4f mfma_f32x4(float a, float b, v4f c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
+__device__ __forceinline__ v4f mfma_b(bf8 a, bf8 b, v4f c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
 
 __device__ __forceinline__ float ld_any(const void* p, int64_t i, int f32) {
     return f32 ? static_cast<const float*>(p)[i] : (float)static_cast<const _Float16*>(p)[i];
@@ -90,6 +104,30 @@ __device__ __forceinline__ bool sign_bit(const uint32_t* bits, int64_t tok, int 
 // Row (query or key) slot of MFMA t's A operand row m: after the MFMA, lane (n, g) register r of
 // tile t holds row 16 g + 4 t + r (the forward's key_slot order).
 __device__ __forceinline__ int slot_row(int t, int m) { return 16 * (m >> 2) + 4 * t + (m & 3); }
+
+// x = hi + lo in bf16 (hi rounded to nearest, lo the rounded remainder).
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+    hi = (__bf16)x;
+    lo = (__bf16)(x - (float)hi);
+}
+
+// The 8 values x[8 s2 .. 8 s2 + 7] as bf16 MFMA operands (step s2 covers rows 16 g + 8 s2 + i).
+__device__ __forceinline__ bf8 pack_exact(const float (&x)[16], int s2) {
+    bf8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[8 * s2 + i];
+    return r;
+}
+
+__device__ __forceinline__ void pack_split(const float (&x)[16], int s2, bf8& hi, bf8& lo) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        __bf16 h, l;
+        split_bf16(x[8 * s2 + i], h, l);
+        hi[i] = h;
+        lo[i] = l;
+    }
+}
 
 // db[h][i][j] = sum over b of dS[b][h][i][j], in batch order (deterministic).
 __global__ __launch_bounds__(256) void bw_dbias_kernel(const float* __restrict__ dsb, float* __restrict__ db, int B,
@@ -126,62 +164,61 @@ __global__ __launch_bounds__(256) void bw_zero_kernel(float* p, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// fp32 operand arrays, 64 rows of one head per workgroup; rows >= N and channels >= d are zero.
+// bf16 operand arrays, 64 rows of one head per workgroup; rows >= N and channels >= d are zero.
 // The tile is gathered into LDS with reads that follow each source's layout (V^ channel-major,
-// dO row-major), then written out contiguously in each destination layout.
+// dO row-major), then written out contiguously in each destination layout.  Needs the row sums.
 template <int CP>
 __global__ __launch_bounds__(256) void bw_prep_kernel(BwArgs a) {
-    constexpr int KS = CP / 4, TP = CP + 1;  // odd LDS row pitch: column walks are conflict-free
+    constexpr int TP = CP + 1;  // odd LDS row pitch: column walks are conflict-free
     __shared__ float sv[kBC * TP], sd[kBC * TP];
-    __shared__ float ssc[CP], smk[kBC], smq[kBC];
+    __shared__ float ssc[CP], sil[kBC];
     __shared__ uint32_t skb[kBC * 4], sqb[kBC * 4];
     const int nb = a.Np / kBC;
     const int64_t bh = blockIdx.x / nb;
     const int j0 = (blockIdx.x % nb) * kBC;
     const int N = a.N, d = a.d, W = a.W, tid = threadIdx.x;
     for (int c = tid; c < CP; c += 256) ssc[c] = c < d ? a.vamax[bh * d + c] / 127.0f : 0.0f;
-    if (tid < kBC) {
-        const bool ok = j0 + tid < N;
-        smk[tid] = ok ? a.kmu[bh * N + j0 + tid] : 0.0f;
-        smq[tid] = ok ? a.qmu[bh * N + j0 + tid] : 0.0f;
-    }
+    if (tid < kBC) sil[tid] = j0 + tid < N ? 1.0f / (255.0f * a.l[bh * N + j0 + tid]) : 0.0f;
     for (int e = tid; e < kBC * W; e += 256) {
         const int jl = e / W, w = e - jl * W;
         const bool ok = j0 + jl < N;
         skb[jl * 4 + w] = ok ? a.kbits[(bh * N + j0 + jl) * W + w] : 0u;
         sqb[jl * 4 + w] = ok ? a.qbits[(bh * N + j0 + jl) * W + w] : 0u;
     }
-    __syncthreads();
     for (int e = tid; e < CP * kBC; e += 256) {  // V^ rows of channels: consecutive threads, consecutive tokens
         const int c = e / kBC, jl = e - c * kBC, j = j0 + jl;
-        sv[jl * TP + c] = c < d && j < N ? ssc[c] * (float)a.vq[(bh * d + c) * a.ldv + j] : 0.0f;
+        sv[jl * TP + c] = c < d && j < N ? (float)a.vq[(bh * d + c) * a.ldv + j] : 0.0f;
     }
     for (int e = tid; e < kBC * CP; e += 256) {  // dO rows: consecutive threads, consecutive channels
         const int jl = e / CP, c = e - jl * CP, j = j0 + jl;
         sd[jl * TP + c] = c < d && j < N ? ld_any(a.dout, (bh * N + j) * d + c, a.g_f32) : 0.0f;
     }
     __syncthreads();
-    const int64_t lin0 = (bh * a.Np + j0) * CP;  // the tile's 64 CP floats in either layout
-    for (int o = tid; o < kBC * CP; o += 256) {  // [row][(c % 4) KS + c / 4]
-        const int jl = o / CP, pp = o - jl * CP, c = (pp % KS) * 4 + pp / KS;
-        a.vt[lin0 + o] = sv[jl * TP + c];
-        a.do1[lin0 + o] = sd[jl * TP + c];
+    const int64_t t0 = (bh * a.Np + j0) * CP;  // the tile's 64 CP values in either layout
+    for (int o = tid; o < kBC * CP; o += 256) {  // [row][c]
+        const int jl = o / CP, c = o - jl * CP;
+        a.vh[t0 + o] = (__bf16)sv[jl * TP + c];
+        split_bf16(sd[jl * TP + c] * ssc[c], a.dos_hi[t0 + o], a.dos_lo[t0 + o]);
     }
-    for (int o = tid; o < kBC * CP; o += 256) {  // [row / 16][c][row % 16]
-        const int j16 = o & 15, c = (o >> 4) % CP, jl = (o / (16 * CP)) * 16 + j16;
+    for (int o = tid; o < kBC * CP; o += 256) {  // [c][row]
+        const int c = o / kBC, jl = o - c * kBC;
         const bool ok = c < d && j0 + jl < N;
-        const float sk = (skb[jl * 4 + (c >> 5)] >> (c & 31)) & 1u ? 1.0f : -1.0f;
-        const float sq = (sqb[jl * 4 + (c >> 5)] >> (c & 31)) & 1u ? 1.0f : -1.0f;
-        a.tt[lin0 + o] = ok ? smk[jl] * sk * a.qk_scale : 0.0f;
-        a.st[lin0 + o] = ok ? smq[jl] * sq * a.qk_scale : 0.0f;
-        a.do2[lin0 + o] = sd[jl * TP + c];
+        const bool bk = (skb[jl * 4 + (c >> 5)] >> (c & 31)) & 1u, bq = (sqb[jl * 4 + (c >> 5)] >> (c & 31)) & 1u;
+        a.sk[t0 + o] = (__bf16)(ok ? (bk ? 1.0f : -1.0f) : 0.0f);
+        a.sq[t0 + o] = (__bf16)(ok ? (bq ? 1.0f : -1.0f) : 0.0f);
+        split_bf16(sd[jl * TP + c] * sil[jl], a.dot_hi[t0 + o], a.dot_lo[t0 + o]);
     }
 }
 
-// 16-byte copy of n floats (a multiple of 4) from global to LDS by the workgroup.
-__device__ __forceinline__ void copy_to_lds(float* dst, const float* src, int n) {
-    for (int i = threadIdx.x; i < n / 4; i += 256)
-        reinterpret_cast<float4*>(dst)[i] = reinterpret_cast<const float4*>(src)[i];
+// Copy `rows` rows of `rowlen` bf16 values (a multiple of 8) from global to LDS rows of pitch
+// `pitch` values, in 16-byte pieces.
+template <typename T>
+__device__ __forceinline__ void copy_rows(T* dst, int pitch, const T* src, int rows, int rowlen) {
+    const int per = rowlen / 8;
+    for (int i = threadIdx.x; i < rows * per; i += 256) {
+        const int r = i / per, c = i - r * per;
+        *reinterpret_cast<uint4*>(dst + r * pitch + 8 * c) = *reinterpret_cast<const uint4*>(src + (int64_t)r * rowlen + 8 * c);
+    }
 }
 
 // Sign words of 64 rows starting at row r0 of a head as fp4 {0, 1} A-operand rows (the forward's
@@ -215,21 +252,24 @@ __device__ __forceinline__ int stage_window(float* win, const BwArgs& a, const v
 // ---------------------------------------------------------------------------------------------
 template <int NT, int BIAS>
 struct alignas(16) BwQLds {
-    static constexpr int W = (NT + 1) / 2, CP = 16 * NT;
+    static constexpr int W = (NT + 1) / 2, CP = 32 * W, RP = CP + 8, TPK = kBC + 8;
     uint32_t k[4 * W * 16 * 4];
     float mu[kBC];
-    float vt[kBC * CP];
-    float tt[kBC * CP];
+    __bf16 vh[kBC * RP];  // V^ of the tile's keys [key][channel]
+    __bf16 sk[CP * TPK];  // sign(k) [channel][key]
     float tw[BIAS == BK_RELPOS_G ? kRelposWin : 4];
     float dwin[BIAS == BK_RELPOS_G ? kTabMax : 4];  // the whole table's gradient, or one tile's window
     int kk[kBC];
 };
 
-template <int NT, int BIAS>
-__global__ __launch_bounds__(256) void bw_q_kernel(BwArgs a) {
-    constexpr int W = (NT + 1) / 2, CP = 16 * NT, KS = CP / 4;
+// A workgroup per 64 queries.  STATS: the row max, row sum and Delta of its queries.  Otherwise:
+// dS, the bias gradient and dq, from the row statistics and the prepared operand arrays.
+template <int NT, int BIAS, bool STATS>
+__global__ __launch_bounds__(256) void bw_rows_kernel(BwArgs a) {
+    typedef BwQLds<NT, BIAS> Lt;
+    constexpr int W = Lt::W, CP = Lt::CP, RP = Lt::RP, TPK = Lt::TPK, NCB = 2 * W;
     constexpr bool DENSE = BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32;
-    __shared__ BwQLds<NT, BIAS> L;
+    __shared__ Lt L;
     const int N = a.N, d = a.d;
     const int nqb = (N + kBR - 1) / kBR;
     const int lb = xcd_logical_block(blockIdx.x, a.B * a.H * nqb);
@@ -244,11 +284,6 @@ __global__ __launch_bounds__(256) void bw_q_kernel(BwArgs a) {
     const LaneQ lq = lane_query<NT>(fa, bh, qw0, g, n16);
     const int i = lq.qi;
     const int64_t tok = (int64_t)bh * N + i;
-
-    // dO of the lane's query, channels g + 4 s: the B operand of dP for every key tile
-    float doreg[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) doreg[s] = a.do1[((int64_t)bh * a.Np + i) * CP + g * KS + s];
 
     const int gw = a.gw, row_len = 2 * gw - 1;
     const int64_t tsz = (int64_t)(2 * a.gh - 1) * row_len;
@@ -270,8 +305,8 @@ __global__ __launch_bounds__(256) void bw_q_kernel(BwArgs a) {
     const int bvoff = (n16 * (int)a.bias_ld + 16 * g) * esz;
 
     // Stage key tile j0: fp4 K operand, mu_k, (relative position) window and key parts, and
-    // (with_mm) the fp32 Vt and t tiles.  Returns the window's table offset.
-    auto stage = [&](int j0, bool with_mm) {
+    // (not STATS) the V^ and sign(k) tiles.  Returns the window's table offset.
+    auto stage = [&](int j0) {
         stage_bits_f4<W>(L.k, a.kbits + (int64_t)bh * N * W, j0, N, d);
         if (tid < kBC) L.mu[tid] = j0 + tid < N ? a.kmu[(int64_t)bh * N + j0 + tid] : 0.0f;
         int woff = 0;
@@ -283,9 +318,10 @@ __global__ __launch_bounds__(256) void bw_q_kernel(BwArgs a) {
                 L.kk[tid] = -4 * (rj * row_len + j - rj * gw);
             }
         }
-        if (with_mm) {
-            copy_to_lds(L.vt, a.vt + ((int64_t)bh * a.Np + j0) * CP, kBC * CP);
-            copy_to_lds(L.tt, a.tt + ((int64_t)bh * a.Np + j0) * CP, kBC * CP);
+        if (!STATS) {
+            const int64_t t0 = ((int64_t)bh * a.Np + j0) * CP;
+            copy_rows(L.vh, RP, a.vh + t0, kBC, CP);
+            copy_rows(L.sk, TPK, a.sk + t0, CP, kBC);
         }
         return woff;
     };
@@ -302,62 +338,67 @@ __global__ __launch_bounds__(256) void bw_q_kernel(BwArgs a) {
         tile_scores<NT, BIAS>(L.k, L.mu, lq, br, wrun, true, N - jg, S, mloc, L.kk + 16 * g);
     };
 
-    // ---- pass 1: exact row max and row sum (online over the tiles), Delta
-    float mrun = -INFINITY, lpart = 0.0f;
-    for (int t = 0; t < ntiles; ++t) {
-        stage(t * kBC, false);
-        __syncthreads();
-        float S[16], mloc = -INFINITY;
-        scores(t * kBC, S, mloc);
-        const float mnew = fmaxf(mrun, rows4_max(mloc));
-        float sum = 0.0f;
+    if (STATS) {  // exact row max and row sum (online over the tiles), Delta
+        float mrun = -INFINITY, lpart = 0.0f;
+        for (int t = 0; t < ntiles; ++t) {
+            stage(t * kBC);
+            __syncthreads();
+            float S[16], mloc = -INFINITY;
+            scores(t * kBC, S, mloc);
+            const float mnew = fmaxf(mrun, rows4_max(mloc));
+            float sum = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) sum += fast_exp2((S[k] - mnew) * kLog2e);
-        lpart = lpart * fast_exp2((mrun - mnew) * kLog2e) + sum;
-        mrun = mnew;
-        __syncthreads();
+            for (int k = 0; k < 16; ++k) sum += fast_exp2((S[k] - mnew) * kLog2e);
+            lpart = lpart * fast_exp2((mrun - mnew) * kLog2e) + sum;
+            mrun = mnew;
+            __syncthreads();
+        }
+        const float lrow = rows4_sum(lpart);
+        float dpart = 0.0f;  // Delta = dO . O, the lane's share: channels g, g + 4, ...
+        for (int c = g; c < d; c += 4) dpart += ld_any(a.dout, tok * d + c, a.g_f32) * ld_any(a.o, tok * d + c, a.g_f32);
+        const float delta = rows4_sum(dpart);
+        if (lq.live && g == 0) {
+            a.m[tok] = mrun;
+            a.l[tok] = lrow;
+            a.delta[tok] = delta;
+        }
+        return;
     }
-    const float mrow = mrun, lrow = rows4_sum(lpart);
-    float dpart = 0.0f;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        const int c = g + 4 * s;
-        if (c < d) dpart += doreg[s] * ld_any(a.o, tok * d + c, a.g_f32);
-    }
-    const float delta = rows4_sum(dpart);
-    if (lq.live && g == 0) {
-        a.m[tok] = mrow;
-        a.l[tok] = lrow;
-        a.delta[tok] = delta;
-    }
-    const float inv_l = lq.live ? 1.0f / lrow : 0.0f;
 
-    // ---- pass 2: P, dP, dS, the bias gradient, dQ
+    const float mrow = a.m[tok], delta = a.delta[tok];
+    const float inv_l = lq.live ? 1.0f / a.l[tok] : 0.0f;
+    // dO s of the lane's query, channels 32 s + 8 g .. + 7, two terms: the B operand of dP
+    bf8 dhi[W], dlo[W];
+#pragma unroll
+    for (int s = 0; s < W; ++s) {
+        const int64_t o = ((int64_t)bh * a.Np + i) * CP + 32 * s + 8 * g;
+        dhi[s] = *reinterpret_cast<const bf8*>(a.dos_hi + o);
+        dlo[s] = *reinterpret_cast<const bf8*>(a.dos_lo + o);
+    }
+
     const bool whole = BIAS == BK_RELPOS_G && a.db && a.dtp;  // the table's gradient accumulates in LDS
     if (BIAS == BK_RELPOS_G && a.db)
         for (int e = tid; e < (whole ? kTabMax : kRelposWin); e += 256) L.dwin[e] = 0.0f;
-    v4f dqacc[NT];
+    v4f dqacc[NCB];
 #pragma unroll
-    for (int cb = 0; cb < NT; ++cb) dqacc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < NCB; ++cb) dqacc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
     for (int t = 0; t < ntiles; ++t) {
         const int j0 = t * kBC, jg = j0 + 16 * g;
-        const int woff = stage(j0, true);
+        const int woff = stage(j0);
         __syncthreads();
         float S[16], mloc = -INFINITY;
         scores(j0, S, mloc);
-        // dP: keys as MFMA rows (the score tile's order), channels as k
+        // dP: keys as MFMA rows (the score tile's order), 32 channels per step
         float dS[16];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-            const float* arow = &L.vt[slot_row(tt, n16) * CP + g * KS];
+            const __bf16* arow = &L.vh[slot_row(tt, n16) * RP + 8 * g];
 #pragma unroll
-            for (int s = 0; s < KS; s += 4) {
-                const float4 a4 = *reinterpret_cast<const float4*>(arow + s);
-                acc = mfma_f32x4(a4.x, doreg[s], acc);
-                acc = mfma_f32x4(a4.y, doreg[s + 1], acc);
-                acc = mfma_f32x4(a4.z, doreg[s + 2], acc);
-                acc = mfma_f32x4(a4.w, doreg[s + 3], acc);
+            for (int s = 0; s < W; ++s) {
+                const bf8 av = *reinterpret_cast<const bf8*>(arow + 32 * s);
+                acc = mfma_b(av, dhi[s], acc);
+                acc = mfma_b(av, dlo[s], acc);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -383,18 +424,21 @@ __global__ __launch_bounds__(256) void bw_q_kernel(BwArgs a) {
                     if (jg + k < N) atomicAdd(&L.dwin[base + L.kk[16 * g + k] / 4], dS[k]);
             }
         }
-        // dQ: channels as MFMA rows, keys as k (step r: keys 16 g + r of the lanes' groups)
+        // dQ: channels as MFMA rows, keys 16 g + 8 s2 + i as k; B = dS mu_k / sqrt(d) in two terms
+        float w[16];
 #pragma unroll
-        for (int cb = 0; cb < NT; ++cb) {
-            const float* arow = &L.tt[(g * CP + 16 * cb + n16) * 16];
+        for (int k = 0; k < 16; ++k) w[k] = dS[k] * (L.mu[16 * g + k] * a.qk_scale);
+        bf8 bh0, bl0, bh1, bl1;
+        pack_split(w, 0, bh0, bl0);
+        pack_split(w, 1, bh1, bl1);
 #pragma unroll
-            for (int r = 0; r < 16; r += 4) {
-                const float4 a4 = *reinterpret_cast<const float4*>(arow + r);
-                dqacc[cb] = mfma_f32x4(a4.x, dS[r], dqacc[cb]);
-                dqacc[cb] = mfma_f32x4(a4.y, dS[r + 1], dqacc[cb]);
-                dqacc[cb] = mfma_f32x4(a4.z, dS[r + 2], dqacc[cb]);
-                dqacc[cb] = mfma_f32x4(a4.w, dS[r + 3], dqacc[cb]);
-            }
+        for (int cb = 0; cb < NCB; ++cb) {
+            const __bf16* arow = &L.sk[(16 * cb + n16) * TPK + 16 * g];
+            const bf8 a0 = *reinterpret_cast<const bf8*>(arow), a1 = *reinterpret_cast<const bf8*>(arow + 8);
+            dqacc[cb] = mfma_b(a0, bh0, dqacc[cb]);
+            dqacc[cb] = mfma_b(a0, bl0, dqacc[cb]);
+            dqacc[cb] = mfma_b(a1, bh1, dqacc[cb]);
+            dqacc[cb] = mfma_b(a1, bl1, dqacc[cb]);
         }
         __syncthreads();
         if (BIAS == BK_RELPOS_G && a.db && !whole) {  // flush the tile's window entries
@@ -415,7 +459,7 @@ __global__ __launch_bounds__(256) void bw_q_kernel(BwArgs a) {
     // ---- dq = mu_q ds ste(q) + sgn(q)/d sum_e ds_e sign(q_e); the lane has channels 16 cb + 4 g + r
     float gpart = 0.0f;
 #pragma unroll
-    for (int cb = 0; cb < NT; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int c = 16 * cb + 4 * g + r;
@@ -425,7 +469,7 @@ __global__ __launch_bounds__(256) void bw_q_kernel(BwArgs a) {
     if (!lq.live) return;
     const float mu = a.qmu[tok];
 #pragma unroll
-    for (int cb = 0; cb < NT; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int c = 16 * cb + 4 * g + r;
@@ -439,12 +483,12 @@ __global__ __launch_bounds__(256) void bw_q_kernel(BwArgs a) {
 // ---------------------------------------------------------------------------------------------
 template <int NT, int BIAS>
 struct alignas(16) BwKLds {
-    static constexpr int W = (NT + 1) / 2, CP = 16 * NT;
+    static constexpr int W = (NT + 1) / 2, CP = 32 * W, RP = CP + 8, TPQ = kBR + 8;
     uint32_t q[4 * W * 16 * 4];
     float cq[kBR], mx[kBR], il[kBR], dl[kBR];
-    float do1[kBR * CP];
-    float do2[kBR * CP];
-    float st[kBR * CP];
+    __bf16 dos_hi[kBR * RP], dos_lo[kBR * RP];  // dO s of the tile's queries [query][channel]
+    __bf16 dot_hi[CP * TPQ], dot_lo[CP * TPQ];  // dO / (255 l) [channel][query]
+    __bf16 sq[CP * TPQ];                        // sign(q) [channel][query]
     float bt[BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32 ? kBR * kBC : 4];  // dense bias tile [query][key]
     float tw[BIAS == BK_RELPOS_G ? kRelposWin : 4];
     int qq[kBR];
@@ -452,9 +496,10 @@ struct alignas(16) BwKLds {
 
 template <int NT, int BIAS>
 __global__ __launch_bounds__(256) void bw_k_kernel(BwArgs a) {
-    constexpr int W = (NT + 1) / 2, CP = 16 * NT, KS = CP / 4;
+    typedef BwKLds<NT, BIAS> Lt;
+    constexpr int W = Lt::W, CP = Lt::CP, RP = Lt::RP, TPQ = Lt::TPQ, NCB = 2 * W;
     constexpr bool DENSE = BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32;
-    __shared__ BwKLds<NT, BIAS> L;
+    __shared__ Lt L;
     const int N = a.N, d = a.d;
     const int nkb = (N + kBC - 1) / kBC;
     const int lb = xcd_logical_block(blockIdx.x, a.B * a.H * nkb);
@@ -463,7 +508,7 @@ __global__ __launch_bounds__(256) void bw_k_kernel(BwArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nqt = (N + kBR - 1) / kBR;
 
-    // the lane's key: fp4 sign operand (+-2) of word g, seed -sum sign(k), mu_k, Vt channels g + 4 s
+    // the lane's key: fp4 sign operand (+-2) of word g, seed -sum sign(k), mu_k, V^ channels 32 s + 8 g
     const int jraw = k0 + wave * 16 + n16;
     const bool klive = jraw < N;
     const int j = klive ? jraw : N - 1;
@@ -472,9 +517,9 @@ __global__ __launch_bounds__(256) void bw_k_kernel(BwArgs a) {
     const float seed = load_q<W>(a.kbits + tok * W, klive, d, g, kop);
     const v4f dseed = v4f{seed, seed, seed, seed};
     const float muk = a.kmu[tok];
-    float vreg[KS];
+    bf8 vreg[W];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) vreg[s] = a.vt[((int64_t)bh * a.Np + j) * CP + g * KS + s];
+    for (int s = 0; s < W; ++s) vreg[s] = *reinterpret_cast<const bf8*>(a.vh + ((int64_t)bh * a.Np + j) * CP + 32 * s + 8 * g);
 
     const int gw = a.gw, row_len = 2 * gw - 1;
     const int64_t tsz = (int64_t)(2 * a.gh - 1) * row_len;
@@ -487,9 +532,9 @@ __global__ __launch_bounds__(256) void bw_k_kernel(BwArgs a) {
         kpart = (rjm - rj) * row_len + gw - 1 - cj;
     }
 
-    v4f dvacc[NT], dkacc[NT];
+    v4f dvacc[NCB], dkacc[NCB];
 #pragma unroll
-    for (int cb = 0; cb < NT; ++cb) dvacc[cb] = dkacc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < NCB; ++cb) dvacc[cb] = dkacc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
 
     for (int qt = 0; qt < nqt; ++qt) {
         const int i0 = qt * kBR;
@@ -500,7 +545,7 @@ __global__ __launch_bounds__(256) void bw_k_kernel(BwArgs a) {
             const bool ok = i < N;
             const int64_t qt_ = (int64_t)bh * N + (ok ? i : N - 1);
             L.cq[tid] = ok ? a.qmu[qt_] * a.qk_scale : 0.0f;
-            L.mx[tid] = ok ? a.m[qt_] : 0.0f;
+            L.mx[tid] = ok ? a.m[qt_] : INFINITY;  // P = 0 for queries >= N
             L.il[tid] = ok ? 1.0f / a.l[qt_] : 0.0f;
             L.dl[tid] = ok ? a.delta[qt_] : 0.0f;
             if (BIAS == BK_RELPOS_G) {
@@ -508,9 +553,12 @@ __global__ __launch_bounds__(256) void bw_k_kernel(BwArgs a) {
                 L.qq[tid] = (ri - i0 / gw) * row_len + ii - ri * gw;
             }
         }
-        copy_to_lds(L.do1, a.do1 + ((int64_t)bh * a.Np + i0) * CP, kBR * CP);
-        copy_to_lds(L.do2, a.do2 + ((int64_t)bh * a.Np + i0) * CP, kBR * CP);
-        copy_to_lds(L.st, a.st + ((int64_t)bh * a.Np + i0) * CP, kBR * CP);
+        const int64_t t0 = ((int64_t)bh * a.Np + i0) * CP;
+        copy_rows(L.dos_hi, RP, a.dos_hi + t0, kBR, CP);
+        copy_rows(L.dos_lo, RP, a.dos_lo + t0, kBR, CP);
+        copy_rows(L.dot_hi, TPQ, a.dot_hi + t0, CP, kBR);
+        copy_rows(L.dot_lo, TPQ, a.dot_lo + t0, CP, kBR);
+        copy_rows(L.sq, TPQ, a.sq + t0, CP, kBR);
         if (DENSE) {
             for (int e = tid; e < kBR * kBC; e += 256) {
                 const int r = e / kBC, c = e - r * kBC;
@@ -523,7 +571,7 @@ __global__ __launch_bounds__(256) void bw_k_kernel(BwArgs a) {
 
         // ---- scores: queries as MFMA rows (slot order), the lane's key as the column
         const int koff = ((g < W ? g : 0) * 16 + n16) * 4;
-        float S[16], P[16], Pq[16], dS[16];
+        float S[16], Pq[16], dS[16];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             const v4f D = mfma_f4(*reinterpret_cast<const v4i*>(&L.q[tt * W * 64 + koff]), kop, dseed);
@@ -540,43 +588,41 @@ __global__ __launch_bounds__(256) void bw_k_kernel(BwArgs a) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-            const float* arow = &L.do1[slot_row(tt, n16) * CP + g * KS];
+            const int ro = slot_row(tt, n16) * RP + 8 * g;
 #pragma unroll
-            for (int s = 0; s < KS; s += 4) {
-                const float4 a4 = *reinterpret_cast<const float4*>(arow + s);
-                acc = mfma_f32x4(a4.x, vreg[s], acc);
-                acc = mfma_f32x4(a4.y, vreg[s + 1], acc);
-                acc = mfma_f32x4(a4.z, vreg[s + 2], acc);
-                acc = mfma_f32x4(a4.w, vreg[s + 3], acc);
+            for (int s = 0; s < W; ++s) {
+                acc = mfma_b(*reinterpret_cast<const bf8*>(&L.dos_hi[ro + 32 * s]), vreg[s], acc);
+                acc = mfma_b(*reinterpret_cast<const bf8*>(&L.dos_lo[ro + 32 * s]), vreg[s], acc);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int kx = 4 * tt + r, il = 16 * g + kx;
                 const float p255 = fast_exp2(__builtin_fmaf(S[kx], kLog2e, kLog2_255 - L.mx[il] * kLog2e));
-                const float iv = L.il[il];  // 0 for queries >= N
-                P[kx] = p255 * (1.0f / 255.0f) * iv;
-                Pq[kx] = __builtin_rintf(p255) * (1.0f / 255.0f) * iv;
-                dS[kx] = P[kx] * (acc[r] - L.dl[il]);
+                Pq[kx] = __builtin_rintf(p255);  // P^; the 1 / (255 l) is in the dO operand
+                dS[kx] = p255 * (1.0f / 255.0f) * L.il[il] * (acc[r] - L.dl[il]);
             }
         }
-        // ---- dV (B = P^ / (255 l)) and dK (B = dS): channels as MFMA rows, queries 16 g + r as k
+        // ---- dV (A = dO / (255 l), B = P^) and dK (A = sign(q), B = dS mu_q / sqrt(d) in two terms):
+        // channels as MFMA rows, queries 16 g + 8 s2 + i as k
+        float w[16];
 #pragma unroll
-        for (int cb = 0; cb < NT; ++cb) {
-            const float* arow_o = &L.do2[(g * CP + 16 * cb + n16) * 16];
-            const float* arow_s = &L.st[(g * CP + 16 * cb + n16) * 16];
+        for (int k = 0; k < 16; ++k) w[k] = dS[k] * L.cq[16 * g + k];
+        const bf8 p0 = pack_exact(Pq, 0), p1 = pack_exact(Pq, 1);
+        bf8 wh0, wl0, wh1, wl1;
+        pack_split(w, 0, wh0, wl0);
+        pack_split(w, 1, wh1, wl1);
 #pragma unroll
-            for (int r = 0; r < 16; r += 4) {
-                const float4 o4 = *reinterpret_cast<const float4*>(arow_o + r);
-                const float4 s4 = *reinterpret_cast<const float4*>(arow_s + r);
-                dvacc[cb] = mfma_f32x4(o4.x, Pq[r], dvacc[cb]);
-                dvacc[cb] = mfma_f32x4(o4.y, Pq[r + 1], dvacc[cb]);
-                dvacc[cb] = mfma_f32x4(o4.z, Pq[r + 2], dvacc[cb]);
-                dvacc[cb] = mfma_f32x4(o4.w, Pq[r + 3], dvacc[cb]);
-                dkacc[cb] = mfma_f32x4(s4.x, dS[r], dkacc[cb]);
-                dkacc[cb] = mfma_f32x4(s4.y, dS[r + 1], dkacc[cb]);
-                dkacc[cb] = mfma_f32x4(s4.z, dS[r + 2], dkacc[cb]);
-                dkacc[cb] = mfma_f32x4(s4.w, dS[r + 3], dkacc[cb]);
-            }
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int ro = (16 * cb + n16) * TPQ + 16 * g;
+            dvacc[cb] = mfma_b(*reinterpret_cast<const bf8*>(&L.dot_hi[ro]), p0, dvacc[cb]);
+            dvacc[cb] = mfma_b(*reinterpret_cast<const bf8*>(&L.dot_lo[ro]), p0, dvacc[cb]);
+            dvacc[cb] = mfma_b(*reinterpret_cast<const bf8*>(&L.dot_hi[ro + 8]), p1, dvacc[cb]);
+            dvacc[cb] = mfma_b(*reinterpret_cast<const bf8*>(&L.dot_lo[ro + 8]), p1, dvacc[cb]);
+            const bf8 a0 = *reinterpret_cast<const bf8*>(&L.sq[ro]), a1 = *reinterpret_cast<const bf8*>(&L.sq[ro + 8]);
+            dkacc[cb] = mfma_b(a0, wh0, dkacc[cb]);
+            dkacc[cb] = mfma_b(a0, wl0, dkacc[cb]);
+            dkacc[cb] = mfma_b(a1, wh1, dkacc[cb]);
+            dkacc[cb] = mfma_b(a1, wl1, dkacc[cb]);
         }
         __syncthreads();
     }
@@ -584,7 +630,7 @@ __global__ __launch_bounds__(256) void bw_k_kernel(BwArgs a) {
     // ---- dk = mu_k dt ste(k) + sgn(k)/d sum_e dt_e sign(k_e), dv; channels 16 cb + 4 g + r
     float gpart = 0.0f;
 #pragma unroll
-    for (int cb = 0; cb < NT; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int c = 16 * cb + 4 * g + r;
@@ -593,7 +639,7 @@ __global__ __launch_bounds__(256) void bw_k_kernel(BwArgs a) {
     const float gsum = rows4_sum(gpart);
     if (!klive) return;
 #pragma unroll
-    for (int cb = 0; cb < NT; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int c = 16 * cb + 4 * g + r;
@@ -609,14 +655,16 @@ __global__ __launch_bounds__(256) void bw_k_kernel(BwArgs a) {
 template <int NT, int BK>
 static void launch_bw_bk(const BwArgs& a, hipStream_t s) {
     const unsigned nb = (unsigned)((int64_t)a.B * a.H * ((a.N + kBC - 1) / kBC));
-    hipLaunchKernelGGL((bw_q_kernel<NT, BK>), dim3(nb), dim3(256), 0, s, a);
+    const unsigned np = (unsigned)((int64_t)a.B * a.H * (a.Np / kBC));
+    hipLaunchKernelGGL((bw_rows_kernel<NT, BK, true>), dim3(nb), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bw_prep_kernel<16 * NT>), dim3(np), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bw_rows_kernel<NT, BK, false>), dim3(nb), dim3(256), 0, s, a);
     hipLaunchKernelGGL((bw_k_kernel<NT, BK>), dim3(nb), dim3(256), 0, s, a);
 }
 
+// One instantiation per 32-channel width: NT = 2 W (the kernels use W = ceil(NT / 2) only).
 template <int NT>
 static void launch_bw_nt(const BwArgs& a, int bk, hipStream_t s) {
-    const unsigned np = (unsigned)((int64_t)a.B * a.H * (a.Np / kBC));
-    hipLaunchKernelGGL((bw_prep_kernel<16 * NT>), dim3(np), dim3(256), 0, s, a);
     switch (bk) {
         case BK_NONE: launch_bw_bk<NT, BK_NONE>(a, s); break;
         case BK_DENSE_F16: launch_bw_bk<NT, BK_DENSE_F16>(a, s); break;
@@ -625,10 +673,10 @@ static void launch_bw_nt(const BwArgs& a, int bk, hipStream_t s) {
     }
 }
 
-int64_t backward_fp32_arrays_bytes(int B, int H, int N, int d, int bias_kind) {
-    const int64_t Np = ((int64_t)N + kBC - 1) / kBC * kBC, CP = 16 * ((d + 15) / 16), BH = (int64_t)B * H;
-    const int64_t extra = bias_kind == 1 ? BH * N * Np : (bias_kind == 2 ? BH * (Np / kBR) * kTabMax : 0);
-    return 5 * BH * Np * CP * 4 + 3 * BH * N * 4 + extra * 4 + 9 * 256;
+int64_t backward_arrays_bytes(int B, int H, int N, int d, int bias_kind) {
+    const int64_t Np = ((int64_t)N + kBC - 1) / kBC * kBC, CP = 32 * ((d + 31) / 32), BH = (int64_t)B * H;
+    const int64_t extra = bias_kind == 1 ? BH * N * Np * 4 : (bias_kind == 2 ? BH * (Np / kBR) * kTabMax * 4 : 0);
+    return 7 * BH * Np * CP * 2 + 3 * BH * N * 4 + extra + 11 * 256;
 }
 
 hipError_t launch_backward(const BwLaunch& L, hipStream_t s) {
@@ -640,36 +688,32 @@ hipError_t launch_backward(const BwLaunch& L, hipStream_t s) {
     a.B = L.B; a.H = L.H; a.N = L.N; a.d = L.d; a.W = (L.d + 31) / 32; a.Np = (int)(((int64_t)L.N + kBC - 1) / kBC * kBC);
     a.qk_scale = (float)(1.0 / sqrt((double)L.d));
     a.clip = L.clip;
-    // fp32 arrays in the scratch region, each 256-byte aligned
-    const int64_t BH = (int64_t)L.B * L.H, CP = 16 * ((L.d + 15) / 16);
-    auto up = [](int64_t x) { return (x + 63) / 64 * 64; };  // floats
-    float* p = L.scratch;
-    const int64_t arr = up(BH * a.Np * CP), vec = up(BH * L.N);
-    a.vt = p; p += arr;
-    a.tt = p; p += arr;
-    a.st = p; p += arr;
-    a.do1 = p; p += arr;
-    a.do2 = p; p += arr;
-    a.m = p; p += vec;
-    a.l = p; p += vec;
-    a.delta = p; p += vec;
-    a.dsb = L.bias_kind == 1 ? p : nullptr;
+    // arrays in the scratch region, each 256-byte aligned
+    const int64_t BH = (int64_t)L.B * L.H, CP = 32 * a.W;
+    auto up = [](int64_t bytes) { return (bytes + 255) / 256 * 256; };
+    char* p = reinterpret_cast<char*>(L.scratch);
+    const int64_t arr = up(BH * a.Np * CP * 2), vec = up(BH * L.N * 4);
+    __bf16** arrays[7] = {&a.vh, &a.dos_hi, &a.dos_lo, &a.sk, &a.sq, &a.dot_hi, &a.dot_lo};
+    for (__bf16** x : arrays) {
+        *x = reinterpret_cast<__bf16*>(p);
+        p += arr;
+    }
+    a.m = reinterpret_cast<float*>(p); p += vec;
+    a.l = reinterpret_cast<float*>(p); p += vec;
+    a.delta = reinterpret_cast<float*>(p); p += vec;
+    a.dsb = L.bias_kind == 1 ? reinterpret_cast<float*>(p) : nullptr;
     const int64_t tsz = (int64_t)(2 * L.gh - 1) * (2 * L.gw - 1);
-    a.dtp = L.bias_kind == 2 && tsz <= kTabMax ? p : nullptr;
+    a.dtp = L.bias_kind == 2 && tsz <= kTabMax ? reinterpret_cast<float*>(p) : nullptr;
     a.dq = L.dq; a.dk = L.dk; a.dv = L.dv; a.db = L.db;
     if (L.db && L.db_count > 0 && L.bias_kind == 2 && !a.dtp)  // table entries collect atomics
         hipLaunchKernelGGL(bw_zero_kernel, dim3((unsigned)((L.db_count + 255) / 256)), dim3(256), 0, s, L.db, L.db_count);
     int bk = BK_NONE;
     if (L.bias_kind == 1) bk = L.bias_f32 ? BK_DENSE_F32 : BK_DENSE_F16;
     if (L.bias_kind == 2) bk = BK_RELPOS_G;
-    switch ((L.d + 15) / 16) {
-        case 1: launch_bw_nt<1>(a, bk, s); break;
-        case 2: launch_bw_nt<2>(a, bk, s); break;
-        case 3: launch_bw_nt<3>(a, bk, s); break;
-        case 4: launch_bw_nt<4>(a, bk, s); break;
-        case 5: launch_bw_nt<5>(a, bk, s); break;
-        case 6: launch_bw_nt<6>(a, bk, s); break;
-        case 7: launch_bw_nt<7>(a, bk, s); break;
+    switch (a.W) {
+        case 1: launch_bw_nt<2>(a, bk, s); break;
+        case 2: launch_bw_nt<4>(a, bk, s); break;
+        case 3: launch_bw_nt<6>(a, bk, s); break;
         default: launch_bw_nt<8>(a, bk, s); break;
     }
     if (L.db && L.bias_kind == 1)

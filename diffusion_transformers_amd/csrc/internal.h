@@ -46,7 +46,7 @@ bool attention_fused_applies(const FwdArgs& a, int bias_kind);
 hipError_t launch_scores(const FwdArgs& a, hipStream_t s);
 
 // Backward of the quantisation-aware forward (backward.hip): packed inputs from launch_prepare,
-// fp32 scratch of backward_fp32_arrays_bytes(B, H, N, d, bias kind) bytes (256-byte aligned).
+// scratch of backward_arrays_bytes(B, H, N, d, bias kind) bytes (256-byte aligned).
 struct BwLaunch {
     const void* q;
     const void* k;
@@ -71,7 +71,7 @@ struct BwLaunch {
     float* db;
     int64_t db_count;
 };
-int64_t backward_fp32_arrays_bytes(int B, int H, int N, int d, int bias_kind);
+int64_t backward_arrays_bytes(int B, int H, int N, int d, int bias_kind);
 hipError_t launch_backward(const BwLaunch& L, hipStream_t s);
 hipError_t launch_qk_stats(const FwdArgs& a, int method, float* rowmax, float* rowsum, hipStream_t s);
 bool relpos_window_fits(int gw);
