@@ -328,6 +328,39 @@ def roofline(w, kbytes: float, ks: float):
     return roof
 
 
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def measure_backward(w, b, sets, calls: int):
+    """The QAT backward (binattn_backward) on the first input set: dO of the forward's output drawn
+    once, `calls` calls timed with HIP events after one warm call.  Its dense products (dP, dQ, dK,
+    dV: 8 B H N^2 d useful flops) run on the bf16 MFMA (rounded operands as two bf16 terms, so up
+    to twice the useful flops are issued), so they are set against its dense peak."""
+    import torch
+    s = sets[0]
+    o = s["o"]
+    dout = torch.randn(o.shape, dtype=o.dtype, device=o.device, generator=torch.Generator(o.device).manual_seed(7))
+    ws = torch.empty((b.lib().binattn_backward_workspace(w.B, w.H, w.N, w.d, s["kind"]),), dtype=torch.uint8,
+                     device=o.device)
+
+    def call():
+        return b.backward(s["q"], s["k"], s["v"], o, dout, s["bias"], s["kind"], s["grid"], workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(calls):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / calls
+    flops = 8.0 * w.B * w.H * w.N * w.N * w.d
+    return {"ms_per_call": ms, "calls": calls, "matmul_tflops": flops / (ms * 1e-3) / 1e12,
+            "frac_of_bf16_mfma_peak": flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "what": "dQ, dK, dV and the bias gradient from the forward's inputs, output and dO (straight-through "
+                    "sign, P and V quantisers), fp32 outputs"}
+
+
 def target_summary(w, m):
     """Per-workload record of a spec target shape: step and forward timings, effective
     TOPS and the roofline fractions recomputed from this run's own launch times."""
@@ -355,6 +388,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=8, help="at most this many input sets cycled through the steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the QAT backward timing of the target shapes")
     ap.add_argument("--qk-ab", action="store_true",
                     help="only time the binary QK tile by its two methods (fp4 MFMA, VALU XOR+popcount) and exit")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -403,9 +437,11 @@ def main():
     for name in [t for t in args.targets.split(",") if t and t != w.name]:
         tw = W.BY_NAME[name]
         tm = measure(tw, W, b, dev, args.steps, args.warmup, args.rotate)
+        bw = None if args.no_backward else measure_backward(tw, b, tm["sets"], max(1, min(args.steps, 20)))
         del tm["sets"]
         torch.cuda.empty_cache()
         targets[name] = target_summary(tw, tm)
+        targets[name]["backward"] = bw
 
     cpu = None
     if not args.no_cpu_baseline:

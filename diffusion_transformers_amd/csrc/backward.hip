@@ -144,18 +144,28 @@ __global__ __launch_bounds__(256) void bw_dbias_kernel(const float* __restrict__
 }
 
 // Table gradient: db[h][e] = sum of the partial tables of the query-block workgroups of head h
-// (stored at logical block (b H + h) nqb + query block), in batch and block order (deterministic).
+// (stored at logical block (b H + h) nqb + query block), in a fixed order (deterministic): a
+// workgroup takes 64 entries, its 4 waves sum every 4th partial (8 running sums each), and the
+// 4 wave sums are added in wave order.
 __global__ __launch_bounds__(256) void bw_dtable_kernel(const float* __restrict__ dtp, float* __restrict__ db, int B,
                                                         int H, int nqb, int tsz) {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= (int64_t)H * tsz) return;
-    const int h = (int)(e / tsz), t = (int)(e - (int64_t)h * tsz);
-    float acc = 0.0f;
-    for (int b = 0; b < B; ++b) {
-        const float* p = dtp + ((int64_t)(b * H + h) * nqb) * kTabMax + t;
-        for (int qb = 0; qb < nqb; ++qb) acc += p[(int64_t)qb * kTabMax];
+    __shared__ float part[4][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t e = (int64_t)blockIdx.x * 64 + lane;
+    const bool ok = e < (int64_t)H * tsz;
+    const int h = ok ? (int)(e / tsz) : 0, t = ok ? (int)(e - (int64_t)h * tsz) : 0;
+    const int np = B * nqb;  // partials of head h: (b H + h) nqb + qb for b < B, qb < nqb
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (ok) {
+        int n = wv, u = 0;
+        for (; n < np; n += 4, u = (u + 1) & 7) {
+            const int b = n / nqb, qb = n - b * nqb;
+            acc[u] += dtp[((int64_t)(b * H + h) * nqb + qb) * kTabMax + t];
+        }
     }
-    db[e] = acc;
+    part[wv][lane] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    __syncthreads();
+    if (wv == 0 && ok) db[e] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
 }
 
 __global__ __launch_bounds__(256) void bw_zero_kernel(float* p, int64_t n) {
@@ -195,18 +205,37 @@ __global__ __launch_bounds__(256) void bw_prep_kernel(BwArgs a) {
     }
     __syncthreads();
     const int64_t t0 = (bh * a.Np + j0) * CP;  // the tile's 64 CP values in either layout
-    for (int o = tid; o < kBC * CP; o += 256) {  // [row][c]
-        const int jl = o / CP, c = o - jl * CP;
-        a.vh[t0 + o] = (__bf16)sv[jl * TP + c];
-        split_bf16(sd[jl * TP + c] * ssc[c], a.dos_hi[t0 + o], a.dos_lo[t0 + o]);
+    auto put = [](__bf16* dst, const __bf16 (&x)[8]) { *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(x); };
+    for (int o8 = tid; o8 < kBC * CP / 8; o8 += 256) {  // [row][c], 8 channels per thread
+        const int jl = o8 / (CP / 8), c0 = 8 * (o8 - jl * (CP / 8));
+        alignas(16) __bf16 v[8], hi[8], lo[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            v[u] = (__bf16)sv[jl * TP + c0 + u];
+            split_bf16(sd[jl * TP + c0 + u] * ssc[c0 + u], hi[u], lo[u]);
+        }
+        const int64_t o = t0 + jl * CP + c0;
+        put(a.vh + o, v);
+        put(a.dos_hi + o, hi);
+        put(a.dos_lo + o, lo);
     }
-    for (int o = tid; o < kBC * CP; o += 256) {  // [c][row]
-        const int c = o / kBC, jl = o - c * kBC;
-        const bool ok = c < d && j0 + jl < N;
-        const bool bk = (skb[jl * 4 + (c >> 5)] >> (c & 31)) & 1u, bq = (sqb[jl * 4 + (c >> 5)] >> (c & 31)) & 1u;
-        a.sk[t0 + o] = (__bf16)(ok ? (bk ? 1.0f : -1.0f) : 0.0f);
-        a.sq[t0 + o] = (__bf16)(ok ? (bq ? 1.0f : -1.0f) : 0.0f);
-        split_bf16(sd[jl * TP + c] * sil[jl], a.dot_hi[t0 + o], a.dot_lo[t0 + o]);
+    for (int o8 = tid; o8 < kBC * CP / 8; o8 += 256) {  // [c][row], 8 rows per thread
+        const int c = o8 / (kBC / 8), r0 = 8 * (o8 - c * (kBC / 8));
+        alignas(16) __bf16 xk[8], xq[8], hi[8], lo[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int jl = r0 + u;
+            const bool ok = c < d && j0 + jl < N;
+            const bool bk = (skb[jl * 4 + (c >> 5)] >> (c & 31)) & 1u, bq = (sqb[jl * 4 + (c >> 5)] >> (c & 31)) & 1u;
+            xk[u] = (__bf16)(ok ? (bk ? 1.0f : -1.0f) : 0.0f);
+            xq[u] = (__bf16)(ok ? (bq ? 1.0f : -1.0f) : 0.0f);
+            split_bf16(sd[jl * TP + c] * sil[jl], hi[u], lo[u]);
+        }
+        const int64_t o = t0 + c * kBC + r0;
+        put(a.sk + o, xk);
+        put(a.sq + o, xq);
+        put(a.dot_hi + o, hi);
+        put(a.dot_lo + o, lo);
     }
 }
 
@@ -453,7 +482,7 @@ __global__ __launch_bounds__(256) void bw_rows_kernel(BwArgs a) {
     }
     if (whole) {  // this workgroup's share of the table gradient, summed over workgroups afterwards
         float* dst = a.dtp + (int64_t)lb * kTabMax;  // logical block: (b H + h) nqb + query block
-        for (int e = tid; e < kTabMax; e += 256) dst[e] = L.dwin[e];
+        for (int e = tid; e < (int)tsz; e += 256) dst[e] = L.dwin[e];
     }
 
     // ---- dq = mu_q ds ste(q) + sgn(q)/d sum_e ds_e sign(q_e); the lane has channels 16 cb + 4 g + r
@@ -720,7 +749,7 @@ hipError_t launch_backward(const BwLaunch& L, hipStream_t s) {
         hipLaunchKernelGGL(bw_dbias_kernel, dim3((unsigned)((L.db_count + 255) / 256)), dim3(256), 0, s, a.dsb, L.db,
                            L.B, L.H, L.N, a.Np);
     if (L.db && a.dtp)
-        hipLaunchKernelGGL(bw_dtable_kernel, dim3((unsigned)((L.db_count + 255) / 256)), dim3(256), 0, s, a.dtp, L.db,
+        hipLaunchKernelGGL(bw_dtable_kernel, dim3((unsigned)((L.db_count + 63) / 64)), dim3(256), 0, s, a.dtp, L.db,
                            L.B, L.H, a.Np / kBR, (int)tsz);
     return hipGetLastError();
 }

@@ -54,6 +54,8 @@ def test_bench_prints_one_json_line():
     t = res["targets"]["dit_xl2_256"]
     assert (t["B"], t["H"], t["N"], t["d"]) == (64, 16, 256, 72)
     assert t["ms_per_step"] > 0 and t["fwd_ms_per_call"] > 0 and 0 < t["fwd_hbm_frac"] < 1
+    bw = t["backward"]
+    assert bw["ms_per_call"] > 0 and 0 < bw["frac_of_bf16_mfma_peak"] < 1
     cpu = res["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
 
