@@ -94,10 +94,11 @@ def step_bytes(w) -> float:
 
 
 def sources_sha() -> str:
-    """sha256 (first 16 hex digits) over the kernel sources, in name order."""
+    """sha256 (first 16 hex digits) over the sources the forward-path kernels are built from
+    (every .hip and .h of csrc but the backward's), in name order."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
+        if name.endswith((".hip", ".h")) and name != "backward.hip":
             h.update(name.encode())
             h.update(open(os.path.join(CSRC, name), "rb").read())
     return h.hexdigest()[:16]

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 4 && 
     if (is_relpos(BIAS)) {
         ri_min = q0 / gw;
         const int ri = lq.qi / gw, ci = lq.qi - ri * gw;
-        aq = (ri - ri_min) * row_len + ci + gw - 1;
+        aq = 4 * ((ri - ri_min) * row_len + ci + gw - 1);  // (in bytes: one form of it stays live)
         lrow = (kBC - 1) / gw;
         lcol = kBC - 1 - lrow * gw;
         rjm_ld = min(lrow, a.gh - 1);
@@ -139,16 +139,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 4 && 
         }
         // (a wave wholly past N computes on clamped inputs and stores nothing: no per-tile test)
         const int jg = tile * kBC + 16 * g;
-        int idx0 = 15;
+        const char* twb = reinterpret_cast<const char*>(s.tw);
+        const float* wrun = s.tw;  // window entry of the run's key jg (+15 entries: its last key)
         if (BIAS == BK_RELPOS) {
-            idx0 = aq + rjm * row_len - kk;
-            if (TAIL && jg >= N) idx0 = 15;  // a run wholly past N is masked; its reads stay in the window
-            kcol += dcol;                    // this lane's keys in the next tile
+            int off = aq + 4 * (rjm * row_len - kk - 15);
+            if (TAIL && jg >= N) off = 0;  // a run wholly past N is masked; its reads stay in the window
+            wrun = reinterpret_cast<const float*>(twb + off);
+            kcol += dcol;  // this lane's keys in the next tile
             kk += drow * row_len + dcol;
             if (kcol >= gw) kcol -= gw, kk += row_len - gw;
         }
-        const float* wrun = s.tw + idx0 - 15;
-        if (BIAS == BK_RELPOS_G) wrun = s.tw + aq + rjm * row_len;  // the keys' parts are gathered from s.kk
+        if (BIAS == BK_RELPOS_G)  // the keys' parts are gathered from s.kk
+            wrun = reinterpret_cast<const float*>(twb + aq + 4 * rjm * row_len);
         float S[16], mloc = -INFINITY;
         tile_scores<NT, BIAS>(s.k, s.mu, lq, bcur, wrun, TAIL, N - jg, S, mloc, s.kk + 16 * g);
         const float mnew = fmaxf(mrun, rows4_max(mloc));
