@@ -34,11 +34,15 @@
 //    row sums, the bf16 operand arrays in the layouts the lanes read (rows of channels, or
 //    channels by 64-row tile), so that tiles are staged in LDS by 16-byte copies and every
 //    operand read is one ds_read_b128.
+//  * Every staging step issues all of a tile's global loads before its first LDS store (a loop of
+//    load, wait, store pays one memory latency per iteration, and the kernels are bound by them).
 //  * bw_rows_kernel<STATS = false> (a workgroup per 64 queries): per key tile the scores, P, dP,
 //    dS, dQ and the bias gradient (dense: each batch item's dS stored and summed over the batch
 //    afterwards; relative position: the table's entries accumulated in LDS).
 //  * bw_k_kernel (a workgroup per 64 keys): per query tile the transposed score tile (queries as
 //    MFMA rows, the lane's key as the column), P and P^, dP, dS, then dV and dK.
+#include <utility>
+
 #include "tile.h"
 
 namespace binattn {
@@ -173,36 +177,88 @@ __global__ __launch_bounds__(256) void bw_zero_kernel(float* p, int64_t n) {
     if (i < n) p[i] = 0.0f;
 }
 
+// Calls f(std::integral_constant<int, K>) for K = 0 .. N-1, so that register arrays are indexed
+// by constants from the start (an array indexed in a loop can be left in scratch memory).
+template <typename F, int... K>
+__device__ __forceinline__ void for_each_k(F&& f, std::integer_sequence<int, K...>) {
+    (f(std::integral_constant<int, K>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    for_each_k(f, std::make_integer_sequence<int, N>{});
+}
+
 // ---------------------------------------------------------------------------------------------
-// bf16 operand arrays, 64 rows of one head per workgroup; rows >= N and channels >= d are zero.
-// The tile is gathered into LDS with reads that follow each source's layout (V^ channel-major,
-// dO row-major), then written out contiguously in each destination layout.  Needs the row sums.
-template <int CP>
+// bf16 operand arrays, 64 rows of one head per workgroup; rows >= N and channels >= d are zero
+// (needs the row sums).  Every load of the tile (dO rows, V^ channel rows, sign words) is issued
+// before the first LDS store; the tile is gathered into LDS along each source's layout, then
+// written out in 16-byte stores in each destination layout.
+template <int CP, bool G32>
 __global__ __launch_bounds__(256) void bw_prep_kernel(BwArgs a) {
     constexpr int TP = CP + 1;  // odd LDS row pitch: column walks are conflict-free
+    constexpr int W = CP / 32, DIT = 8 * CP / 256, VIT = (4 * CP + 255) / 256;
     __shared__ float sv[kBC * TP], sd[kBC * TP];
     __shared__ float ssc[CP], sil[kBC];
     __shared__ uint32_t skb[kBC * 4], sqb[kBC * 4];
     const int nb = a.Np / kBC;
     const int64_t bh = blockIdx.x / nb;
     const int j0 = (blockIdx.x % nb) * kBC;
-    const int N = a.N, d = a.d, W = a.W, tid = threadIdx.x;
-    for (int c = tid; c < CP; c += 256) ssc[c] = c < d ? a.vamax[bh * d + c] / 127.0f : 0.0f;
-    if (tid < kBC) sil[tid] = j0 + tid < N ? 1.0f / (255.0f * a.l[bh * N + j0 + tid]) : 0.0f;
-    for (int e = tid; e < kBC * W; e += 256) {
-        const int jl = e / W, w = e - jl * W;
-        const bool ok = j0 + jl < N;
-        skb[jl * 4 + w] = ok ? a.kbits[(bh * N + j0 + jl) * W + w] : 0u;
-        sqb[jl * 4 + w] = ok ? a.qbits[(bh * N + j0 + jl) * W + w] : 0u;
+    const int N = a.N, d = a.d, tid = threadIdx.x;
+    // ---- loads: dO chunks (row tid % 64, channels 8 (i / 64) ..+7), V^ chunks (channel t % CP,
+    // tokens 16 (t / CP) ..+15), sign words, scales, row sums
+    uint4 dv[DIT], dv2[G32 ? DIT : 1], vv[VIT];
+    static_for<DIT>([&](auto k) {
+        const int i = tid + 256 * k, r = i & 63, c0 = 8 * (i >> 6), j = j0 + r;
+        dv[k] = make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (G32) dv2[k] = make_uint4(0u, 0u, 0u, 0u);
+        if (j < N && c0 < d) {
+            const int64_t e = (bh * N + j) * d + c0;
+            if constexpr (G32) {
+                dv[k] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.dout) + e);
+                dv2[k] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.dout) + e + 4);
+            } else {
+                dv[k] = *reinterpret_cast<const uint4*>(static_cast<const _Float16*>(a.dout) + e);
+            }
+        }
+    });
+    static_for<VIT>([&](auto k) {
+        const int t = tid + 256 * k, c = t % CP, q = t / CP;
+        vv[k] = make_uint4(0u, 0u, 0u, 0u);  // (V^ past N is zero in its padded rows)
+        if (t < 4 * CP && c < d) vv[k] = *reinterpret_cast<const uint4*>(a.vq + (bh * d + c) * a.ldv + j0 + 16 * q);
+    });
+    const int bw = tid >> 6, br = tid & 63;
+    const bool bok = tid < kBC * W && j0 + br < N;
+    const uint32_t kword = bok ? a.kbits[(bh * N + j0 + br) * W + bw] : 0u;
+    const uint32_t qword = bok ? a.qbits[(bh * N + j0 + br) * W + bw] : 0u;
+    const float sc = tid < CP && tid < d ? a.vamax[bh * d + tid] / 127.0f : 0.0f;
+    const float lrow = tid < kBC && j0 + tid < N ? a.l[bh * N + j0 + tid] : 0.0f;
+    // ---- LDS
+    if (tid < CP) ssc[tid] = sc;
+    if (tid < kBC) sil[tid] = j0 + tid < N ? 1.0f / (255.0f * lrow) : 0.0f;
+    if (tid < kBC * W) {
+        skb[br * 4 + bw] = kword;
+        sqb[br * 4 + bw] = qword;
     }
-    for (int e = tid; e < CP * kBC; e += 256) {  // V^ rows of channels: consecutive threads, consecutive tokens
-        const int c = e / kBC, jl = e - c * kBC, j = j0 + jl;
-        sv[jl * TP + c] = c < d && j < N ? (float)a.vq[(bh * d + c) * a.ldv + j] : 0.0f;
-    }
-    for (int e = tid; e < kBC * CP; e += 256) {  // dO rows: consecutive threads, consecutive channels
-        const int jl = e / CP, c = e - jl * CP, j = j0 + jl;
-        sd[jl * TP + c] = c < d && j < N ? ld_any(a.dout, (bh * N + j) * d + c, a.g_f32) : 0.0f;
-    }
+    static_for<DIT>([&](auto k) {
+        const int i = tid + 256 * k, r = i & 63, c0 = 8 * (i >> 6);
+        if constexpr (G32) {
+            const uint32_t w8[8] = {dv[k].x, dv[k].y, dv[k].z, dv[k].w, dv2[k].x, dv2[k].y, dv2[k].z, dv2[k].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sd[r * TP + c0 + e] = __uint_as_float(w8[e]);
+        } else {
+            const h8 hv = __builtin_bit_cast(h8, dv[k]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sd[r * TP + c0 + e] = (float)hv[e];
+        }
+    });
+    static_for<VIT>([&](auto k) {
+        const int t = tid + 256 * k, c = t % CP, q = t / CP;
+        if (t < 4 * CP) {
+            const uint32_t w4[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sv[(16 * q + e) * TP + c] = (float)(int)(int8_t)(w4[e >> 2] >> (8 * (e & 3)));
+        }
+    });
     __syncthreads();
     const int64_t t0 = (bh * a.Np + j0) * CP;  // the tile's 64 CP values in either layout
     auto put = [](__bf16* dst, const __bf16 (&x)[8]) { *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(x); };
@@ -239,44 +295,123 @@ __global__ __launch_bounds__(256) void bw_prep_kernel(BwArgs a) {
     }
 }
 
-// Copy `rows` rows of `rowlen` bf16 values (a multiple of 8) from global to LDS rows of pitch
-// `pitch` values, in 16-byte pieces.
-template <typename T>
-__device__ __forceinline__ void copy_rows(T* dst, int pitch, const T* src, int rows, int rowlen) {
-    const int per = rowlen / 8;
-    for (int i = threadIdx.x; i < rows * per; i += 256) {
-        const int r = i / per, c = i - r * per;
-        *reinterpret_cast<uint4*>(dst + r * pitch + 8 * c) = *reinterpret_cast<const uint4*>(src + (int64_t)r * rowlen + 8 * c);
-    }
-}
+// Staging in two phases, every global load of a tile issued before the first LDS store (a loop
+// of load, wait, store would pay one memory latency per iteration): load() into registers,
+// store() into LDS.
 
-// Sign words of 64 rows starting at row r0 of a head as fp4 {0, 1} A-operand rows (the forward's
-// K staging), rows >= N zero.
-template <int W>
-__device__ __forceinline__ void stage_bits_f4(uint32_t* dst, const uint32_t* bits, int r0, int N, int d) {
-    for (int id = threadIdx.x; id < kBC * W; id += 256) {
-        const int r = id / W, w = id - r * W;
-        uint32_t word = r0 + r < N ? bits[(int64_t)(r0 + r) * W + w] : 0u;
-        const int left = d - 32 * w;
-        if (left < 32) word &= (1u << left) - 1u;
-        uint32_t o[4];
-        unpack_bits32_f4(word, o);
-        const int t = (r & 15) >> 2, m = 4 * (r >> 4) + (r & 3);
-        *reinterpret_cast<uint4*>(&dst[((t * W + w) * 16 + m) * 4]) = make_uint4(o[0], o[1], o[2], o[3]);
+// ROWS rows of RL bf16 values (8 ROWS RL / 8 is a multiple of 256): thread tid holds the 16-byte
+// chunks tid + 256 k of the row-major tile.
+template <int ROWS, int RL>
+struct BfTile {
+    static constexpr int PER = RL / 8, TOT = ROWS * PER, IT = TOT / 256;
+    static_assert(TOT % 256 == 0, "whole chunks per thread");
+    uint4 v[IT];
+    __device__ __forceinline__ void load(const __bf16* src) {
+        static_for<IT>([&](auto k) {
+            v[k] = *reinterpret_cast<const uint4*>(src + 8 * (threadIdx.x + 256 * k));
+        });
     }
-}
+    template <int PITCH>
+    __device__ __forceinline__ void store(__bf16* dst) const {
+        static_for<IT>([&](auto k) {
+            const int i = threadIdx.x + 256 * k, r = i / PER, c = i - r * PER;
+            *reinterpret_cast<uint4*>(dst + r * PITCH + 8 * c) = v[k];
+        });
+    }
+};
+
+// Sign words of 64 rows starting at row r0 of a head, one word per thread (thread tid < 64 W: row
+// tid % 64, word tid / 64), rows >= N zero, stored as the fp4 {0, 1} A-operand rows of the QK
+// tile (the forward's K staging).
+template <int W>
+struct SignTile {
+    uint32_t word;
+    __device__ __forceinline__ void load(const uint32_t* bits, int r0, int N) {
+        const int id = threadIdx.x, w = id >> 6, r = id & 63;
+        word = id < kBC * W && r0 + r < N ? bits[(int64_t)(r0 + r) * W + w] : 0u;
+    }
+    __device__ __forceinline__ void store_fp4(uint32_t* dst, int d) const {
+        const int id = threadIdx.x, w = id >> 6, r = id & 63;
+        if (id < kBC * W) {
+            uint32_t x = word;
+            const int left = d - 32 * w;
+            if (left < 32) x &= (1u << left) - 1u;
+            uint32_t o[4];
+            unpack_bits32_f4(x, o);
+            const int t = (r & 15) >> 2, m = 4 * (r >> 4) + (r & 3);
+            *reinterpret_cast<uint4*>(&dst[((t * W + w) * 16 + m) * 4]) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+};
 
 // Relative position on any grid: the table rows that queries [q0, q0 + 64) and keys [j0, j0 + 64)
 // touch, from row ri_min - rjm + gh - 1 (rjm: grid row of the tile's last key), at row stride
-// 2 gw - 1; returns that start's element offset in the head's table.
-__device__ __forceinline__ int stage_window(float* win, const BwArgs& a, const void* table, int q0, int j0) {
-    const int gw = a.gw, row_len = 2 * gw - 1, tsz = (2 * a.gh - 1) * row_len;
-    const int ri_min = q0 / gw, rjm = min((j0 + kBC - 1) / gw, a.gh - 1);
-    const int off = (ri_min - rjm + a.gh - 1) * row_len;
-    for (int e = threadIdx.x; e < kRelposWin; e += 256)
-        win[e] = off + e < tsz ? ld_any(table, off + e, a.bias_f32) : 0.0f;
-    return off;
-}
+// 2 gw - 1 (entries past the table read 0, through the buffer's range); off: that start's element
+// offset in the head's table.
+struct WinTile {
+    uint32_t v[kRelposWin / 256];  // raw table bits (fp32, or fp16 in the low half), converted when stored
+    int off, f32;
+    __device__ __forceinline__ void load(const BwArgs& a, const void* table, int q0, int j0) {
+        const int gw = a.gw, row_len = 2 * gw - 1, tsz = (2 * a.gh - 1) * row_len;
+        const int ri_min = q0 / gw, rjm = min((j0 + kBC - 1) / gw, a.gh - 1);
+        off = (ri_min - rjm + a.gh - 1) * row_len;
+        f32 = a.bias_f32;
+        const int esz = f32 ? 4 : 2;
+        const __amdgpu_buffer_rsrc_t tr = buffer_rsrc((const char*)table + (int64_t)off * esz, (tsz - off) * esz);
+#pragma unroll
+        for (int i = 0; i < kRelposWin / 256; ++i) {
+            const int o = (threadIdx.x + 256 * i) * esz;
+            v[i] = f32 ? __builtin_amdgcn_raw_buffer_load_b32(tr, o, 0, 0) : __builtin_amdgcn_raw_buffer_load_b16(tr, o, 0, 0);
+        }
+    }
+    __device__ __forceinline__ void store(float* win) const {
+#pragma unroll
+        for (int i = 0; i < kRelposWin / 256; ++i)
+            win[threadIdx.x + 256 * i] = f32 ? __uint_as_float(v[i]) : (float)__builtin_bit_cast(_Float16, (uint16_t)v[i]);
+    }
+};
+
+// Dense bias of queries [i0, i0 + 64) and keys [k0, k0 + 64) of head h as fp32 [query][key]
+// (entries past N zero): 16-byte loads along the rows (row starts are 16-byte aligned), 2 per
+// thread for fp16 and 4 for fp32.
+template <bool F32>
+struct DenseTile {
+    static constexpr int EPC = F32 ? 4 : 8, CPR = kBC / EPC, IT = kBR * CPR / 256;  // elements per chunk, chunks per row
+    uint4 v[IT];
+    __device__ __forceinline__ void load(const BwArgs& a, int h, int i0, int k0) {
+        const int N = a.N;
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int i = threadIdx.x + 256 * k, r = i / CPR, c = i - r * CPR;
+            v[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (i0 + r < N && k0 + EPC * c < N)  // the chunk then lies within the row's bias_ld entries
+                v[k] = *reinterpret_cast<const uint4*>((const char*)a.bias +
+                                                        (((int64_t)h * N + i0 + r) * a.bias_ld + k0 + EPC * c) * (F32 ? 4 : 2));
+        }
+    }
+    __device__ __forceinline__ void store(float* dst, int k0, int N) const {
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int i = threadIdx.x + 256 * k, r = i / CPR, c = i - r * CPR;
+            float f[EPC];
+            if constexpr (F32) {
+                f[0] = __uint_as_float(v[k].x); f[1] = __uint_as_float(v[k].y);
+                f[2] = __uint_as_float(v[k].z); f[3] = __uint_as_float(v[k].w);
+            } else {
+                const h8 x = __builtin_bit_cast(h8, v[k]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = (float)x[e];
+            }
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+                if (k0 + EPC * c + e >= N) f[e] = 0.0f;  // padding columns past N
+            }
+#pragma unroll
+            for (int e = 0; e < EPC; e += 4)
+                *reinterpret_cast<float4*>(&dst[r * kBC + EPC * c + e]) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
+        }
+    }
+};
 
 // ---------------------------------------------------------------------------------------------
 template <int NT, int BIAS>
@@ -293,8 +428,10 @@ struct alignas(16) BwQLds {
 
 // A workgroup per 64 queries.  STATS: the row max, row sum and Delta of its queries.  Otherwise:
 // dS, the bias gradient and dq, from the row statistics and the prepared operand arrays.
+// (LDS allows at most 3 workgroups per CU: registers up to that occupancy hold a tile's staged
+// loads without spilling.)
 template <int NT, int BIAS, bool STATS>
-__global__ __launch_bounds__(256) void bw_rows_kernel(BwArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) void bw_rows_kernel(BwArgs a) {
     typedef BwQLds<NT, BIAS> Lt;
     constexpr int W = Lt::W, CP = Lt::CP, RP = Lt::RP, TPK = Lt::TPK, NCB = 2 * W;
     constexpr bool DENSE = BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32;
@@ -336,11 +473,25 @@ __global__ __launch_bounds__(256) void bw_rows_kernel(BwArgs a) {
     // Stage key tile j0: fp4 K operand, mu_k, (relative position) window and key parts, and
     // (not STATS) the V^ and sign(k) tiles.  Returns the window's table offset.
     auto stage = [&](int j0) {
-        stage_bits_f4<W>(L.k, a.kbits + (int64_t)bh * N * W, j0, N, d);
-        if (tid < kBC) L.mu[tid] = j0 + tid < N ? a.kmu[(int64_t)bh * N + j0 + tid] : 0.0f;
+        SignTile<W> kst;
+        kst.load(a.kbits + (int64_t)bh * N * W, j0, N);
+        const float mu = tid < kBC && j0 + tid < N ? a.kmu[(int64_t)bh * N + j0 + tid] : 0.0f;
+        WinTile win;
+        if (BIAS == BK_RELPOS_G) win.load(a, table, q0, j0);
+        BfTile<kBC, CP> tvh;
+        BfTile<CP, kBC> tsk;
+        const int64_t t0 = ((int64_t)bh * a.Np + j0) * CP;
+        if (!STATS) {
+            tvh.load(a.vh + t0);
+            tsk.load(a.sk + t0);
+        }
+        // (every load above is issued before the stores below)
+        kst.store_fp4(L.k, d);
+        if (tid < kBC) L.mu[tid] = mu;
         int woff = 0;
         if (BIAS == BK_RELPOS_G) {
-            woff = stage_window(L.tw, a, table, q0, j0);
+            win.store(L.tw);
+            woff = win.off;
             if (tid < kBC) {
                 const int j = min(j0 + tid, N - 1);  // keys past N are masked: any in-window entry
                 const int rj = j / gw;
@@ -348,9 +499,8 @@ __global__ __launch_bounds__(256) void bw_rows_kernel(BwArgs a) {
             }
         }
         if (!STATS) {
-            const int64_t t0 = ((int64_t)bh * a.Np + j0) * CP;
-            copy_rows(L.vh, RP, a.vh + t0, kBC, CP);
-            copy_rows(L.sk, TPK, a.sk + t0, CP, kBC);
+            tvh.template store<RP>(L.vh);
+            tsk.template store<TPK>(L.sk);
         }
         return woff;
     };
@@ -396,13 +546,22 @@ __global__ __launch_bounds__(256) void bw_rows_kernel(BwArgs a) {
 
     const float mrow = a.m[tok], delta = a.delta[tok];
     const float inv_l = lq.live ? 1.0f / a.l[tok] : 0.0f;
-    // dO s of the lane's query, channels 32 s + 8 g .. + 7, two terms: the B operand of dP
+    // dO s of the lane's query, channels 32 s + 8 g .. + 7 (0 past d and N), two terms: the B
+    // operand of dP
     bf8 dhi[W], dlo[W];
 #pragma unroll
     for (int s = 0; s < W; ++s) {
-        const int64_t o = ((int64_t)bh * a.Np + i) * CP + 32 * s + 8 * g;
-        dhi[s] = *reinterpret_cast<const bf8*>(a.dos_hi + o);
-        dlo[s] = *reinterpret_cast<const bf8*>(a.dos_lo + o);
+        const int c0 = 32 * s + 8 * g;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = c0 + e;
+            const float x = lq.live && c < d ? ld_any(a.dout, tok * d + c, a.g_f32) * (a.vamax[(int64_t)bh * d + c] / 127.0f)
+                                             : 0.0f;
+            __bf16 h_, l_;
+            split_bf16(x, h_, l_);
+            dhi[s][e] = h_;
+            dlo[s][e] = l_;
+        }
     }
 
     const bool whole = BIAS == BK_RELPOS_G && a.db && a.dtp;  // the table's gradient accumulates in LDS
@@ -523,8 +682,10 @@ struct alignas(16) BwKLds {
     int qq[kBR];
 };
 
+// (LDS allows at most 2 workgroups per CU: registers up to that occupancy hold a tile's staged
+// loads without spilling.)
 template <int NT, int BIAS>
-__global__ __launch_bounds__(256) void bw_k_kernel(BwArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void bw_k_kernel(BwArgs a) {
     typedef BwKLds<NT, BIAS> Lt;
     constexpr int W = Lt::W, CP = Lt::CP, RP = Lt::RP, TPQ = Lt::TPQ, NCB = 2 * W;
     constexpr bool DENSE = BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32;
@@ -546,7 +707,7 @@ __global__ __launch_bounds__(256) void bw_k_kernel(BwArgs a) {
     const float seed = load_q<W>(a.kbits + tok * W, klive, d, g, kop);
     const v4f dseed = v4f{seed, seed, seed, seed};
     const float muk = a.kmu[tok];
-    bf8 vreg[W];
+    bf8 vreg[W];  // V^ of the lane's key (exact; 0 past d)
 #pragma unroll
     for (int s = 0; s < W; ++s) vreg[s] = *reinterpret_cast<const bf8*>(a.vh + ((int64_t)bh * a.Np + j) * CP + 32 * s + 8 * g);
 
@@ -567,35 +728,52 @@ __global__ __launch_bounds__(256) void bw_k_kernel(BwArgs a) {
 
     for (int qt = 0; qt < nqt; ++qt) {
         const int i0 = qt * kBR;
-        // ---- stage the query tile
-        stage_bits_f4<W>(L.q, a.qbits + (int64_t)bh * N * W, i0, N, d);
+        // ---- stage the query tile: every load, then the LDS stores
+        SignTile<W> qst;
+        qst.load(a.qbits + (int64_t)bh * N * W, i0, N);
+        float st_cq = 0.0f, st_mx = INFINITY, st_l = 1.0f, st_dl = 0.0f;  // queries >= N: P = 0
+        const bool qok = tid < kBR && i0 + tid < N;
+        if (qok) {
+            const int64_t qt_ = (int64_t)bh * N + i0 + tid;
+            st_cq = a.qmu[qt_];
+            st_mx = a.m[qt_];
+            st_l = a.l[qt_];
+            st_dl = a.delta[qt_];
+        }
+        // (two batches of loads, each issued whole before its stores: one batch of every tile
+        // would not fit the registers)
+        const int64_t t0 = ((int64_t)bh * a.Np + i0) * CP;
+        BfTile<kBR, CP> tdh, tdl;
+        tdh.load(a.dos_hi + t0);
+        tdl.load(a.dos_lo + t0);
+        DenseTile<BIAS == BK_DENSE_F32> btile;
+        if (DENSE) btile.load(a, h, i0, k0);
+        WinTile win;
+        if (BIAS == BK_RELPOS_G) win.load(a, table, i0, k0);
+        // (loads above, stores below)
+        qst.store_fp4(L.q, d);
         if (tid < kBR) {
-            const int i = i0 + tid;
-            const bool ok = i < N;
-            const int64_t qt_ = (int64_t)bh * N + (ok ? i : N - 1);
-            L.cq[tid] = ok ? a.qmu[qt_] * a.qk_scale : 0.0f;
-            L.mx[tid] = ok ? a.m[qt_] : INFINITY;  // P = 0 for queries >= N
-            L.il[tid] = ok ? 1.0f / a.l[qt_] : 0.0f;
-            L.dl[tid] = ok ? a.delta[qt_] : 0.0f;
+            L.cq[tid] = st_cq * a.qk_scale;
+            L.mx[tid] = st_mx;
+            L.il[tid] = qok ? 1.0f / st_l : 0.0f;
+            L.dl[tid] = st_dl;
             if (BIAS == BK_RELPOS_G) {
-                const int ii = ok ? i : N - 1, ri = ii / gw;
+                const int ii = min(i0 + tid, N - 1), ri = ii / gw;
                 L.qq[tid] = (ri - i0 / gw) * row_len + ii - ri * gw;
             }
         }
-        const int64_t t0 = ((int64_t)bh * a.Np + i0) * CP;
-        copy_rows(L.dos_hi, RP, a.dos_hi + t0, kBR, CP);
-        copy_rows(L.dos_lo, RP, a.dos_lo + t0, kBR, CP);
-        copy_rows(L.dot_hi, TPQ, a.dot_hi + t0, CP, kBR);
-        copy_rows(L.dot_lo, TPQ, a.dot_lo + t0, CP, kBR);
-        copy_rows(L.sq, TPQ, a.sq + t0, CP, kBR);
-        if (DENSE) {
-            for (int e = tid; e < kBR * kBC; e += 256) {
-                const int r = e / kBC, c = e - r * kBC;
-                const bool ok = i0 + r < N && k0 + c < N;
-                L.bt[e] = ok ? ld_any(a.bias, ((int64_t)h * N + i0 + r) * a.bias_ld + k0 + c, a.bias_f32) : 0.0f;
-            }
-        }
-        if (BIAS == BK_RELPOS_G) stage_window(L.tw, a, table, i0, k0);
+        tdh.template store<RP>(L.dos_hi);
+        tdl.template store<RP>(L.dos_lo);
+        if (DENSE) btile.store(L.bt, k0, N);
+        if (BIAS == BK_RELPOS_G) win.store(L.tw);
+        BfTile<CP, kBR> toh, tol, tsq;
+        toh.load(a.dot_hi + t0);
+        tol.load(a.dot_lo + t0);
+        tsq.load(a.sq + t0);
+        // (loads above, stores below)
+        toh.template store<TPQ>(L.dot_hi);
+        tol.template store<TPQ>(L.dot_lo);
+        tsq.template store<TPQ>(L.sq);
         __syncthreads();
 
         // ---- scores: queries as MFMA rows (slot order), the lane's key as the column
@@ -686,7 +864,10 @@ static void launch_bw_bk(const BwArgs& a, hipStream_t s) {
     const unsigned nb = (unsigned)((int64_t)a.B * a.H * ((a.N + kBC - 1) / kBC));
     const unsigned np = (unsigned)((int64_t)a.B * a.H * (a.Np / kBC));
     hipLaunchKernelGGL((bw_rows_kernel<NT, BK, true>), dim3(nb), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((bw_prep_kernel<16 * NT>), dim3(np), dim3(256), 0, s, a);
+    if (a.g_f32)
+        hipLaunchKernelGGL((bw_prep_kernel<16 * NT, true>), dim3(np), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((bw_prep_kernel<16 * NT, false>), dim3(np), dim3(256), 0, s, a);
     hipLaunchKernelGGL((bw_rows_kernel<NT, BK, false>), dim3(nb), dim3(256), 0, s, a);
     hipLaunchKernelGGL((bw_k_kernel<NT, BK>), dim3(nb), dim3(256), 0, s, a);
 }
