@@ -505,10 +505,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
         return woff;
     };
     // Scores of key tile j0 for the lane's query (keys >= N: -inf), the forward's tile code.
-    auto scores = [&](int j0, float (&S)[16], float& mloc) {
+    // Dense bias rows of the lane's query for key tile j0 (fetched a tile ahead of their use).
+    auto fetch_bias = [&](int j0, BiasRegs<BIAS>& br) {
+        if (DENSE && j0 < N) load_bias<BIAS>(br, buffer_rsrc(brow + j0 * esz, brow_bytes - j0 * esz), bvoff);
+    };
+    auto scores = [&](int j0, float (&S)[16], float& mloc, const BiasRegs<BIAS>& br) {
         const int jg = j0 + 16 * g;
-        BiasRegs<BIAS> br;
-        if (DENSE) load_bias<BIAS>(br, buffer_rsrc(brow + j0 * esz, brow_bytes - j0 * esz), bvoff);
         const float* wrun = L.tw;
         if (BIAS == BK_RELPOS_G) {
             const int rjm = min((j0 + kBC - 1) / gw, a.gh - 1);
@@ -519,11 +521,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
 
     if (STATS) {  // exact row max and row sum (online over the tiles), Delta
         float mrun = -INFINITY, lpart = 0.0f;
+        BiasRegs<BIAS> bcur, bnext;
+        fetch_bias(0, bcur);
         for (int t = 0; t < ntiles; ++t) {
+            fetch_bias((t + 1) * kBC, bnext);
             stage(t * kBC);
             __syncthreads();
             float S[16], mloc = -INFINITY;
-            scores(t * kBC, S, mloc);
+            scores(t * kBC, S, mloc, bcur);
+            bcur = bnext;
             const float mnew = fmaxf(mrun, rows4_max(mloc));
             float sum = 0.0f;
 #pragma unroll
@@ -567,15 +573,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
     const bool whole = BIAS == BK_RELPOS_G && a.db && a.dtp;  // the table's gradient accumulates in LDS
     if (BIAS == BK_RELPOS_G && a.db)
         for (int e = tid; e < (whole ? kTabMax : kRelposWin); e += 256) L.dwin[e] = 0.0f;
+    BiasRegs<BIAS> bcur, bnext;
+    fetch_bias(0, bcur);
     v4f dqacc[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) dqacc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
     for (int t = 0; t < ntiles; ++t) {
         const int j0 = t * kBC, jg = j0 + 16 * g;
+        fetch_bias(j0 + kBC, bnext);
         const int woff = stage(j0);
         __syncthreads();
         float S[16], mloc = -INFINITY;
-        scores(j0, S, mloc);
+        scores(j0, S, mloc, bcur);
+        bcur = bnext;
         // dP: keys as MFMA rows (the score tile's order), 32 channels per step
         float dS[16];
 #pragma unroll
