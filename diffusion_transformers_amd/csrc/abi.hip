@@ -119,11 +119,19 @@ int run_attention(const void* q, const void* k, const void* v, int dtype, int bi
     float* km = reinterpret_cast<float*>(ws + l.kmu);
     int8_t* vq = reinterpret_cast<int8_t*>(ws + l.vq);
     float* va = reinterpret_cast<float*>(ws + l.vamax);
-    hipError_t e = launch_prepare(q, k, v, dtype == BINATTN_F32, B * H, N, d, binattn_vq_ld(N), qb, qm, kb, km, vq,
-                                  va, stream);
+    FwdArgs a = forward_args(qb, qm, kb, km, vq, va, bias_dtype, bias, bias_ld, grid_h, grid_w, B, H, N, d, out,
+                             out_dtype);
+    // streamed rows: the forward packs Q in its own prologue, the preparation takes K and V only
+    const bool qx = forward_streams(a, bias_kind);
+    if (qx) {
+        a.qbits = nullptr;
+        a.qmu = nullptr;
+        a.qx = q;
+        a.qx_f32 = dtype == BINATTN_F32;
+    }
+    hipError_t e = launch_prepare(qx ? nullptr : q, k, v, dtype == BINATTN_F32, B * H, N, d, binattn_vq_ld(N), qb, qm,
+                                  kb, km, vq, va, stream);
     if (e != hipSuccess) return BINATTN_ELAUNCH;
-    const FwdArgs a = forward_args(qb, qm, kb, km, vq, va, bias_dtype, bias, bias_ld, grid_h, grid_w, B, H, N, d,
-                                   out, out_dtype);
     return launched(launch_forward(a, bias_kind, stream));
 }
 

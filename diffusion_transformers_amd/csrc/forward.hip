@@ -193,6 +193,8 @@ static hipError_t launch_fwd_nt(const FwdArgs& a, int bk, hipStream_t s) {
     return hipGetLastError();
 }
 
+bool forward_streams(const FwdArgs& a, int bias_kind) { return stream_picked(a, bias_kind == 2); }
+
 hipError_t launch_forward(const FwdArgs& a, int bias_kind, hipStream_t s) {
     int bk = BK_NONE;
     if (bias_kind == 1) bk = a.bias_f32 ? BK_DENSE_F32 : BK_DENSE_F16;

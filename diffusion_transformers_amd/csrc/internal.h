@@ -27,16 +27,21 @@ struct FwdArgs {
     const _Float16* k_raw;
     const _Float16* v_raw;
     int wrs;              // head-resident kernel: LDS row stride of its relative-position window
+    const void* qx;       // streamed rows: fp16 / fp32 Q packed in the kernel's prologue (qbits, qmu unused)
+    int qx_f32;
 };
 
 hipError_t launch_pack_qk(const void* x, int f32, int64_t ntok, int d, uint32_t* bits, float* mu,
                           hipStream_t s);
 hipError_t launch_quant_v(const void* v, int f32, int BH, int N, int d, int64_t ldv, int8_t* vq, float* vamax,
                           hipStream_t s);
+// q may be null: then only K and V are prepared.
 hipError_t launch_prepare(const void* q, const void* k, const void* v, int f32, int BH, int N, int d, int64_t ldv,
                           uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu, int8_t* vq, float* vamax,
                           hipStream_t s);
 hipError_t launch_forward(const FwdArgs& a, int bias_kind, hipStream_t s);
+// Whether launch_forward runs the streaming kernel for this shape (which can pack Q itself).
+bool forward_streams(const FwdArgs& a, int bias_kind);
 // The forward with the relative-position bias on a grid whose width is not a multiple of 16.
 hipError_t launch_forward_gather(const FwdArgs& a, hipStream_t s);
 // Whole attention from fp16 Q, K, V in one kernel where the shape allows it (short rows);

@@ -4,7 +4,7 @@
 //
 // One grid, two kinds of workgroup: the first B*H quantise one head each with its V held in
 // registers (the long ones, dispatched first so that none starts late), the rest pack spans of
-// 256 Q tokens and then of K tokens.  Heads whose V does not fit the register budget take the
+// 256 Q tokens and then of K tokens (K only when the forward packs Q itself).  Heads whose V does not fit the register budget take the
 // general path: the pack kernel, then the absmax and quantise kernels.
 #include "common.h"
 #include "internal.h"
@@ -29,10 +29,10 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
     }
     const int64_t ntok = (int64_t)BH * N;
     const int64_t pb = b - BH;
-    if (pb < npack)
+    if (q && pb < npack)
         pack_wave<T>(q, ntok, d, W, qbits, qmu, pb);
     else
-        pack_wave<T>(k, ntok, d, W, kbits, kmu, pb - npack);
+        pack_wave<T>(k, ntok, d, W, kbits, kmu, q ? pb - npack : pb);
 }
 
 template <typename T>
@@ -43,7 +43,7 @@ static hipError_t launch_prepare_t(const T* q, const T* k, const T* v, int BH, i
     const int64_t ntok = (int64_t)BH * N;
     const int64_t npack = pack_blocks(ntok);
     const int nc = quant_chunks_per_thread<T>(N, d);
-    const int64_t nblocks = BH + 2 * npack;
+    const int64_t nblocks = BH + (q ? 2 : 1) * npack;  // (no Q: K and V only)
     if (nblocks <= 0x7fffffff && nc <= 20) {
         const dim3 grid((unsigned)nblocks), block(256);
         if (nc <= 8)
@@ -55,7 +55,7 @@ static hipError_t launch_prepare_t(const T* q, const T* k, const T* v, int BH, i
         return hipGetLastError();
     }
     const int f32 = sizeof(T) == 4;
-    hipError_t e = launch_pack_qk(q, f32, ntok, d, qbits, qmu, s);
+    hipError_t e = q ? launch_pack_qk(q, f32, ntok, d, qbits, qmu, s) : hipSuccess;
     if (e == hipSuccess) e = launch_pack_qk(k, f32, ntok, d, kbits, kmu, s);
     if (e == hipSuccess) e = launch_quant_v(v, f32, BH, N, d, ldv, vq, vamax, s);
     return e;

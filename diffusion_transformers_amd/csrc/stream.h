@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 4 && 
 
     const int qw0 = q0 + wave * 16;
     const bool wave_live = qw0 < N;
-    const LaneQ lq = lane_query<NT>(a, bh, qw0, g, n16);
+    const LaneQ lq = a.qx ? lane_query_raw<NT>(a, bh, qw0, g, n16) : lane_query<NT>(a, bh, qw0, g, n16);
 
     // relative position (see above): per lane the query part aq and the key part kk (kcol: the
     // key's grid column); uniform, the grid position (lrow, lcol) of the last key of the last
@@ -214,6 +214,16 @@ inline void launch_stream(const FwdArgs& a, int ntiles, dim3 grid, hipStream_t s
         hipLaunchKernelGGL((binattn_fwd_stream_kernel<NT, BK, true, TF32>), grid, dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL((binattn_fwd_stream_kernel<NT, BK, false, TF32>), grid, dim3(256), 0, s, a);
+}
+
+// The kernel launch_fwd_bk picks: the head-resident kernel for rows of <= 4 tiles (relative
+// position: when the whole row's window fits) and, at d <= 64 without the relative-position bias,
+// for rows of <= 10 tiles; the streaming kernel otherwise.
+inline bool stream_picked(const FwdArgs& a, bool relpos) {
+    const int ntiles = (a.N + kBC - 1) / kBC, nt = (a.d + 15) / 16;
+    if (ntiles <= kKeepTiles && (!relpos || keep_window_fits(a))) return false;
+    if (nt <= 4 && !relpos && ntiles <= kLongTiles) return false;
+    return true;
 }
 
 template <int NT, int BK>

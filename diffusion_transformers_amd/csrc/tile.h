@@ -347,6 +347,73 @@ __device__ __forceinline__ LaneQ lane_query(const FwdArgs& a, int bh, int qw0, i
     return lq;
 }
 
+// The lane's query packed in the kernel's own prologue from fp16 / fp32 Q (a.qx): its sign word g
+// and mu_q with pack_wave's arithmetic -- the same sign test, the same per-chunk partial |x| sums,
+// added in channel order (lanes g = 0, 1, .. add theirs in turn) -- so that the packed path and
+// this one agree bit for bit ("BinaryAttention" paper notes, key design 1).
+template <int NT>
+__device__ __forceinline__ LaneQ lane_query_raw(const FwdArgs& a, int bh, int qw0, int g, int n16) {
+    constexpr int W = (NT + 1) / 2;
+    LaneQ lq;
+    const int N = a.N, d = a.d, cpt = d >> 3;
+    const int i = qw0 + n16;
+    lq.live = i < N;
+    lq.qi = lq.live ? i : N - 1;
+    const int64_t row = ((int64_t)bh * N + lq.qi) * d;
+    uint4 v[8];  // chunks 4 g .. 4 g + 3 (fp16: one 16-byte load each; fp32: two)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        if (4 * g + c < cpt) {
+            if (a.qx_f32) {
+                const float* x = static_cast<const float*>(a.qx) + row + 8 * (4 * g + c);
+                v[2 * c] = *reinterpret_cast<const uint4*>(x);
+                v[2 * c + 1] = *reinterpret_cast<const uint4*>(x + 4);
+            } else {
+                v[c] = *reinterpret_cast<const uint4*>(static_cast<const _Float16*>(a.qx) + row + 8 * (4 * g + c));
+            }
+        }
+    }
+    uint32_t word = 0;
+    float psum[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        uint32_t byte = 0;
+        float sum = 0.0f;
+        if (a.qx_f32) {
+            const uint32_t w8[8] = {v[2 * c].x, v[2 * c].y, v[2 * c].z, v[2 * c].w,
+                                    v[2 * c + 1].x, v[2 * c + 1].y, v[2 * c + 1].z, v[2 * c + 1].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float f = __uint_as_float(w8[e]);
+                byte |= (f >= 0.0f ? 1u : 0u) << e;  // -0.0 >= 0 holds: zero counts as +1
+                sum += fabsf(f);
+            }
+        } else {
+            chunk_sign_abs(__builtin_bit_cast(h8, v[c]), byte, sum);
+        }
+        psum[c] = sum;
+        if (4 * g + c < cpt) word |= byte << (8 * c);
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < W; ++gg) {
+        if (g == gg) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (4 * g + c < cpt) acc += psum[c];
+        }
+        acc = __shfl(acc, 16 * gg + n16);
+    }
+    lq.qop = q_operand(word, lq.live && g < W, d, g);
+    const float pos = rows4_sum((float)__builtin_popcount(g < W ? word : 0u));  // sign bits set over the query
+    const float seed = lq.live ? (float)d - 2.0f * pos : 0.0f;
+    lq.dseed = v4f{seed, seed, seed, seed};
+    lq.cq = lq.live ? acc / (float)d * a.qk_scale : 0.0f;
+    return lq;
+}
+
 // Scores of one tile for one lane: S[k] for keys jg + k, k = 0..15, in natural units, keys >= N
 // (k >= nvalid on the tail tile) set to -inf, and the running lane max mloc over them.
 // sk/smu: the staged tile.  Lanes whose channel group g is past d read the operand rows of group

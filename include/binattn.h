@@ -183,7 +183,11 @@ int binattn_prepare(const void* q, const void* k, const void* v, int dtype, int 
  * fp16 inputs with rows of at most 256 keys, d of 56, 64, 72, 80, 120 or 128 (and, for the
  * relative-position bias, a table window that fits the kernel's staging) it runs as one
  * kernel that packs K, quantises V and packs its queries itself (the workspace is then not
- * written); otherwise as those two calls.  binattn_attention_one_kernel tells which.
+ * written); otherwise as those two calls, except that rows the forward streams (more than
+ * 640 keys at d <= 64, more than 256 keys above, and relative-position rows whose whole-row
+ * window does not fit) have their queries packed inside the forward's prologue, with the
+ * preparation taking only K and V -- the same results, bit for bit.
+ * binattn_attention_one_kernel tells whether the one-kernel form applies.
  *
  *   q, k, v    [B,H,N,d] of dtype (contiguous)
  *   bias...    as binattn_forward
