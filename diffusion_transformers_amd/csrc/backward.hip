@@ -430,10 +430,16 @@ struct alignas(16) BwQLds {
 // dS, the bias gradient and dq, from the row statistics and the prepared operand arrays.
 // (LDS allows at most 3 workgroups per CU: registers up to that occupancy hold a tile's staged
 // loads without spilling.)
-template <int NT, int BIAS, bool STATS>
+// RUN16 (relative position on a grid whose width is a multiple of 16, d > 32): a wave's 16
+// queries lie in one grid row and so do the 16 keys of a lane group, so the 256 dS values of a
+// (wave, group) pair fall on the 31 table entries of their diagonals ci - cj: they are summed
+// along those diagonals in LDS first (the V^ and sign tiles' space, free after dQ), and 2 LDS
+// atomics per lane replace 16.
+template <int NT, int BIAS, bool STATS, bool RUN16 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) void bw_rows_kernel(BwArgs a) {
     typedef BwQLds<NT, BIAS> Lt;
     constexpr int W = Lt::W, CP = Lt::CP, RP = Lt::RP, TPK = Lt::TPK, NCB = 2 * W;
+    static_assert(!RUN16 || 2 * (kBC * RP + CP * TPK) >= 4 * 4 * 16 * 17 * 4, "diagonal scratch fits the two tiles");
     constexpr bool DENSE = BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32;
     __shared__ Lt L;
     const int N = a.N, d = a.d;
@@ -613,13 +619,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
             for (int k = 0; k < 16; k += 4)
                 *reinterpret_cast<float4*>(drow + k) = make_float4(dS[k], dS[k + 1], dS[k + 2], dS[k + 3]);
         }
-        if (BIAS == BK_RELPOS_G && a.db) {
-            if (lq.live) {
+        if (BIAS == BK_RELPOS_G && a.db && !RUN16) {
+            if (lq.live) {  // (keys past N add their dS = 0 at key N - 1's entry: no per-key test)
                 const int rjm = min((j0 + kBC - 1) / gw, a.gh - 1);
                 const int base = aq + rjm * row_len + (whole ? woff : 0);  // window index (+ its table offset)
+                char* drow = reinterpret_cast<char*>(L.dwin) + 4 * base;   // L.kk: the keys' byte offsets from it
+                int kb[16];
 #pragma unroll
-                for (int k = 0; k < 16; ++k)
-                    if (jg + k < N) atomicAdd(&L.dwin[base + L.kk[16 * g + k] / 4], dS[k]);
+                for (int k = 0; k < 16; k += 4) {
+                    const int4 o4 = *reinterpret_cast<const int4*>(&L.kk[16 * g + k]);
+                    kb[k] = o4.x; kb[k + 1] = o4.y; kb[k + 2] = o4.z; kb[k + 3] = o4.w;
+                }
+#pragma unroll
+                for (int k = 0; k < 16; ++k) atomicAdd(reinterpret_cast<float*>(drow + kb[k]), dS[k]);
             }
         }
         // dQ: channels as MFMA rows, keys 16 g + 8 s2 + i as k; B = dS mu_k / sqrt(d) in two terms
@@ -638,8 +650,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
             dqacc[cb] = mfma_b(a1, bh1, dqacc[cb]);
             dqacc[cb] = mfma_b(a1, bl1, dqacc[cb]);
         }
+        if (RUN16 && a.db) {  // the table gradient by diagonals (see above)
+            __syncthreads();  // every wave is done with the V^ and sign tiles
+            float* dg = reinterpret_cast<float*>(L.vh) + (wave * 4 + g) * 16 * 17;  // [query col][key col], pitch 17
+#pragma unroll
+            for (int k = 0; k < 16; ++k) dg[n16 * 17 + k] = dS[k];  // (0 for queries past N)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int d0 = n16 - 15, d1 = n16 + 1;  // this lane's diagonals ci - cj
+            float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                if (t - d0 < 16) s0 += dg[t * 17 + t - d0];       // ci = t, cj = t - d0
+                if (t + d1 < 16) s1 += dg[(t + d1) * 17 + t];     // ci = t + d1, cj = t
+            }
+            if (qw0 < N && jg < N) {  // (N is a multiple of the grid width: whole rows and runs)
+                const int ri = qw0 / gw, ci0 = qw0 - ri * gw, rj = jg / gw, cj0 = jg - rj * gw;
+                const int t0 = (ri - rj + a.gh - 1) * row_len + ci0 - cj0 + gw - 1 - (whole ? 0 : woff);
+                atomicAdd(&L.dwin[t0 + d0], s0);
+                if (d1 < 16) atomicAdd(&L.dwin[t0 + d1], s1);
+            }
+        }
         __syncthreads();
-        if (BIAS == BK_RELPOS_G && a.db && !whole) {  // flush the tile's window entries
+        // flush the window's entries once the next key tile moves it (tiles whose last keys share
+        // a grid row share the window)
+        const bool moves = t + 1 == ntiles || min((j0 + 2 * kBC - 1) / gw, a.gh - 1) != min((j0 + kBC - 1) / gw, a.gh - 1);
+        if (BIAS == BK_RELPOS_G && a.db && !whole && moves) {
             float* dtab = a.db + h * tsz;
             for (int e = tid; e < kRelposWin; e += 256) {
                 const float v = L.dwin[e];
@@ -878,7 +915,10 @@ static void launch_bw_bk(const BwArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((bw_prep_kernel<16 * NT, true>), dim3(np), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL((bw_prep_kernel<16 * NT, false>), dim3(np), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((bw_rows_kernel<NT, BK, false>), dim3(nb), dim3(256), 0, s, a);
+    if (is_relpos(BK) && a.gw % 16 == 0 && a.W >= 2)
+        hipLaunchKernelGGL((bw_rows_kernel<NT, BK, false, (NT > 2)>), dim3(nb), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((bw_rows_kernel<NT, BK, false>), dim3(nb), dim3(256), 0, s, a);
     hipLaunchKernelGGL((bw_k_kernel<NT, BK>), dim3(nb), dim3(256), 0, s, a);
 }
 

@@ -85,6 +85,12 @@ CASES = [
     (1, 2, 100, 40, "f32", "dense", (), 0.0),
     (1, 1, 577, 64, "f16", "dense", (), 0.0),
     (1, 1, 1024, 64, "f16", "relpos", (8, 128), 0.0),
+    # grid widths that are multiples of 16 take the diagonal sums of the table gradient: a table
+    # larger than the kernel's LDS copy (31 x 255 entries: per-tile windows) and d = 32 (no room
+    # for the diagonal scratch: per-key atomics)
+    (1, 1, 2048, 64, "f16", "relpos", (16, 128), 0.0),
+    (2, 1, 256, 32, "f16", "relpos", (16, 16), 0.0),
+    (1, 2, 512, 96, "f32", "relpos", (16, 32), 0.0),
 ]
 
 
