@@ -68,6 +68,7 @@ def _load():
     lib.oracle_backward.argtypes = [vp, vp, vp, i32, vp, i32, i32, i64, i64, i64, i32, vp, ctypes.c_double, vp, vp, vp,
                                     vp]
     lib.oracle_backward.restype = i32
+    lib.oracle_qkv_project.argtypes = [vp, vp, vp, i64, i32, i64, vp, vp]
     _lib = lib
     return lib
 
@@ -205,3 +206,24 @@ def backward(q, k, v, dout, bias=None, bias_kind=BIAS_NONE, grid=None, ste_clip=
     if rc != 0:
         raise ValueError(f"oracle_backward failed with code {rc}")
     return dq, dk, dv, db
+
+
+def qkv_project(x, w, bias, H: int, d: int):
+    """The QKV projection that produces the attention's inputs, in fp64.
+
+    x [B,N,C] (C = H d), w [3C,C] (row o is output feature o), bias [3C] or None.  Output
+    feature o = p C + h d + c is channel c of head h of part p (0: Q, 1: K, 2: V), the usual
+    [3, H, d] order of a fused projection.  Returns q, k, v [B,H,N,d] and, in the same layout,
+    mq, mk, mv: sum_i |x_i w_oi| + |bias_o|, the magnitude that bounds any summation order's
+    rounding error."""
+    x, w = _f64(x), _f64(w)
+    b = None if bias is None else _f64(bias)
+    B, N, C = x.shape
+    if C != H * d or w.shape != (3 * C, C) or (b is not None and b.shape != (3 * C,)):
+        raise ValueError("shapes of x, w, bias do not match H, d")
+    y = np.zeros((B * N, 3 * C), dtype=np.float64)
+    mag = np.zeros((B * N, 3 * C), dtype=np.float64)
+    _load().oracle_qkv_project(_ptr(x), _ptr(w), _ptr(b), B * N, C, 3 * C, _ptr(y), _ptr(mag))
+    split = lambda a: np.ascontiguousarray(a.reshape(B, N, 3, H, d).transpose(2, 0, 3, 1, 4))
+    ys, ms = split(y), split(mag)
+    return ys[0], ys[1], ys[2], ms[0], ms[1], ms[2]

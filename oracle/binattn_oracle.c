@@ -474,3 +474,27 @@ int oracle_backward(const double* q, const double* k, const double* v, int bias_
     ctx_free(&c);
     return fail ? -2 : 0;
 }
+
+/* The producer of Q, K and V: the attention block's linear QKV projection, whose output is what
+ * key design 1 binarises (the sign and mean |x| of each token's Q and K) and key design 3
+ * quantises (V).  y[m][o] = sum_i x[m][i] w[o][i] + bias[o] in fp64, in index order, for
+ * x [M, C], w [O, C] (row o: output feature o), bias [O] or NULL.  mag[m][o] = sum_i
+ * |x[m][i] w[o][i]| + |bias[o]| bounds the rounding error of any other summation order (NULL:
+ * not written).  The split of the O = 3C outputs into Q, K, V and heads is the caller's. */
+void oracle_qkv_project(const double* x, const double* w, const double* bias, int64_t M, int C, int64_t O,
+                        double* y, double* mag) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const double* xr = x + m * C;
+        for (int64_t o = 0; o < O; ++o) {
+            const double* wr = w + o * C;
+            double s = bias ? bias[o] : 0.0, a = bias ? fabs(bias[o]) : 0.0;
+            for (int i = 0; i < C; ++i) {
+                s += xr[i] * wr[i];
+                a += fabs(xr[i] * wr[i]);
+            }
+            y[m * O + o] = s;
+            if (mag) mag[m * O + o] = a;
+        }
+    }
+}

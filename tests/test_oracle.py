@@ -336,3 +336,58 @@ def test_rows_match_full_forward():
     rows = np.array([0, 7, 39, 40, 111, B * H * N - 1])
     part = oracle.forward_rows(q, k, v, rows, table, oracle.BIAS_RELPOS, grid=(5, 8))
     np.testing.assert_array_equal(part, full.reshape(-1, d)[rows])
+
+
+# ---- the QKV projection (the producer whose output key designs 1 and 3 take) ----
+
+def test_qkv_project_equals_float_matmul_by_index():
+    """Every q/k/v entry equals numpy's fp64 x @ w.T + bias at the feature o = p C + h d + c,
+    looked up entry by entry (the [3, H, d] split and the [B,H,N,d] layout)."""
+    B, N, H, d = 2, 5, 3, 8
+    C = H * d
+    rng = np.random.default_rng(11)
+    x, w, bias = rng.standard_normal((B, N, C)), rng.standard_normal((3 * C, C)), rng.standard_normal(3 * C)
+    q, k, v, mq, mk, mv = oracle.qkv_project(x, w, bias, H, d)
+    y = x.reshape(B * N, C) @ w.T + bias
+    a = np.abs(x.reshape(B * N, C))[:, None, :] * np.abs(w)[None, :, :]
+    mag = a.sum(-1) + np.abs(bias)
+    for p, (t, m) in enumerate(((q, mq), (k, mk), (v, mv))):
+        assert t.shape == (B, H, N, d)
+        for b in range(B):
+            for h in range(H):
+                for n in range(N):
+                    for c in range(d):
+                        o = p * C + h * d + c
+                        assert abs(t[b, h, n, c] - y[b * N + n, o]) <= 1e-12 * mag[b * N + n, o]
+                        assert abs(m[b, h, n, c] - mag[b * N + n, o]) <= 1e-12 * mag[b * N + n, o]
+                        assert abs(t[b, h, n, c]) <= m[b, h, n, c]
+
+
+def test_qkv_project_selection_weights():
+    """One-hot weight rows copy one input feature: output o of token (b, n) is x[b, n, pi(o)]
+    exactly, plus the bias; with no bias it is the copy itself."""
+    B, N, H, d = 2, 3, 2, 16
+    C = H * d
+    rng = np.random.default_rng(5)
+    pi = rng.integers(0, C, 3 * C)
+    w = np.zeros((3 * C, C))
+    w[np.arange(3 * C), pi] = 1.0
+    x = np.arange(B * N * C, dtype=np.float64).reshape(B, N, C) - 40.0
+    q, k, v, *_ = oracle.qkv_project(x, w, None, H, d)
+    bias = np.arange(3 * C, dtype=np.float64) * 0.5
+    qb, kb, vb, *_ = oracle.qkv_project(x, w, bias, H, d)
+    for p, (t, tb) in enumerate(((q, qb), (k, kb), (v, vb))):
+        for b in range(B):
+            for h in range(H):
+                for n in range(N):
+                    for c in range(d):
+                        o = p * C + h * d + c
+                        assert t[b, h, n, c] == x[b, n, pi[o]]
+                        assert tb[b, h, n, c] == x[b, n, pi[o]] + bias[o]
+
+
+def test_qkv_project_rejects_mismatched_shapes():
+    with pytest.raises(ValueError):
+        oracle.qkv_project(np.zeros((1, 2, 12)), np.zeros((36, 12)), None, 2, 8)
+    with pytest.raises(ValueError):
+        oracle.qkv_project(np.zeros((1, 2, 16)), np.zeros((48, 16)), np.zeros(47), 2, 8)
