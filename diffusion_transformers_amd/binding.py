@@ -68,6 +68,8 @@ def _load():
     lib.binattn_backward.restype = i32
     lib.binattn_keep_plan.argtypes = [i64, i32, i32, i32, ctypes.POINTER(ctypes.c_int)]
     lib.binattn_keep_plan.restype = i32
+    lib.binattn_qkv_pack.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.binattn_qkv_pack.restype = i32
     return lib
 
 
@@ -75,7 +77,8 @@ _lib = _load()
 EXPORTS = ["binattn_abi_version", "binattn_strerror", "binattn_words", "binattn_vq_ld", "binattn_pack_qk",
            "binattn_quant_v", "binattn_forward", "binattn_scores_i32", "binattn_qk_rowstats",
            "binattn_prepare", "binattn_attention_workspace", "binattn_attention", "binattn_attention_one_kernel",
-           "binattn_keep_plan", "binattn_attention_noalloc", "binattn_backward_workspace", "binattn_backward"]
+           "binattn_keep_plan", "binattn_attention_noalloc", "binattn_backward_workspace", "binattn_backward",
+           "binattn_qkv_pack"]
 NOALLOC_SCRATCH_BYTES = 64 << 20  # BINATTN_NOALLOC_SCRATCH_BYTES
 QK_MFMA, QK_POPCOUNT = 0, 1
 
@@ -195,6 +198,33 @@ def pack_qk(x: torch.Tensor, bits=None, mu=None):
     _need(mu, "mu", (B, H, N), (torch.float32,), x.device)
     _check("binattn_pack_qk", _lib.binattn_pack_qk(_p(x), _dt(x), B, H, N, d, _p(bits), _p(mu), _stream()))
     return bits, mu
+
+
+def qkv_pack(x: torch.Tensor, w: torch.Tensor, bias, H: int, d: int, with_qk: bool = False):
+    """The QKV projection with Q and K binarised in its epilogue.
+
+    x [B,N,H d] fp16, w [3 H d, H d] fp16 (a linear layer's weight), bias [3 H d] fp16 or None
+    -> (q_bits, q_mu, k_bits, k_mu, v [B,H,N,d] fp16), plus (q, k) fp16 [B,H,N,d] with_qk."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 3:
+        raise ValueError("x must be a 3-D tensor [B,N,C]")
+    B, N, C = x.shape
+    if C != H * d:
+        raise ValueError(f"x has {C} features, expected H*d = {H * d}")
+    _need(x, "x", (B, N, C), (torch.float16,))
+    _need(w, "w", (3 * C, C), (torch.float16,), x.device)
+    if bias is not None:
+        _need(bias, "bias", (3 * C,), (torch.float16,), x.device)
+    dev, W = x.device, words(d)
+    qb = torch.empty((B, H, N, W), dtype=torch.int32, device=dev)
+    kb = torch.empty((B, H, N, W), dtype=torch.int32, device=dev)
+    qm = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    km = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    v = torch.empty((B, H, N, d), dtype=torch.float16, device=dev)
+    q = torch.empty((B, H, N, d), dtype=torch.float16, device=dev) if with_qk else None
+    k = torch.empty((B, H, N, d), dtype=torch.float16, device=dev) if with_qk else None
+    _check("binattn_qkv_pack", _lib.binattn_qkv_pack(_p(x), _p(w), _p(bias), B, N, H, d, _p(qb), _p(qm), _p(kb),
+                                                     _p(km), _p(v), _p(q), _p(k), _stream()))
+    return (qb, qm, kb, km, v, q, k) if with_qk else (qb, qm, kb, km, v)
 
 
 def quant_v(v: torch.Tensor, vq=None, vamax=None):

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbinattn.so")
-SOURCES = ["pack.hip", "quant.hip", "prep.hip", "forward.hip", "forward_gather.hip", "attention.hip", "backward.hip", "abi.hip"]
+SOURCES = ["pack.hip", "quant.hip", "prep.hip", "forward.hip", "forward_gather.hip", "attention.hip", "backward.hip", "project.hip", "abi.hip"]
 ARCH = "gfx950"
 
 

@@ -331,6 +331,33 @@ int64_t binattn_backward_workspace(int B, int H, int N, int d, int bias_kind) {
     return workspace_layout(B, H, N, d).total + backward_arrays_bytes(B, H, N, d, bias_kind);
 }
 
+int binattn_qkv_pack(const void* x, const void* w, const void* bias, int B, int N, int H, int d,
+                     uint32_t* q_bits, float* q_mu, uint32_t* k_bits, float* k_mu, void* v, void* q, void* k,
+                     void* stream) {
+    if (!x || !w || !q_bits || !q_mu || !k_bits || !k_mu || !v) return BINATTN_EINVAL;
+    int rc = check_dims(B, H, N, d);
+    if (rc) return rc;
+    const int64_t M = (int64_t)B * N;
+    int hpt = 0, nb = 0, nmt = 0, nnt = 0;
+    if ((int64_t)H * d > (1 << 20) || M > ((int64_t)1 << 40)) return BINATTN_EUNSUPPORTED;
+    qkv_pack_plan(H, d, M, &hpt, &nb, &nmt, &nnt);
+    if ((int64_t)nmt * nnt > 0x7FFFFFFF) return BINATTN_EUNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w) || (bias && !aligned16(bias)) || !aligned16(q_bits) || !aligned16(q_mu) ||
+        !aligned16(k_bits) || !aligned16(k_mu) || !aligned16(v) || (q && !aligned16(q)) || (k && !aligned16(k)))
+        return BINATTN_EALIGN;
+    if ((rc = device_ready())) return rc;
+    ProjArgs a = {};
+    a.x = static_cast<const _Float16*>(x);
+    a.w = static_cast<const _Float16*>(w);
+    a.bias = static_cast<const _Float16*>(bias);
+    a.M = M; a.N = N; a.H = H; a.d = d;
+    a.qbits = q_bits; a.qmu = q_mu; a.kbits = k_bits; a.kmu = k_mu;
+    a.v = static_cast<_Float16*>(v);
+    a.q = static_cast<_Float16*>(q);
+    a.k = static_cast<_Float16*>(k);
+    return launched(launch_qkv_pack(a, (hipStream_t)stream));
+}
+
 int binattn_backward(const void* q, const void* k, const void* v, const void* o, const void* dout, int dtype,
                      int grad_dtype, int bias_kind, int bias_dtype, const void* bias, int64_t bias_ld, int grid_h,
                      int grid_w, int B, int H, int N, int d, float ste_clip, float* dq, float* dk, float* dv,

@@ -86,4 +86,25 @@ bool relpos_window_fits(int gw);
 int keep_plan_max_blocks();
 void keep_plan_host(int64_t nheads, int nqb, int slots, bool fused, int plan[4]);
 
+// The QKV projection with Q/K binarised in its epilogue (project.hip).  The caller fills the
+// pointers and x/w shapes (M tokens of C = H d features, N tokens per batch item); the launcher
+// fills the tile plan.
+struct ProjArgs {
+    const _Float16* x;
+    const _Float16* w;
+    const _Float16* bias;  // may be null
+    int64_t M;
+    int N, H, d, C, W;
+    int hpt, nsec, nmt, nnt;  // head sections per tile, 3H, token tiles, feature tiles
+    uint32_t* qbits;
+    float* qmu;
+    uint32_t* kbits;
+    float* kmu;
+    _Float16* v;
+    _Float16* q;  // may be null
+    _Float16* k;  // may be null
+};
+void qkv_pack_plan(int H, int d, int64_t M, int* hpt, int* nb, int* nmt, int* nnt);
+hipError_t launch_qkv_pack(const ProjArgs& a, hipStream_t s);
+
 }  // namespace binattn

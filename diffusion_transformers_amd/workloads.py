@@ -102,3 +102,18 @@ def make(w: Workload, seed: int | None = None):
 def custom(B, H, N, d, dtype="f16", bias="dense", grid=(), seed=0, outlier_frac=0.0):
     """Inputs for an ad-hoc shape with the same recipe (used for ragged / edge cases)."""
     return make(Workload(f"custom_{B}x{H}x{N}x{d}", B, H, N, d, dtype, bias, tuple(grid), outlier_frac), seed)
+
+
+def projection_inputs(B, N, H, d, bias=True, seed=0):
+    """Inputs of the QKV projection that produces a workload's Q, K and V.
+
+    Recipe: rng = numpy.random.default_rng(seed); x = standard_normal([B,N,H d]) (the tokens'
+    hidden states); w = standard_normal([3 H d, H d]) / sqrt(H d) (so every projected entry has
+    unit variance); bias = standard_normal([3 H d]) * 0.02 when asked; all drawn in float32 in
+    that order and cast to fp16 (round-to-nearest-even)."""
+    rng = np.random.default_rng(seed)
+    C = H * d
+    x = rng.standard_normal((B, N, C), dtype=np.float32)
+    w = rng.standard_normal((3 * C, C), dtype=np.float32) / np.float32(np.sqrt(C))
+    b = rng.standard_normal(3 * C, dtype=np.float32) * np.float32(0.02) if bias else None
+    return dict(x=x.astype(np.float16), w=w.astype(np.float16), bias=None if b is None else b.astype(np.float16))

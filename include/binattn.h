@@ -102,6 +102,33 @@ int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t
                     void* stream);
 
 /*
+ * binattn_qkv_pack -- the QKV projection that produces the attention's inputs, with Q and K
+ * binarised in its epilogue.
+ * Passages: key design 1 (Scaled Binary Representations): Q and K enter the attention only as
+ * channel signs and per-token mean |x|, so the producer hands over those; key design 3 (Hybrid
+ * Quantization): V is quantised per channel over all N tokens of a head, which binattn_quant_v
+ * does afterwards from the fp16 v written here.
+ *
+ *   x       [B,N,C] fp16, C = H*d: the tokens' hidden states, read only
+ *   w       [3C,C]  fp16: row o is output feature o (a linear layer's weight), read only
+ *   bias    [3C]    fp16, or NULL for none
+ *   Output feature o = p*C + h*d + c is channel c of head h of part p (0: Q, 1: K, 2: V).
+ *   y[b,n,o] = fp16(sum_i x[b,n,i] * w[o,i] + bias[o]): fp32 accumulation in an unspecified
+ *   order, one round-to-nearest-even to fp16 at the end.
+ *   q_bits, q_mu, k_bits, k_mu   [B,H,N,W] uint32 and [B,H,N] fp32: exactly what
+ *           binattn_pack_qk writes for the fp16 Q and K of y (bit: y >= 0, -0.0 included;
+ *           mu = mean |y| in fp32, pad bits 0)
+ *   v       [B,H,N,d] fp16: the V part of y
+ *   q, k    [B,H,N,d] fp16, or NULL: the Q and K parts of y themselves, for callers that also
+ *           need them (a training step's backward); NULL skips the write
+ * Sizes as for the other entry points (d a multiple of 8, 8..128; N <= 65536); B*N <= 2^40.
+ * Only fp16 is implemented (the fp16 MFMA).  x, w and the outputs must not overlap.
+ */
+int binattn_qkv_pack(const void* x, const void* w, const void* bias, int B, int N, int H, int d,
+                     uint32_t* q_bits, float* q_mu, uint32_t* k_bits, float* k_mu, void* v, void* q, void* k,
+                     void* stream);
+
+/*
  * binattn_forward -- BinaryAttention forward from packed Q/K and quantised V.
  * Passages: key design 1 (binary score with per-token scales), key design 2
  * (S_ij = mu_q mu_k s_i.t_j / sqrt(d) + b_ij), key design 3 (P quantised to u8
