@@ -362,6 +362,52 @@ def measure_backward(w, b, sets, calls: int):
                     "sign, P and V quantisers), fp32 outputs"}
 
 
+FP16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def measure_producer(w, W, b, dev, calls: int):
+    """The producer of the attention's inputs (binattn_qkv_pack: the QKV projection with Q and K
+    binarised in its epilogue) for workload w's shapes, on seeded projection inputs, against
+    the unfused route a caller would otherwise take: the library GEMM (torch.addmm, hipBLASLt)
+    writing Q, K, V in fp16, their permute to [B,H,N,d] and the separate packing pass."""
+    import torch
+    C = w.H * w.d
+    inp = W.projection_inputs(w.B, w.N, w.H, w.d, bias=True, seed=7)
+    x, wt, bias = (torch.from_numpy(inp[k]).to(dev) for k in ("x", "w", "bias"))
+    x2 = x.reshape(w.B * w.N, C)
+
+    def fused():
+        b.qkv_pack(x, wt, bias, w.H, w.d)
+
+    def gemm():
+        torch.addmm(bias, x2, wt.t())
+
+    def unfused():
+        y = torch.addmm(bias, x2, wt.t()).reshape(w.B, w.N, 3, w.H, w.d).permute(2, 0, 3, 1, 4).contiguous()
+        b.prepare(y[0], y[1], y[2])
+
+    def timed(f):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(calls):
+            f()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / calls
+
+    ms_f, ms_g, ms_u = timed(fused), timed(gemm), timed(unfused)
+    flops = 2.0 * w.B * w.N * C * 3 * C
+    tf = flops / (ms_f * 1e-3) / 1e12
+    return {"ms_per_call": ms_f, "calls": calls, "tflops": tf, "frac_of_fp16_mfma_peak": tf / FP16_MFMA_PEAK_TFLOPS,
+            "library_gemm_ms": ms_g, "library_gemm_tflops": flops / (ms_g * 1e-3) / 1e12,
+            "unfused_ms": ms_u, "speedup_vs_unfused": ms_u / ms_f,
+            "what": "x [B,N,H d] fp16 times w [3 H d, H d]^T plus bias -> Q and K sign words and mu, V fp16; "
+                    "unfused: library GEMM + permute + the separate packing and V quantisation"}
+
+
 def target_summary(w, m):
     """Per-workload record of a spec target shape: step and forward timings, effective
     TOPS and the roofline fractions recomputed from this run's own launch times."""
@@ -390,6 +436,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the QAT backward timing of the target shapes")
+    ap.add_argument("--no-producer", action="store_true",
+                    help="skip the timing of the QKV projection with Q/K binarised in its epilogue")
     ap.add_argument("--qk-ab", action="store_true",
                     help="only time the binary QK tile by its two methods (fp4 MFMA, VALU XOR+popcount) and exit")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -444,6 +492,12 @@ def main():
         targets[name] = target_summary(tw, tm)
         targets[name]["backward"] = bw
 
+    producer = None
+    if not args.no_producer:
+        producer = {name: measure_producer(W.BY_NAME[name], W, b, dev, max(1, min(args.steps, 20)))
+                    for name in [w.name] + [t for t in args.targets.split(",") if t and t != w.name]}
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp0, w, args.cpu_seconds)
@@ -476,6 +530,7 @@ def main():
         "step_hbm_gbs": step_bytes(w) / (step_ms * 1e-3) / 1e9,
         "roofline": m["roofline"],
         "targets": targets,
+        "producer": producer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))

@@ -16,8 +16,9 @@
 // tokens x all of the tile's features: 4 x NB accumulator tiles.  The x operand is private to a
 // wave, so it goes from global memory straight into MFMA operand registers, one k-step ahead;
 // the w operand is shared by the four waves and staged through LDS, double-buffered, one barrier
-// per 32-wide k-step.  Tiles are numbered so that an XCD runs consecutive ones: all feature runs
-// of one token block, whose x rows stay in that XCD's L2.
+// per 32-wide k-step.  Tiles are numbered so that an XCD runs consecutive ones, in bands of a few
+// token blocks whose x rows stay in that XCD's L2 while the feature runs go by, each w slab
+// serving the band's token blocks together.
 // Epilogue: the fp32 tile plus bias, rounded to fp16, goes to LDS as [token][feature]; then
 // each lane owns one token and, per head section, stores its d values (V, and Q or K when
 // asked) or packs them into sign words and mu (Q, K).
@@ -32,6 +33,7 @@ namespace {
 constexpr int kPM = 256;      // tokens per workgroup (64 per wave)
 constexpr int kPK = 32;       // k per step (one MFMA depth)
 constexpr int kPBP = kPK + 8;  // halfs per staged w row: 80-byte pitch
+constexpr int kBand = 8;      // token blocks per band of the tile order
 
 __device__ __forceinline__ v4f mfma_h(h8 a, h8 b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -53,8 +55,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int NBL = (BN * 4 + 255) / 256;  // 16-byte w chunks per thread and k-step
     __shared__ Lt L;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    // tile order: bands of kBand token blocks; inside a band the token block runs fastest, so
+    // the workgroups that run together on one XCD share their w slabs as well as their x rows
     const int tau = xcd_logical_block(blockIdx.x, a.nmt * a.nnt);
-    const int mt = tau / a.nnt, nt = tau - mt * a.nnt;
+    const int band = tau / (kBand * a.nnt), in_band = tau - band * kBand * a.nnt;
+    const int gm = min(kBand, a.nmt - band * kBand);
+    const int nt = in_band / gm, mt = band * kBand + (in_band - nt * gm);
     const int64_t m0 = (int64_t)mt * kPM;
     const int s0 = nt * a.hpt, nsec = min(a.hpt, a.nsec - s0), ncol = nsec * a.d;
     const int C = a.C, nk = (C + kPK - 1) / kPK;

@@ -176,6 +176,21 @@ def test_noalloc_validation(lib):
     assert _noalloc(lib, B=4, H=64, N=8192, d=128) == -2
 
 
+def _qkv(lib, **kw):
+    args = dict(x=_a(256), w=_a(512), bias=None, B=2, N=5, H=3, d=64, qb=_a(768), qm=_a(1024), kb=_a(1280),
+                km=_a(1536), v=_a(1792), q=None, k=None, stream=None)
+    args.update(kw)
+    return lib.binattn_qkv_pack(*args.values())
+
+
+def test_qkv_pack_validation(lib):
+    assert _qkv(lib, x=None) == -1 and _qkv(lib, w=None) == -1 and _qkv(lib, v=None) == -1
+    assert _qkv(lib, km=None) == -1
+    assert _qkv(lib, B=0) == -1 and _qkv(lib, N=-1) == -1
+    assert _qkv(lib, d=60) == -2 and _qkv(lib, d=136) == -2 and _qkv(lib, N=70000) == -2
+    assert _qkv(lib, x=_a(258)) == -3 and _qkv(lib, bias=_a(260)) == -3 and _qkv(lib, q=_a(262)) == -3
+
+
 def test_valid_arguments_without_a_device_report_enodevice(lib):
     import torch
     if torch.cuda.is_available():
@@ -184,6 +199,7 @@ def test_valid_arguments_without_a_device_report_enodevice(lib):
     assert _fwd(lib) == -4
     assert _fwd(lib, kind=2, bias=_a(4096), gh=16, gw=16) == -4
     assert _fwd(lib, kind=1, bias=_a(4096), ld=(1 << 26) - 8) == -4  # the largest fp16 dense-bias stride accepted
+    assert _qkv(lib) == -4 and _qkv(lib, bias=_a(2048), q=_a(2304), k=_a(2560)) == -4
     assert _noalloc(lib) == -4                    # two-launch shape, batch items fit the scratch
     assert _noalloc(lib, B=64, H=16, N=4096) == -4  # several chunks of batch items
     assert _noalloc(lib, N=197) == -4             # one kernel, no scratch

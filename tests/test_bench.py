@@ -56,6 +56,9 @@ def test_bench_prints_one_json_line():
     assert t["ms_per_step"] > 0 and t["fwd_ms_per_call"] > 0 and 0 < t["fwd_hbm_frac"] < 1
     bw = t["backward"]
     assert bw["ms_per_call"] > 0 and 0 < bw["frac_of_bf16_mfma_peak"] < 1
+    for name in ("highres_16k", "dit_xl2_256"):
+        p = res["producer"][name]
+        assert p["ms_per_call"] > 0 and 0 < p["frac_of_fp16_mfma_peak"] < 1 and p["unfused_ms"] > 0
     cpu = res["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
 
