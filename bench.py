@@ -95,10 +95,10 @@ def step_bytes(w) -> float:
 
 def sources_sha() -> str:
     """sha256 (first 16 hex digits) over the sources the forward-path kernels are built from
-    (every .hip and .h of csrc but the backward's), in name order."""
+    (every .hip and .h of csrc but the backward's and the producer's), in name order."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")) and name != "backward.hip":
+        if name.endswith((".hip", ".h")) and name not in ("backward.hip", "project.hip"):
             h.update(name.encode())
             h.update(open(os.path.join(CSRC, name), "rb").read())
     return h.hexdigest()[:16]
