@@ -15,7 +15,8 @@ namespace binattn {
 // Longer rows: key tiles streamed through a two-stage LDS ring, FlashAttention-2 running max.
 // DEFER: keep the PV sums in int32 across tiles and fold them into fp32 only when some row
 // max of the wave moves (long rows, where that becomes rare).  TF32: the relative-position
-// table is fp32 (else fp16).
+// table is fp32 (else fp16).  QX: the queries arrive unpacked (a.qx) and are packed in the
+// prologue (a separate instantiation, so that its launches are told apart in profiles).
 //
 // Relative position: the window staged for a tile holds the table rows its queries and keys
 // touch, from row dr_lo = ri_min - rjm + gh - 1 (ri_min: grid row of the block's first query,
@@ -23,7 +24,7 @@ namespace binattn {
 // (ri - ri_min + rjm - rj) row_len + ci - cj + gw - 1: a query part fixed per lane, a tile part
 // rjm row_len, and a key part rj row_len + cj that moves by a whole tile of keys per step --
 // all stepped from tile to tile without a division.
-template <int NT, int BIAS, bool DEFER, bool TF32>
+template <int NT, int BIAS, bool DEFER, bool TF32, bool QX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 4 && (BIAS == BK_RELPOS || BIAS == BK_NONE) ? 4 : 1))) void binattn_fwd_stream_kernel(FwdArgs a) {
     constexpr int TW = is_relpos(BIAS) ? kRelposWin : 4;
     typedef TileRegs<NT, TW> Regs;
@@ -54,7 +55,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 4 && 
 
     const int qw0 = q0 + wave * 16;
     const bool wave_live = qw0 < N;
-    const LaneQ lq = a.qx ? lane_query_raw<NT>(a, bh, qw0, g, n16) : lane_query<NT>(a, bh, qw0, g, n16);
+    LaneQ lq;
+    if constexpr (QX)
+        lq = lane_query_raw<NT>(a, bh, qw0, g, n16);
+    else
+        lq = lane_query<NT>(a, bh, qw0, g, n16);
 
     // relative position (see above): per lane the query part aq and the key part kk (kcol: the
     // key's grid column); uniform, the grid position (lrow, lcol) of the last key of the last
@@ -210,10 +215,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 4 && 
 
 template <int NT, int BK, bool TF32>
 inline void launch_stream(const FwdArgs& a, int ntiles, dim3 grid, hipStream_t s) {
-    if (ntiles >= kDeferTiles)
-        hipLaunchKernelGGL((binattn_fwd_stream_kernel<NT, BK, true, TF32>), grid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((binattn_fwd_stream_kernel<NT, BK, false, TF32>), grid, dim3(256), 0, s, a);
+    const bool defer = ntiles >= kDeferTiles;
+    if (a.qx) {
+        if (defer)
+            hipLaunchKernelGGL((binattn_fwd_stream_kernel<NT, BK, true, TF32, true>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((binattn_fwd_stream_kernel<NT, BK, false, TF32, true>), grid, dim3(256), 0, s, a);
+    } else if (defer) {
+        hipLaunchKernelGGL((binattn_fwd_stream_kernel<NT, BK, true, TF32, false>), grid, dim3(256), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((binattn_fwd_stream_kernel<NT, BK, false, TF32, false>), grid, dim3(256), 0, s, a);
+    }
 }
 
 // The kernel launch_fwd_bk picks: the head-resident kernel for rows of <= 4 tiles (relative
