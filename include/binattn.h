@@ -122,7 +122,9 @@ int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t
  *   q, k    [B,H,N,d] fp16, or NULL: the Q and K parts of y themselves, for callers that also
  *           need them (a training step's backward); NULL skips the write
  * Sizes as for the other entry points (d a multiple of 8, 8..128; N <= 65536); B*N <= 2^40.
- * Only fp16 is implemented (the fp16 MFMA).  x, w and the outputs must not overlap.
+ * Only fp16 is implemented (the fp16 MFMA).  x, w and bias must hold finite values (the
+ * kernel may multiply entries of x by zero weights past the end of a row).  x, w and the
+ * outputs must not overlap.
  */
 int binattn_qkv_pack(const void* x, const void* w, const void* bias, int B, int N, int H, int d,
                      uint32_t* q_bits, float* q_mu, uint32_t* k_bits, float* k_mu, void* v, void* q, void* k,
