@@ -172,3 +172,38 @@ def test_qkv_pack_full_size_sampled_tokens(name):
     check_part("v", tr(rv), tr(mv), C, d, vals=v)
     check_part("q", tr(rq), tr(mq), C, d, bits=qb, mu=qm)
     check_part("k", tr(rk), tr(mk), C, d, bits=kb, mu=km)
+
+
+@pytest.mark.parametrize("case", [(2, 256, 4, 72, "relpos", (16, 16)), (1, 197, 3, 64, "dense", ())],
+                         ids=["dit-like-relpos", "deit-like-dense"])
+def test_producer_pipeline_against_the_oracle_attention(case):
+    """End to end: the producer's outputs through binattn_quant_v and binattn_forward give the
+    oracle's attention of the oracle's projection (its fp16-rounded Q, K, V), to the forward's
+    own bar: max |O - O_ref| <= 1e-2 max|V|, mean <= 1e-3 max|V|, relative Frobenius <= 5e-2."""
+    from diffusion_transformers_amd import binding as b
+    B, N, H, d, bias_kind, grid = case
+    _say(f"producer pipeline {case}")
+    inp = W.projection_inputs(B, N, H, d, bias=True, seed=11)
+    rng = np.random.default_rng(12)
+    if bias_kind == "relpos":
+        gh, gw = grid
+        table = (rng.standard_normal((H, (2 * gh - 1) * (2 * gw - 1))) * 0.02).astype(np.float16)
+        bt, kind, okind = _t(table), b.BIAS_RELPOS, oracle.BIAS_RELPOS
+        obias = table
+    else:
+        dense = (rng.standard_normal((H, N, N)) * 0.02).astype(np.float16)
+        bt, kind, okind = b.aligned_dense_bias(_t(dense)), b.BIAS_DENSE, oracle.BIAS_DENSE
+        obias = dense
+    qb, qm, kb, km, v = b.qkv_pack(_t(inp["x"]), _t(inp["w"]), _t(inp["bias"]), H, d)
+    vq, va = b.quant_v(v)
+    o = b.forward(qb, qm, kb, km, vq, va, d, bt, kind, grid or None, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rq, rk, rv, *_ = oracle.qkv_project(inp["x"], inp["w"], inp["bias"], H, d)
+    f16 = lambda a: a.astype(np.float16).astype(np.float64)
+    ref = oracle.forward(f16(rq), f16(rk), f16(rv), obias, okind, grid or None)
+    vmax = float(np.abs(f16(rv)).max())
+    err = np.abs(o.cpu().numpy().astype(np.float64) - ref)
+    mx, mn = err.max() / vmax, err.mean() / vmax
+    fro = np.linalg.norm(err) / np.linalg.norm(ref)
+    _say(f"  O err: max {mx:.3e} mean {mn:.3e} relfro {fro:.3e} (x max|V|)")
+    assert mx <= 1e-2 and mn <= 1e-3 and fro <= 5e-2, (mx, mn, fro)
