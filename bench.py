@@ -409,7 +409,7 @@ def measure_producer(w, W, b, dev, calls: int):
 
 
 def target_summary(w, m):
-    """Per-workload record of a spec target shape: step and forward timings, effective
+    """Per-workload record of a target shape (DeiT-B/384, DiT-XL/2): step and forward timings, effective
     TOPS and the roofline fractions recomputed from this run's own launch times."""
     ops = w.ops()
     fwd_s = m["fwd_ms"] * 1e-3
