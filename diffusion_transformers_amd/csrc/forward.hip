@@ -35,7 +35,8 @@
 //    v_cvt_pk_u8_f32; the row sum is taken over the unquantised p.
 //  * PV with signed int8 MFMA: sum P^ V^ = sum (P^-128) V^ + 128 sum V^.  Short rows take
 //    the column sums once per head while staging and start the accumulator there; streamed
-//    rows add them per tile as two more MFMAs (B = 64) into the same accumulator.
+//    rows use the bytes 127 - P^ (also int8 for every P^) and accumulate the negated sum,
+//    sum (127 - P^) V^ - 127 sum V^, with one constant MFMA (B = -127) per channel tile.
 //  * Epilogue: O = acc * s_c / sum(p), s_c = a_c / 127 from the channel absmax a_c.
 #include "stream.h"
 

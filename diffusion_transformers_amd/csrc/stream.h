@@ -166,25 +166,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 4 && 
             for (int ct = 0; ct < NT; ++ct) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    accf[ct][r] = DEFER ? (accf[ct][r] + (float)acci[ct][r]) * alpha : accf[ct][r] * alpha;
+                    accf[ct][r] = DEFER ? (accf[ct][r] - (float)acci[ct][r]) * alpha : accf[ct][r] * alpha;
                 if (DEFER) acci[ct] = v4i{0, 0, 0, 0};
             }
         }
         mrun = mnew;
-        const v4i pw = tile_probs(S, kLog2_255 - mnew * kLog2e, lsum);
+        // PV on the signed int8 MFMA with the bytes 127 - P^ and one constant MFMA (B = -127):
+        // sum_j (127 - P^_j) V^_j - 127 sum_j V^_j = -sum_j P^_j V^_j, so the accumulators hold
+        // the negated sums (one constant MFMA per channel tile instead of two for +128 sum V^)
+        const v4i pw = tile_probs<0x7F7F7F7Fu>(S, kLog2_255 - mnew * kLog2e, lsum);
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
             const v4i vop = *reinterpret_cast<const v4i*>(&s.v[(ct * kWave + lane) * 4]);
             if (DEFER) {
-                v4i x = mfma_i8(vop, pw, acci[ct]);
-                x = mfma_i8(vop, kC64, x);
-                acci[ct] = mfma_i8(vop, kC64, x);
+                acci[ct] = mfma_i8(vop, kCm127, mfma_i8(vop, pw, acci[ct]));
             } else {
-                v4i x = mfma_i8(vop, pw, v4i{0, 0, 0, 0});
-                x = mfma_i8(vop, kC64, x);
-                x = mfma_i8(vop, kC64, x);
+                const v4i x = mfma_i8(vop, kCm127, mfma_i8(vop, pw, v4i{0, 0, 0, 0}));
 #pragma unroll
-                for (int r = 0; r < 4; ++r) accf[ct][r] += (float)x[r];
+                for (int r = 0; r < 4; ++r) accf[ct][r] -= (float)x[r];
             }
         }
     };
@@ -208,7 +207,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 4 && 
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) accf[ct][r] += (float)acci[ct][r];
+            for (int r = 0; r < 4; ++r) accf[ct][r] -= (float)acci[ct][r];
     }
     store_out<NT>(a, bh, lq, sScale, accf, rows4_sum(lsum));
 }

@@ -480,8 +480,10 @@ __device__ __forceinline__ void tile_scores(const uint32_t* __restrict__ sk, con
     }
 }
 
-// Quantised probabilities of one tile as the B operand of the PV MFMA (bytes P^ - 128) and
-// their unquantised sum: p = 255 exp(S - m) with negm = log2(255) - m log2(e).
+// Quantised probabilities of one tile as the B operand of the PV MFMA and their unquantised sum:
+// p = 255 exp(S - m) with negm = log2(255) - m log2(e).  Bytes P^ ^ FLIP as int8: FLIP = 0x80
+// gives P^ - 128; FLIP = 0x7F gives 127 - P^ (for every P^ in 0..255).
+template <uint32_t FLIP = 0x80808080u>
 __device__ __forceinline__ v4i tile_probs(const float (&S)[16], float negm, float& lsum) {
     v4i pw;
 #pragma unroll
@@ -493,7 +495,7 @@ __device__ __forceinline__ v4i tile_probs(const float (&S)[16], float negm, floa
             lsum += p;
             word = __builtin_amdgcn_cvt_pk_u8_f32(p, r, word);
         }
-        pw[t] = (int)(word ^ 0x80808080u);
+        pw[t] = (int)(word ^ FLIP);
     }
     return pw;
 }
@@ -537,7 +539,7 @@ __device__ __forceinline__ v4i tile_probs4(const float (&S)[4], float negm, floa
     return v4i{(int)(word ^ 0x80808080u), 0, 0, 0};
 }
 
-constexpr v4i kC64 = v4i{0x40404040, 0x40404040, 0x40404040, 0x40404040};
+constexpr v4i kCm127 = v4i{(int)0x81818181, (int)0x81818181, (int)0x81818181, (int)0x81818181};  // int8 -127
 
 // Dequantise, normalise and store the lane's 4*NT channels of its query.
 template <int NT>
