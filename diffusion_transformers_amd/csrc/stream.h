@@ -158,8 +158,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 4 && 
             wrun = reinterpret_cast<const float*>(twb + aq + 4 * rjm * row_len);
         float S[16], mloc = -INFINITY;
         tile_scores<NT, BIAS>(s.k, s.mu, lq, bcur, wrun, TAIL, N - jg, S, mloc, s.kk + 16 * g);
-        const float mnew = fmaxf(mrun, rows4_max(mloc));
-        if (__any(mnew > mrun)) {
+        // The row max moves only if some lane's own max exceeds it: the cross-lane reduction and
+        // the fold run only then (a row whose max stays gets alpha = 1).
+        if (__any(mloc > mrun)) {
+            const float mnew = fmaxf(mrun, rows4_max(mloc));
             const float alpha = fast_exp2((mrun - mnew) * kLog2e);  // 0 on the first tile
             lsum *= alpha;
 #pragma unroll
@@ -169,8 +171,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 4 && 
                     accf[ct][r] = DEFER ? (accf[ct][r] - (float)acci[ct][r]) * alpha : accf[ct][r] * alpha;
                 if (DEFER) acci[ct] = v4i{0, 0, 0, 0};
             }
+            mrun = mnew;
         }
-        mrun = mnew;
+        const float mnew = mrun;
         // PV on the signed int8 MFMA with the bytes 127 - P^ and one constant MFMA (B = -127):
         // sum_j (127 - P^_j) V^_j - 127 sum_j V^_j = -sum_j P^_j V^_j, so the accumulators hold
         // the negated sums (one constant MFMA per channel tile instead of two for +128 sum V^)
