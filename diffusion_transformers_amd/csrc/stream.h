@@ -55,6 +55,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 4 && 
 
     const int qw0 = q0 + wave * 16;
     const bool wave_live = qw0 < N;
+    const int vrow = lane ^ ((lane >> 3) & 6);  // the lane's V^ operand row as store_tile<.., SWZ> stores it
     LaneQ lq;
     if constexpr (QX)
         lq = lane_query_raw<NT>(a, bh, qw0, g, n16);
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 4 && 
     auto step = [&](int tile, BiasRegs<BIAS>& bcur, BiasRegs<BIAS>& bnext, auto tail_c) {
         constexpr bool TAIL = decltype(tail_c)::value;
         Lds& s = lds[tile & 1];
-        store_tile<NT, TW, false, TF32>(regs, s, d);
+        store_tile<NT, TW, false, TF32, true>(regs, s, d);
         if (BIAS == BK_RELPOS_G && tid < kBC) {
             s.kk[tid] = -4 * (tile * kBC + tid < N ? tr * row_len + tc : klast);
             tc += dcol;  // key tid of the next tile
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 4 && 
         if (BIAS == BK_RELPOS_G)  // the keys' parts are gathered from s.kk
             wrun = reinterpret_cast<const float*>(twb + aq + 4 * rjm * row_len);
         float S[16], mloc = -INFINITY;
-        tile_scores<NT, BIAS>(s.k, s.mu, lq, bcur, wrun, TAIL, N - jg, S, mloc, s.kk + 16 * g);
+        tile_scores<NT, BIAS, true>(s.k, s.mu, lq, bcur, wrun, TAIL, N - jg, S, mloc, s.kk + 16 * g);
         // The row max moves only if some lane's own max exceeds it: the cross-lane reduction and
         // the fold run only then (a row whose max stays gets alpha = 1).
         if (__any(mloc > mrun)) {
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 4 && 
         const v4i pw = tile_probs<0x7F7F7F7Fu>(S, kLog2_255 - mnew * kLog2e, lsum);
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
-            const v4i vop = *reinterpret_cast<const v4i*>(&s.v[(ct * kWave + lane) * 4]);
+            const v4i vop = *reinterpret_cast<const v4i*>(&s.v[(ct * kWave + vrow) * 4]);
             if (DEFER) {
                 acci[ct] = mfma_i8(vop, kCm127, mfma_i8(vop, pw, acci[ct]));
             } else {

@@ -174,7 +174,11 @@ __device__ __forceinline__ void load_tile(TileRegs<NT, TW>& r, const FwdArgs& a,
 // narrow score tile: key j is K operand row j of MFMA 0, and the V^ dword of keys 4q..4q+3 is the
 // first dword of operand lane (slot, q) -- those lanes' other bytes meet zero P^ bytes.
 // TF32: the relative-position table (TW >= 256) is fp32, else fp16.
-template <int NT, int TW, bool NARROW = false, bool TF32 = false>
+// SWZ (streamed tiles, staged once per tile by the whole workgroup): the 16-byte operand rows are
+// stored with their index XOR-swizzled within each aligned group of eight -- K rows of sign word w
+// at row ^ 4 (w & 1), V^ rows of key chunk gg at row ^ 2 gg -- so that every eight lanes of a
+// staging store hit eight different bank groups (the readers apply the same XOR to their rows).
+template <int NT, int TW, bool NARROW = false, bool TF32 = false, bool SWZ = false>
 __device__ __forceinline__ void store_tile(const TileRegs<NT, TW>& r, TileLds<NT, TW>& s, int d) {
     typedef TileRegs<NT, TW> R;
     const int tid = threadIdx.x;
@@ -190,6 +194,7 @@ __device__ __forceinline__ void store_tile(const TileRegs<NT, TW>& r, TileLds<NT
             unpack_bits32_f4(word, o);
             int t = 0, m = j;
             if (!NARROW) m = key_slot(j, t);
+            if (SWZ) m ^= 4 * (w & 1);
             *reinterpret_cast<uint4*>(&s.k[((t * R::W + w) * 16 + m) * 4]) = make_uint4(o[0], o[1], o[2], o[3]);
         }
     }
@@ -201,7 +206,7 @@ __device__ __forceinline__ void store_tile(const TileRegs<NT, TW>& r, TileLds<NT
             int ct;
             const int m = chan_slot<NT>(c, ct);
             if (!NARROW) {
-                *reinterpret_cast<uint4*>(&s.v[(ct * kWave + m + 16 * gg) * 4]) = r.v[i];
+                *reinterpret_cast<uint4*>(&s.v[(ct * kWave + ((m + 16 * gg) ^ (SWZ ? 2 * gg : 0))) * 4]) = r.v[i];
             } else if (gg == 0) {
                 const uint4 x = r.v[i];
                 s.v[(ct * kWave + m) * 4] = x.x;
@@ -422,14 +427,15 @@ __device__ __forceinline__ LaneQ lane_query_raw(const FwdArgs& a, int bh, int qw
 // is wrun[15 - k]: a grid row holds whole runs, and the column offset falls as the key rises).
 // RELPOS_G: wrun is the window entry of the lane's query part, and kk (LDS) holds the byte
 // offsets from it of the entries of keys jg .. jg + 15 (any grid width).
-template <int NT, int BIAS>
+template <int NT, int BIAS, bool SWZ = false>
 __device__ __forceinline__ void tile_scores(const uint32_t* __restrict__ sk, const float* __restrict__ smu,
                                             const LaneQ& lq, const BiasRegs<BIAS>& bias, const float* wrun,
                                             bool tail, int nvalid, float (&S)[16], float& mloc,
                                             const int* kk = nullptr) {
     constexpr int W = (NT + 1) / 2;
     const int lane = threadIdx.x & 63, g = lane >> 4, m16 = lane & 15;
-    const int koff = ((g < W ? g : 0) * 16 + m16) * 4;  // lane-constant
+    const int gw = g < W ? g : 0;
+    const int koff = (gw * 16 + (SWZ ? m16 ^ (4 * (gw & 1)) : m16)) * 4;  // lane-constant
     v4f D[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) D[t] = mfma_f4(*reinterpret_cast<const v4i*>(&sk[t * W * 64 + koff]), lq.qop, lq.dseed);
