@@ -345,6 +345,49 @@ def test_forward_closed_forms():
     np.testing.assert_allclose(o2, V.astype(np.float64)[:, :, jstar, :], rtol=1e-5, atol=1e-3)
 
 
+def test_streamed_rows_closed_forms():
+    """Streamed rows (32 and 16 key tiles, int32 accumulation across tiles) against closed forms:
+    identical keys give every P^ = 255 and O = the column mean of V; a one-hot +30 dense bias
+    selects one V row, its tile raising the running max by about 30 (a fold with a vanishing
+    rescale of everything before it)."""
+    _say("streamed closed forms")
+    B, H, N, d = 1, 2, 2048, 64
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((B, H, N, d)).astype(np.float16)
+    k = np.repeat(rng.standard_normal((B, H, 1, d)), N, axis=2).astype(np.float16)
+    V = rng.integers(-127, 128, size=(B, H, N, d)).astype(np.float16)
+    V[:, :, 0, :] = 127  # channel max 127: V^ = V and s = 1
+    inp = dict(q=q, k=k, v=V, bias=None, workload=W.Workload("c", B, H, N, d, "f16", "none"))
+    o = gpu_pipeline(inp, out_dtype=torch.float32)["o"].cpu().numpy()
+    np.testing.assert_allclose(o, np.broadcast_to(V.astype(np.float64).mean(axis=2, keepdims=True), o.shape),
+                               rtol=2e-6, atol=2e-4)
+    N2 = 1024
+    bias = np.zeros((H, N2, N2), dtype=np.float32)
+    jstar = (np.arange(N2) * 37 + 11) % N2
+    bias[:, np.arange(N2), jstar] = 30.0
+    k2 = rng.standard_normal((B, H, N2, d)).astype(np.float16)
+    V2 = V[:, :, :N2]
+    inp2 = dict(q=q[:, :, :N2], k=k2, v=V2, bias=bias.astype(np.float16),
+                workload=W.Workload("c", B, H, N2, d, "f16", "dense"))
+    o2 = gpu_pipeline(inp2, out_dtype=torch.float32)["o"].cpu().numpy()
+    np.testing.assert_allclose(o2, V2.astype(np.float64)[:, :, jstar, :], rtol=1e-5, atol=1e-3)
+
+
+@pytest.mark.parametrize("slope", [0.06, -0.06])
+def test_streamed_rows_running_max_every_tile(slope):
+    """A dense bias that rises along the keys moves every row's running max at every one of the
+    32 key tiles (a fold per tile); one that falls moves it only on the first tile.  Both against
+    the oracle at the forward's bar."""
+    _say(f"streamed running max, slope {slope}")
+    B, H, N, d = 1, 2, 2048, 64
+    inp = W.custom(B, H, N, d, "f16", "dense", (), seed=29)
+    j = np.arange(N, dtype=np.float32)
+    inp["bias"] = (inp["bias"].astype(np.float32) + slope * j[None, None, :]).astype(np.float16)
+    g = gpu_pipeline(inp)
+    ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["bias"], oracle.BIAS_DENSE)
+    assert_o(g["o"].cpu().numpy(), ref, float(np.abs(inp["v"].astype(np.float64)).max()), f"slope {slope}")
+
+
 def test_forward_is_deterministic():
     inp = W.custom(4, 3, 577, 64, "f16", "dense", seed=5)
     a = gpu_pipeline(inp)["o"].cpu().numpy()
