@@ -37,8 +37,10 @@
 //  * Every staging step issues all of a tile's global loads before its first LDS store (a loop of
 //    load, wait, store pays one memory latency per iteration, and the kernels are bound by them).
 //  * bw_rows_kernel<STATS = false> (a workgroup per 64 queries): per key tile the scores, P, dP,
-//    dS, dQ and the bias gradient (dense: each batch item's dS stored and summed over the batch
-//    afterwards; relative position: the table's entries accumulated in LDS).
+//    dS, dQ and the bias gradient (dense: each batch item's dS stored in bf16 and summed over the
+//    batch in fp32 afterwards -- a sum of independent terms, so the rounding (relative 2^-9 per
+//    term) does not cancel into the result the way it would inside dQ's row sums; relative
+//    position: the table's entries accumulated in LDS).
 //  * bw_k_kernel (a workgroup per 64 keys): per query tile the transposed score tile (queries as
 //    MFMA rows, the lane's key as the column), P and P^, dP, dS, then dV and dK.
 #include <utility>
@@ -84,7 +86,7 @@ struct BwArgs {
     float* dk;
     float* dv;
     float* db;       // dense [H,N,N] or table [H,(2gh-1)(2gw-1)], fp32; may be null
-    float* dsb;      // dense bias gradient: dS of every batch item [B][H][N][Np], summed over B afterwards
+    __bf16* dsb;     // dense bias gradient: dS of every batch item [B][H][N][Np] in bf16, summed over B afterwards
     float* dtp;      // table gradient of each query-block workgroup [B H nqb][kTabMax] when the table has
                      // at most kTabMax entries (else null: the entries go to db by atomics per key tile)
 };
@@ -133,18 +135,29 @@ __device__ __forceinline__ void pack_split(const float (&x)[16], int s2, bf8& hi
     }
 }
 
-// db[h][i][j] = sum over b of dS[b][h][i][j], in batch order (deterministic).
-__global__ __launch_bounds__(256) void bw_dbias_kernel(const float* __restrict__ dsb, float* __restrict__ db, int B,
+// db[h][i][j] = sum over b of dS[b][h][i][j] (stored in bf16), in fp32 and batch order
+// (deterministic).  A thread takes four consecutive keys (one 8-byte load per batch item; the
+// stored rows are padded to Np keys with zeros).
+__global__ __launch_bounds__(256) void bw_dbias_kernel(const __bf16* __restrict__ dsb, float* __restrict__ db, int B,
                                                        int H, int N, int Np) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int nq = Np / 4;
     const int64_t hn = (int64_t)H * N;
-    if (e >= hn * N) return;
-    const int64_t r = e / N, j = e - r * N;  // r = h N + i
+    if (e >= hn * nq) return;
+    const int64_t r = e / nq;  // r = h N + i
+    const int j = 4 * (int)(e - r * nq);
     const int64_t stride = hn * Np;
-    const float* p = dsb + r * Np + j;
-    float acc = 0.0f;
-    for (int b = 0; b < B; ++b) acc += p[b * stride];
-    db[e] = acc;
+    const __bf16* p = dsb + r * Np + j;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int b = 0; b < B; ++b) {
+        typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+        const bf4 x = *reinterpret_cast<const bf4*>(p + b * stride);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] += (float)x[t];
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        if (j + t < N) db[r * N + j + t] = acc[t];
 }
 
 // Table gradient: db[h][e] = sum of the partial tables of the query-block workgroups of head h
@@ -614,10 +627,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
         // the bias gradient: dS of this batch item stored whole (dense; summed over the batch by
         // bw_dbias_kernel), or into the table entries
         if (DENSE && a.db && lq.live) {
-            float* drow = a.dsb + ((int64_t)bh * N + i) * a.Np + jg;  // keys past N hold 0
+            __bf16* drow = a.dsb + ((int64_t)bh * N + i) * a.Np + jg;  // keys past N hold 0
+            alignas(16) __bf16 hv[16];  // rounded to bf16 (relative 2^-9): halves the bytes stored and summed
 #pragma unroll
-            for (int k = 0; k < 16; k += 4)
-                *reinterpret_cast<float4*>(drow + k) = make_float4(dS[k], dS[k + 1], dS[k + 2], dS[k + 3]);
+            for (int k = 0; k < 16; ++k) hv[k] = (__bf16)dS[k];
+#pragma unroll
+            for (int k = 0; k < 16; k += 8)
+                *reinterpret_cast<uint4*>(drow + k) = *reinterpret_cast<const uint4*>(hv + k);
         }
         if (BIAS == BK_RELPOS_G && a.db && !RUN16) {
             if (lq.live) {  // (keys past N add their dS = 0 at key N - 1's entry: no per-key test)
@@ -935,7 +951,7 @@ static void launch_bw_nt(const BwArgs& a, int bk, hipStream_t s) {
 
 int64_t backward_arrays_bytes(int B, int H, int N, int d, int bias_kind) {
     const int64_t Np = ((int64_t)N + kBC - 1) / kBC * kBC, CP = 32 * ((d + 31) / 32), BH = (int64_t)B * H;
-    const int64_t extra = bias_kind == 1 ? BH * N * Np * 4 : (bias_kind == 2 ? BH * (Np / kBR) * kTabMax * 4 : 0);
+    const int64_t extra = bias_kind == 1 ? BH * N * Np * 2 : (bias_kind == 2 ? BH * (Np / kBR) * kTabMax * 4 : 0);
     return 7 * BH * Np * CP * 2 + 3 * BH * N * 4 + extra + 11 * 256;
 }
 
@@ -961,7 +977,7 @@ hipError_t launch_backward(const BwLaunch& L, hipStream_t s) {
     a.m = reinterpret_cast<float*>(p); p += vec;
     a.l = reinterpret_cast<float*>(p); p += vec;
     a.delta = reinterpret_cast<float*>(p); p += vec;
-    a.dsb = L.bias_kind == 1 ? reinterpret_cast<float*>(p) : nullptr;
+    a.dsb = L.bias_kind == 1 ? reinterpret_cast<__bf16*>(p) : nullptr;
     const int64_t tsz = (int64_t)(2 * L.gh - 1) * (2 * L.gw - 1);
     a.dtp = L.bias_kind == 2 && tsz <= kTabMax ? reinterpret_cast<float*>(p) : nullptr;
     a.dq = L.dq; a.dk = L.dk; a.dv = L.dv; a.db = L.db;
@@ -977,8 +993,8 @@ hipError_t launch_backward(const BwLaunch& L, hipStream_t s) {
         default: launch_bw_nt<8>(a, bk, s); break;
     }
     if (L.db && L.bias_kind == 1)
-        hipLaunchKernelGGL(bw_dbias_kernel, dim3((unsigned)((L.db_count + 255) / 256)), dim3(256), 0, s, a.dsb, L.db,
-                           L.B, L.H, L.N, a.Np);
+        hipLaunchKernelGGL(bw_dbias_kernel, dim3((unsigned)(((int64_t)L.H * L.N * (a.Np / 4) + 255) / 256)), dim3(256),
+                           0, s, a.dsb, L.db, L.B, L.H, L.N, a.Np);
     if (L.db && a.dtp)
         hipLaunchKernelGGL(bw_dtable_kernel, dim3((unsigned)((L.db_count + 63) / 64)), dim3(256), 0, s, a.dtp, L.db,
                            L.B, L.H, a.Np / kBR, (int)tsz);
