@@ -427,30 +427,31 @@ struct DenseTile {
 };
 
 // ---------------------------------------------------------------------------------------------
-template <int NT, int BIAS>
+// (ST: the row statistics pass, which stages only the score operands)
+template <int NT, int BIAS, bool ST = false>
 struct alignas(16) BwQLds {
     static constexpr int W = (NT + 1) / 2, CP = 32 * W, RP = CP + 8, TPK = kBC + 8;
     uint32_t k[4 * W * 16 * 4];
     float mu[kBC];
-    __bf16 vh[kBC * RP];  // V^ of the tile's keys [key][channel]
-    __bf16 sk[CP * TPK];  // sign(k) [channel][key]
+    __bf16 vh[ST ? 8 : kBC * RP];  // V^ of the tile's keys [key][channel]
+    __bf16 sk[ST ? 8 : CP * TPK];  // sign(k) [channel][key]
     float tw[BIAS == BK_RELPOS_G ? kRelposWin : 4];
-    float dwin[BIAS == BK_RELPOS_G ? kTabMax : 4];  // the whole table's gradient, or one tile's window
+    float dwin[BIAS == BK_RELPOS_G && !ST ? kTabMax : 4];  // the whole table's gradient, or one tile's window
     int kk[kBC];
 };
 
-// A workgroup per 64 queries.  STATS: the row max, row sum and Delta of its queries.  Otherwise:
-// dS, the bias gradient and dq, from the row statistics and the prepared operand arrays.
-// (LDS allows at most 3 workgroups per CU: registers up to that occupancy hold a tile's staged
-// loads without spilling.)
+// A workgroup per 64 queries.  STATS: the row max, row sum and Delta of its queries (a few KB of
+// LDS, up to 8 waves per SIMD).  Otherwise: dS, the bias gradient and dq, from the row
+// statistics and the prepared operand arrays (LDS allows at most 3 workgroups per CU: registers
+// up to that occupancy hold a tile's staged loads without spilling).
 // RUN16 (relative position on a grid whose width is a multiple of 16, d > 32): a wave's 16
 // queries lie in one grid row and so do the 16 keys of a lane group, so the 256 dS values of a
 // (wave, group) pair fall on the 31 table entries of their diagonals ci - cj: they are summed
 // along those diagonals in LDS first (the V^ and sign tiles' space, free after dQ), and 2 LDS
 // atomics per lane replace 16.
 template <int NT, int BIAS, bool STATS, bool RUN16 = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) void bw_rows_kernel(BwArgs a) {
-    typedef BwQLds<NT, BIAS> Lt;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, STATS ? 8 : 3))) void bw_rows_kernel(BwArgs a) {
+    typedef BwQLds<NT, BIAS, STATS> Lt;
     constexpr int W = Lt::W, CP = Lt::CP, RP = Lt::RP, TPK = Lt::TPK, NCB = 2 * W;
     static_assert(!RUN16 || 2 * (kBC * RP + CP * TPK) >= 4 * 4 * 16 * 17 * 4, "diagonal scratch fits the two tiles");
     constexpr bool DENSE = BIAS == BK_DENSE_F16 || BIAS == BK_DENSE_F32;
@@ -539,13 +540,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
     };
 
     if (STATS) {  // exact row max and row sum (online over the tiles), Delta
+        // tile t + 1's operands are loaded into registers before tile t's scores and stored to
+        // LDS after them
+        SignTile<W> kst;
+        float kmu = 0.0f;
+        WinTile win;
+        auto load_ops = [&](int j0) {
+            kst.load(a.kbits + (int64_t)bh * N * W, j0, N);
+            kmu = tid < kBC && j0 + tid < N ? a.kmu[(int64_t)bh * N + j0 + tid] : 0.0f;
+            if (BIAS == BK_RELPOS_G) win.load(a, table, q0, j0);
+        };
+        auto store_ops = [&](int j0) {
+            kst.store_fp4(L.k, d);
+            if (tid < kBC) L.mu[tid] = kmu;
+            if (BIAS == BK_RELPOS_G) {
+                win.store(L.tw);
+                if (tid < kBC) {
+                    const int j = min(j0 + tid, N - 1);  // keys past N are masked: any in-window entry
+                    const int rj = j / gw;
+                    L.kk[tid] = -4 * (rj * row_len + j - rj * gw);
+                }
+            }
+        };
         float mrun = -INFINITY, lpart = 0.0f;
         BiasRegs<BIAS> bcur, bnext;
         fetch_bias(0, bcur);
+        load_ops(0);
         for (int t = 0; t < ntiles; ++t) {
-            fetch_bias((t + 1) * kBC, bnext);
-            stage(t * kBC);
+            store_ops(t * kBC);
             __syncthreads();
+            if (t + 1 < ntiles) load_ops((t + 1) * kBC);
+            fetch_bias((t + 1) * kBC, bnext);
             float S[16], mloc = -INFINITY;
             scores(t * kBC, S, mloc, bcur);
             bcur = bnext;
@@ -558,8 +583,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) voi
             __syncthreads();
         }
         const float lrow = rows4_sum(lpart);
-        float dpart = 0.0f;  // Delta = dO . O, the lane's share: channels g, g + 4, ...
-        for (int c = g; c < d; c += 4) dpart += ld_any(a.dout, tok * d + c, a.g_f32) * ld_any(a.o, tok * d + c, a.g_f32);
+        // Delta = dO . O, the lane's share: 16-byte chunks g, g + 4, ... of the two rows (d is a
+        // multiple of 8 and the rows 16-byte aligned)
+        float dpart = 0.0f;
+        if (a.g_f32) {
+            const float4* pd = reinterpret_cast<const float4*>((const float*)a.dout + tok * d);
+            const float4* po = reinterpret_cast<const float4*>((const float*)a.o + tok * d);
+            for (int c = g; 4 * c < d; c += 4) {
+                const float4 x = pd[c], y = po[c];
+                dpart += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+            }
+        } else {
+            const h8* pd = reinterpret_cast<const h8*>((const _Float16*)a.dout + tok * d);
+            const h8* po = reinterpret_cast<const h8*>((const _Float16*)a.o + tok * d);
+            for (int c = g; 8 * c < d; c += 4) {
+                const h8 x = pd[c], y = po[c];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dpart += (float)x[e] * (float)y[e];
+            }
+        }
         const float delta = rows4_sum(dpart);
         if (lq.live && g == 0) {
             a.m[tok] = mrun;
