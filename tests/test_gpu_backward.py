@@ -84,6 +84,10 @@ CASES = [
     (1, 1, 300, 128, "f16", "none", (), 0.0),
     (1, 2, 100, 40, "f32", "dense", (), 0.0),
     (1, 1, 577, 64, "f16", "dense", (), 0.0),
+    # many key tiles for the row statistics (their next tile loaded during the current one) and
+    # Delta from whole 16-byte chunks of dO and O, fp32 over d = 128
+    (1, 2, 1100, 64, "f16", "dense", (), 0.0),
+    (1, 1, 1500, 128, "f32", "none", (), 0.0),
     (1, 1, 1024, 64, "f16", "relpos", (8, 128), 0.0),
     # grid widths that are multiples of 16 take the diagonal sums of the table gradient: a table
     # larger than the kernel's LDS copy (31 x 255 entries: per-tile windows) and d = 32 (no room
