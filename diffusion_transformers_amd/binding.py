@@ -43,6 +43,8 @@ def _load():
     lib.binattn_pack_qk.restype = i32
     lib.binattn_quant_v.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.binattn_quant_v.restype = i32
+    lib.binattn_vq_canonical.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+    lib.binattn_vq_canonical.restype = i32
     lib.binattn_forward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, vp, i32, vp]
     lib.binattn_forward.restype = i32
     lib.binattn_scores_i32.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
@@ -75,7 +77,7 @@ def _load():
 
 _lib = _load()
 EXPORTS = ["binattn_abi_version", "binattn_strerror", "binattn_words", "binattn_vq_ld", "binattn_pack_qk",
-           "binattn_quant_v", "binattn_forward", "binattn_scores_i32", "binattn_qk_rowstats",
+           "binattn_quant_v", "binattn_vq_canonical", "binattn_forward", "binattn_scores_i32", "binattn_qk_rowstats",
            "binattn_prepare", "binattn_attention_workspace", "binattn_attention", "binattn_attention_one_kernel",
            "binattn_keep_plan", "binattn_attention_noalloc", "binattn_backward_workspace", "binattn_backward",
            "binattn_qkv_pack"]
@@ -240,6 +242,20 @@ def quant_v(v: torch.Tensor, vq=None, vamax=None):
     _need(vamax, "vamax", (B, H, d), (torch.float32,), v.device)
     _check("binattn_quant_v", _lib.binattn_quant_v(_p(v), _dt(v), B, H, N, d, _p(vq), _p(vamax), _stream()))
     return vq, vamax
+
+
+def vq_canonical(vq: torch.Tensor, N: int, out=None) -> torch.Tensor:
+    """vq int8 [B,H,d,ldv] (channel-major, as quant_v writes it) -> int8 [B,H,N,d] token-major,
+    rearranged by the library's kernel (binattn_vq_canonical)."""
+    if vq.dim() != 4:
+        raise ValueError(f"vq must be 4-D [B,H,d,ldv], got {tuple(vq.shape)}")
+    B, H, d, _ = vq.shape
+    _need(vq, "vq", (B, H, d, vq_ld(N)), (torch.int8,), vq.device)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.int8, device=vq.device)
+    _need(out, "out", (B, H, N, d), (torch.int8,), vq.device)
+    _check("binattn_vq_canonical", _lib.binattn_vq_canonical(_p(vq), B, H, N, d, _p(out), _stream()))
+    return out
 
 
 def aligned_dense_bias(bias: torch.Tensor) -> torch.Tensor:

@@ -218,6 +218,15 @@ int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t
                                    (hipStream_t)stream));
 }
 
+int binattn_vq_canonical(const int8_t* vq, int B, int H, int N, int d, int8_t* out, void* stream) {
+    if (!vq || !out) return BINATTN_EINVAL;
+    int rc = check_dims(B, H, N, d);
+    if (rc) return rc;
+    if (!aligned16(vq) || !aligned16(out)) return BINATTN_EALIGN;
+    if ((rc = device_ready())) return rc;
+    return launched(launch_vq_canonical(vq, (int64_t)B * H, N, d, binattn_vq_ld(N), out, (hipStream_t)stream));
+}
+
 int binattn_forward(const uint32_t* q_bits, const float* q_mu, const uint32_t* k_bits, const float* k_mu,
                     const int8_t* vq, const float* vamax, int bias_kind, int bias_dtype, const void* bias,
                     int64_t bias_ld, int grid_h, int grid_w, int B, int H, int N, int d, void* out,

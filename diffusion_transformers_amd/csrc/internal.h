@@ -35,6 +35,7 @@ hipError_t launch_pack_qk(const void* x, int f32, int64_t ntok, int d, uint32_t*
                           hipStream_t s);
 hipError_t launch_quant_v(const void* v, int f32, int BH, int N, int d, int64_t ldv, int8_t* vq, float* vamax,
                           hipStream_t s);
+hipError_t launch_vq_canonical(const int8_t* vq, int64_t BH, int N, int d, int64_t ldv, int8_t* out, hipStream_t s);
 // q may be null: then only K and V are prepared.
 hipError_t launch_prepare(const void* q, const void* k, const void* v, int f32, int BH, int N, int d, int64_t ldv,
                           uint32_t* qbits, float* qmu, uint32_t* kbits, float* kmu, int8_t* vq, float* vamax,

@@ -168,4 +168,42 @@ hipError_t launch_quant_v(const void* v, int f32, int BH, int N, int d, int64_t 
     return launch_quant_t<_Float16>((const _Float16*)v, BH, N, d, ldv, vq, vamax, s);
 }
 
+// The canonical token-major copy of a channel-major V^ ([B,H,d,ldv] -> [B,H,N,d]; bytes only).
+// A workgroup takes one 64-token block of a head at a time (heads strided by gridDim.y): the d
+// channel rows of the block (64 bytes each, 16-byte loads; ldv is a multiple of 64) go to an LDS
+// tile [channel][token], then each thread assembles 8 channels of a token and stores them as one
+// 8-byte word (d is a multiple of 8).
+__global__ __launch_bounds__(256) void vq_canonical_kernel(const int8_t* __restrict__ vq, int64_t BH, int N, int d,
+                                                           int64_t ldv, int8_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) uint8_t sT[128][80];  // rows of 64 tokens, 16-byte aligned
+    const int n0 = blockIdx.x * 64, tid = threadIdx.x, ng = d / 8;
+    for (int64_t bh = blockIdx.y; bh < BH; bh += gridDim.y) {
+        const int8_t* src = vq + bh * d * ldv + n0;
+        for (int i = tid; i < 4 * d; i += 256) {
+            const int c = i >> 2, q = i & 3;
+            *reinterpret_cast<uint4*>(&sT[c][16 * q]) = *reinterpret_cast<const uint4*>(src + (int64_t)c * ldv + 16 * q);
+        }
+        __syncthreads();
+        for (int i = tid; i < 64 * ng; i += 256) {
+            const int t = i / ng, cg = i - t * ng;
+            if (n0 + t < N) {
+                uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    lo |= (uint32_t)sT[8 * cg + e][t] << (8 * e);
+                    hi |= (uint32_t)sT[8 * cg + 4 + e][t] << (8 * e);
+                }
+                *reinterpret_cast<uint2*>(out + (bh * N + n0 + t) * d + 8 * cg) = make_uint2(lo, hi);
+            }
+        }
+        __syncthreads();  // the tile is read before the next head's block overwrites it
+    }
+}
+
+hipError_t launch_vq_canonical(const int8_t* vq, int64_t BH, int N, int d, int64_t ldv, int8_t* out, hipStream_t s) {
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)(BH < 65535 ? BH : 65535));
+    hipLaunchKernelGGL(vq_canonical_kernel, grid, dim3(256), 0, s, vq, BH, N, d, ldv, out);
+    return hipGetLastError();
+}
+
 }  // namespace binattn

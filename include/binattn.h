@@ -102,6 +102,20 @@ int binattn_quant_v(const void* v, int dtype, int B, int H, int N, int d, int8_t
                     void* stream);
 
 /*
+ * binattn_vq_canonical -- the canonical token-major layout of a quantised V.
+ * Passage: key design 3 (Hybrid Quantization): V is held as 8-bit integers per
+ * token and channel; binattn_quant_v writes them channel-major for the PV
+ * product, and this call only rearranges those bytes (no arithmetic).
+ *
+ *   vq   [B,H,d,ldv] int8 as binattn_quant_v writes it, ldv = binattn_vq_ld(N),
+ *                    read only (the whole extent; entries for tokens n >= N are
+ *                    ignored)
+ *   out  [B,H,N,d]   int8: out[b,h,n,c] = vq[b,h,c,n]
+ * Sizes and errors as for binattn_quant_v.
+ */
+int binattn_vq_canonical(const int8_t* vq, int B, int H, int N, int d, int8_t* out, void* stream);
+
+/*
  * binattn_qkv_pack -- the QKV projection that produces the attention's inputs, with Q and K
  * binarised in its epilogue.
  * Passages: key design 1 (Scaled Binary Representations): Q and K enter the attention only as

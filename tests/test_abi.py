@@ -66,6 +66,10 @@ def test_pack_and_quant_validation(lib):
     assert lib.binattn_pack_qk(_a(258), 1, 2, 3, 5, 64, ok[6], ok[7], None) == -3
     assert lib.binattn_quant_v(ok[0], 1, 2, 3, 5, 64, None, ok[7], None) == -1
     assert lib.binattn_quant_v(ok[0], 1, 2, 3, 5, 64, _a(520), ok[7], None) == -3
+    assert lib.binattn_vq_canonical(None, 2, 3, 5, 64, ok[6], None) == -1
+    assert lib.binattn_vq_canonical(ok[0], 2, 0, 5, 64, ok[6], None) == -1
+    assert lib.binattn_vq_canonical(ok[0], 2, 3, 5, 60, ok[6], None) == -2
+    assert lib.binattn_vq_canonical(ok[0], 2, 3, 5, 64, _a(520), None) == -3
 
 
 def _fwd(lib, **kw):
@@ -196,6 +200,7 @@ def test_valid_arguments_without_a_device_report_enodevice(lib):
     if torch.cuda.is_available():
         pytest.skip("a device is present")
     assert lib.binattn_pack_qk(_a(256), 1, 2, 3, 5, 64, _a(512), _a(1024), None) == -4
+    assert lib.binattn_vq_canonical(_a(256), 2, 3, 5, 64, _a(512), None) == -4
     assert _fwd(lib) == -4
     assert _fwd(lib, kind=2, bias=_a(4096), gh=16, gw=16) == -4
     assert _fwd(lib, kind=1, bias=_a(4096), ld=(1 << 26) - 8) == -4  # the largest fp16 dense-bias stride accepted

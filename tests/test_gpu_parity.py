@@ -131,6 +131,23 @@ def test_quant_v_parity(dtype, d, N):
     np.testing.assert_array_equal(va.cpu().numpy() / np.float32(127), ovs)
 
 
+@pytest.mark.parametrize("B,H,N,d", [(1, 1, 1, 8), (2, 3, 197, 64), (1, 2, 577, 72), (2, 1, 65, 40),
+                                     (1, 1, 1000, 128), (2, 16, 16384, 64)])
+def test_vq_canonical(B, H, N, d):
+    """binattn_vq_canonical: the channel-major V^ rearranged to [B,H,N,d], byte for byte the
+    oracle's token-major quantised V and the strided view of the channel-major array."""
+    _say(f"vq_canonical B={B} H={H} N={N} d={d}")
+    inp = W.custom(B, H, N, d, "f16", "none", seed=N + d)
+    b = _b()
+    vq, _ = b.quant_v(_t(inp["v"]))
+    out = torch.full((B, H, N, d), 99, dtype=torch.int8, device=DEV)  # every byte is overwritten
+    b.vq_canonical(vq, N, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, b.vq_token_major(vq, N).contiguous())
+    ovq, _ = oracle.quant_v(inp["v"].astype(np.float64))
+    np.testing.assert_array_equal(out.cpu().numpy(), ovq)
+
+
 # ---------------------------------------------------------------- integer scores (key design 1)
 
 @pytest.mark.parametrize("d", [8, 32, 64, 72, 128])
